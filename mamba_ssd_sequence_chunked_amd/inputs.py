@@ -1,0 +1,196 @@
+"""Seeded synthetic inputs for the SSD layer core.
+
+This module only draws random numbers and rounds them to the storage
+types the kernels read (bf16 by round-to-nearest-even on the fp32 bit
+pattern, fp32 by a plain cast).  It holds none of the method's
+arithmetic: both the fp64 oracle and the HIP path receive the arrays it
+returns, so input quantisation is never counted as error.
+
+The workload shapes and distributions are the five configurations the
+library is measured on:
+
+  tiny     fp32, B=1 L=512 H=4 P=16 N=16 G=1 Q=64
+  l130m    bf16, B=8 L=2048 H=24 P=64 N=128 G=1 Q=256, init state N(0, 0.1^2)
+  l2p7b    bf16, B=4 L=4096 H=80 P=64 N=128 G=1 Q=256   (a 2.7B-class layer,
+           d_inner 5120; the headline workload)
+  long64k  bf16, B=1 L=65536 H=80 P=64 N=256 G=8 Q=256
+  decode   bf16, batch 256 H=80 P=64 N=128 G=1, 1024 single-token steps on
+           an fp32 state initialised N(0, 0.1^2)
+
+Distributions: x ~ N(0,1); dt = softplus(z) with z ~ N(0,1) - 2
+("tiny", "l130m", "decode") or z ~ N(0,1) + log(expm1(U(1e-3, 1e-1)))
+("l2p7b", "long64k"); A_h = -exp(U(0, log 16)); B, C ~ N(0,1)/sqrt(N);
+D ~ N(0,1).  Draw order per configuration: x, dt noise, dt uniform (if
+any), A uniform, B, C, D, initial state (if any); all draws are fp64 from
+``numpy.random.default_rng(seed)``.  The decode workload draws A, D and the
+state from ``default_rng(seed)`` and step t's x, dt, B, C from
+``default_rng([seed, t])`` so any step can be regenerated alone.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+__all__ = [
+    "CONFIGS", "SSDConfig", "SSDInputs", "StepInputs", "bf16_bits", "bf16_to_f64",
+    "make_inputs", "make_step_params", "make_step_inputs", "make_random",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class SSDConfig:
+    name: str
+    batch: int
+    seqlen: int            # for the decode workload: number of steps
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    chunk_size: int        # 0 for the decode workload
+    dtype: str             # "f32" or "bf16": storage type of x, B, C and y
+    dt_kind: str           # "shifted" = softplus(N(0,1) - 2); "ranged" = softplus(N + log(expm1(U)))
+    init: bool             # random N(0, 0.1^2) initial state
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+CONFIGS = {
+    "tiny": SSDConfig("tiny", 1, 512, 4, 16, 16, 1, 64, "f32", "shifted", False, 0),
+    "l130m": SSDConfig("l130m", 8, 2048, 24, 64, 128, 1, 256, "bf16", "shifted", True, 1),
+    "l2p7b": SSDConfig("l2p7b", 4, 4096, 80, 64, 128, 1, 256, "bf16", "ranged", False, 2),
+    "long64k": SSDConfig("long64k", 1, 65536, 80, 64, 256, 8, 256, "bf16", "ranged", False, 3),
+    "decode": SSDConfig("decode", 256, 1024, 80, 64, 128, 1, 0, "bf16", "shifted", True, 4),
+}
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round to bf16 (nearest-even on the fp32 bit pattern); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of bf16 bit patterns."""
+    return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def _softplus(z: np.ndarray) -> np.ndarray:
+    # log(1 + e^z) without overflow for large z
+    return np.logaddexp(0.0, z)
+
+
+def _store(a64: np.ndarray, dtype: str) -> np.ndarray:
+    return bf16_bits(a64) if dtype == "bf16" else a64.astype(np.float32)
+
+
+@dataclasses.dataclass
+class SSDInputs:
+    """One forward problem.  x, B, C hold float32 arrays (dtype "f32") or
+    uint16 bf16 bit patterns (dtype "bf16"); dt, A, D, init are float32."""
+    x: np.ndarray          # (batch, seqlen, nheads, headdim)
+    dt: np.ndarray         # (batch, seqlen, nheads), positive
+    A: np.ndarray          # (nheads,), negative
+    B: np.ndarray          # (batch, seqlen, ngroups, dstate)
+    C: np.ndarray          # (batch, seqlen, ngroups, dstate)
+    D: np.ndarray          # (nheads,)
+    init: Optional[np.ndarray]   # (batch, nheads, headdim, dstate) or None (zeros)
+    chunk_size: int
+    dtype: str
+
+    @property
+    def dims(self):
+        b, l, h, p = self.x.shape
+        return b, l, h, p, self.B.shape[3], self.B.shape[2]
+
+    def f64(self, name: str) -> np.ndarray:
+        """fp64 copy of one input (exact: every stored value is representable)."""
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if name in ("x", "B", "C") and self.dtype == "bf16":
+            return bf16_to_f64(a)
+        return a.astype(np.float64)
+
+
+def _draw_dt(rng: np.random.Generator, shape, kind: str) -> np.ndarray:
+    z = rng.standard_normal(shape)
+    if kind == "shifted":
+        z = z - 2.0
+    else:
+        u = rng.uniform(1e-3, 1e-1, size=shape)
+        z = z + np.log(np.expm1(u))
+    return _softplus(z)
+
+
+def make_random(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype="bf16",
+                dt_kind="shifted", init=False, seed=0) -> SSDInputs:
+    """Draw one forward problem of any shape with the workload distributions."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, nheads, headdim))
+    dt = _draw_dt(rng, (batch, seqlen, nheads), dt_kind)
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), size=nheads))
+    Bm = rng.standard_normal((batch, seqlen, ngroups, dstate)) / np.sqrt(dstate)
+    Cm = rng.standard_normal((batch, seqlen, ngroups, dstate)) / np.sqrt(dstate)
+    D = rng.standard_normal(nheads)
+    h0 = 0.1 * rng.standard_normal((batch, nheads, headdim, dstate)) if init else None
+    return SSDInputs(
+        x=_store(x, dtype), dt=dt.astype(np.float32), A=A.astype(np.float32),
+        B=_store(Bm, dtype), C=_store(Cm, dtype), D=D.astype(np.float32),
+        init=None if h0 is None else h0.astype(np.float32), chunk_size=chunk_size, dtype=dtype)
+
+
+def make_inputs(name: str) -> SSDInputs:
+    """The forward problem of a named configuration (not "decode")."""
+    c = CONFIGS[name]
+    if c.chunk_size == 0:
+        raise ValueError(f"{name} is a decode workload; use make_step_params/make_step_inputs")
+    return make_random(c.batch, c.seqlen, c.nheads, c.headdim, c.dstate, c.ngroups, c.chunk_size,
+                       c.dtype, c.dt_kind, c.init, c.seed)
+
+
+@dataclasses.dataclass
+class StepInputs:
+    x: np.ndarray    # (batch, nheads, headdim) storage dtype
+    dt: np.ndarray   # (batch, nheads) float32
+    B: np.ndarray    # (batch, ngroups, dstate) storage dtype
+    C: np.ndarray    # (batch, ngroups, dstate) storage dtype
+    dtype: str
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if name in ("x", "B", "C") and self.dtype == "bf16":
+            return bf16_to_f64(a)
+        return a.astype(np.float64)
+
+
+def make_step_params(name: str = "decode", batch: Optional[int] = None):
+    """Fixed decode parameters: (A, D, state0) as float32 arrays.
+
+    ``batch`` below the configured batch returns the leading rows of the
+    same draw, so a slice of the workload regenerates identically."""
+    c = CONFIGS[name]
+    rng = np.random.default_rng(c.seed)
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), size=c.nheads))
+    D = rng.standard_normal(c.nheads)
+    state = 0.1 * rng.standard_normal((c.batch, c.nheads, c.headdim, c.dstate))
+    b = c.batch if batch is None else batch
+    return A.astype(np.float32), D.astype(np.float32), np.ascontiguousarray(state[:b].astype(np.float32))
+
+
+def make_step_inputs(name: str, step: int, batch: Optional[int] = None) -> StepInputs:
+    """Step ``step``'s fresh token inputs for the decode workload."""
+    c = CONFIGS[name]
+    rng = np.random.default_rng([c.seed, step])
+    x = rng.standard_normal((c.batch, c.nheads, c.headdim))
+    dt = _draw_dt(rng, (c.batch, c.nheads), c.dt_kind)
+    Bm = rng.standard_normal((c.batch, c.ngroups, c.dstate)) / np.sqrt(c.dstate)
+    Cm = rng.standard_normal((c.batch, c.ngroups, c.dstate)) / np.sqrt(c.dstate)
+    b = c.batch if batch is None else batch
+    return StepInputs(x=_store(x[:b], c.dtype), dt=dt[:b].astype(np.float32),
+                      B=_store(Bm[:b], c.dtype), C=_store(Cm[:b], c.dtype), dtype=c.dtype)

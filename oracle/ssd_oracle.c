@@ -1,0 +1,151 @@
+/*
+ * ssd_oracle.c - plain fp64 CPU oracle of the Mamba-2 SSD layer core.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the library (the HIP kernels, the
+ * C ABI or its Python binding) includes, links or calls this file; only the
+ * tests, the package's smoke entry and the benchmark's CPU-baseline leg do.
+ * It shares no code, header, table or helper with the GPU path.
+ *
+ * It is the token-by-token recurrence, written out as the pages state it,
+ * in double precision, with no chunking, blocking or reordering:
+ *
+ *   a_t      = exp(dt_t * A_h)                 discretised decay, Abar = exp(Delta A)
+ *                                              ["Mamba-2: State Space Models and Linear-Time
+ *                                              Sequence Modeling Without Attention",
+ *                                              section "State Space Models: The Core Abstraction"]
+ *   h_t      = a_t * h_{t-1} + (dt_t x_t) B_t  the selective recurrence h_t = A_t h_{t-1} + B_t x_t
+ *                                              ["Mamba-2" wiki note, section "Question";
+ *                                              "Why Does Mamba-2 Resemble the Transformer?",
+ *                                              section "The Problem"], with the transition a
+ *                                              scalar times identity per head ("Transformers are
+ *                                              SSMs" paper card, section "How It Works") and the
+ *                                              input scaled by dt (the Mamba2Block listing of the
+ *                                              mohakchugh blog, section "Architecture: Multi-Head SSM")
+ *   y_t      = C_t . h_t + D_h x_t             readout y_t = C_t^T h_t (ql.gl, "The Problem") plus
+ *                                              the skip term D x of the continuous system
+ *                                              (mohakchugh blog, "The Core Abstraction")
+ *
+ * Per head h the state is a P x N matrix (one N-vector per headdim channel
+ * p); channels never interact, so every (b, h, p) row runs independently.
+ * B and C are shared by the heads of a group: head h reads group
+ * h / (H / G) (contiguous blocks of heads; the pages do not fix this).
+ * h_{-1} is the caller's initial state (zeros when absent) and the state
+ * after the last token is returned as the final state.
+ *
+ * Layouts (row-major, all double): x (B,L,H,P); dt (B,L,H); A, D (H);
+ * B, C (B,L,G,N); init and final (B,H,P,N); y (B,L,H,P).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Optional record: the state after each token index record_t[k] (ascending)
+ * is copied into recorded (B, n_record, H, P, N).  Returns 0, or -1 on bad
+ * arguments. */
+int ssd_oracle_forward(const double* x, const double* dt, const double* A, const double* Bm,
+                       const double* Cm, const double* D, const double* init, double* y,
+                       double* final_states, int64_t batch, int64_t seqlen, int64_t nheads,
+                       int64_t headdim, int64_t dstate, int64_t ngroups, const int64_t* record_t,
+                       int64_t n_record, double* recorded, int nthreads)
+{
+    if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0 || (n_record > 0 && (record_t == NULL || recorded == NULL)))
+        return -1;
+    const int64_t heads_per_group = nheads / ngroups;
+    const int64_t rows = batch * nheads * headdim;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dstate);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t b = r / (nheads * headdim);
+            const int64_t h = (r / headdim) % nheads;
+            const int64_t p = r % headdim;
+            const int64_t g = h / heads_per_group;
+            const int64_t state_off = ((b * nheads + h) * headdim + p) * dstate;
+            for (int64_t n = 0; n < dstate; ++n) S[n] = init ? init[state_off + n] : 0.0;
+            int64_t k = 0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const double dtv = dt[(b * seqlen + t) * nheads + h];
+                const double xv = x[((b * seqlen + t) * nheads + h) * headdim + p];
+                const double* Bt = Bm + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double* Ct = Cm + ((b * seqlen + t) * ngroups + g) * dstate;
+                const double a = exp(dtv * A[h]);
+                const double u = dtv * xv;
+                double acc = 0.0;
+                for (int64_t n = 0; n < dstate; ++n) {
+                    S[n] = a * S[n] + u * Bt[n];
+                    acc += Ct[n] * S[n];
+                }
+                y[((b * seqlen + t) * nheads + h) * headdim + p] = acc + D[h] * xv;
+                while (k < n_record && record_t[k] == t) {
+                    memcpy(recorded + (((b * n_record + k) * nheads + h) * headdim + p) * dstate, S,
+                           sizeof(double) * (size_t)dstate);
+                    ++k;
+                }
+            }
+            memcpy(final_states + state_off, S, sizeof(double) * (size_t)dstate);
+        }
+        free(S);
+    }
+    return 0;
+}
+
+/* One token of the recurrence applied to the caller's state, in place:
+ * state (B,H,P,N); x (B,H,P); dt (B,H); B, C (B,G,N); y (B,H,P).
+ * O(1) work per token in the sequence length ("Transformers are SSMs"
+ * paper card, section "Why It Matters"). */
+int ssd_oracle_step(double* state, const double* x, const double* dt, const double* A,
+                    const double* Bm, const double* Cm, const double* D, double* y, int64_t batch,
+                    int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int nthreads)
+{
+    if (batch < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0)
+        return -1;
+    const int64_t heads_per_group = nheads / ngroups;
+    const int64_t rows = batch * nheads * headdim;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int64_t b = r / (nheads * headdim);
+        const int64_t h = (r / headdim) % nheads;
+        const int64_t g = h / heads_per_group;
+        double* S = state + r * dstate;
+        const double dtv = dt[b * nheads + h];
+        const double xv = x[r];
+        const double* Bt = Bm + (b * ngroups + g) * dstate;
+        const double* Ct = Cm + (b * ngroups + g) * dstate;
+        const double a = exp(dtv * A[h]);
+        const double u = dtv * xv;
+        double acc = 0.0;
+        for (int64_t n = 0; n < dstate; ++n) {
+            S[n] = a * S[n] + u * Bt[n];
+            acc += Ct[n] * S[n];
+        }
+        y[r] = acc + D[h] * xv;
+    }
+    return 0;
+}
+
+int ssd_oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

@@ -1,0 +1,320 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function raises AssertionError when the oracle (the default
+build, or a variant passed as ``lib``) disagrees with an independent
+statement of the same result: a brute-force dense quadratic form, a closed
+form, a textbook routine, a hand-worked example or an invariant.  None of
+them re-types the recurrence loop itself.
+"""
+from __future__ import annotations
+
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+TOL = 1e-12
+
+
+def _rel(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / den)
+
+
+def rand_problem(seed, b=2, L=24, H=4, P=3, N=5, G=2, init=True, A_zero=False):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((b, L, H, P))
+    dt = np.logaddexp(0.0, rng.standard_normal((b, L, H)) - 1.0)
+    A = np.zeros(H) if A_zero else -np.exp(rng.uniform(0.0, np.log(16.0), H))
+    Bm = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    Cm = rng.standard_normal((b, L, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    h0 = 0.3 * rng.standard_normal((b, H, P, N)) if init else None
+    return x, dt, A, Bm, Cm, D, h0
+
+
+def dense_mixer(x, dt, A, Bm, Cm, D, h0):
+    """y and final state from the explicit matrix-mixer expansion.
+
+    M[t, i] = C_t . B_i * dt_i * prod_{j=i+1..t} a_j for i <= t, zero above
+    the diagonal ("Mamba-2" wiki note, section "Matrix Mixer View";
+    mohakchugh blog, section "The Duality"), y = M x + D x, plus the initial
+    state carried by prod_{j<=t} a_j.  The decay products are formed as
+    products of the per-step a_j = exp(dt_j A_h), not via a recurrence."""
+    b, L, H, P = x.shape
+    G, N = Bm.shape[2], Bm.shape[3]
+    hpg = H // G
+    y = np.zeros((b, L, H, P))
+    fin = np.zeros((b, H, P, N))
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            a = np.exp(dt[bi, :, h] * A[h])
+            dec = np.zeros((L, L))       # dec[t, i] = prod_{j=i+1..t} a_j
+            for t in range(L):
+                for i in range(t + 1):
+                    dec[t, i] = np.prod(a[i + 1:t + 1])
+            carry = np.array([np.prod(a[:t + 1]) for t in range(L)])
+            CB = Cm[bi, :, g, :] @ Bm[bi, :, g, :].T          # (L, L): C_t . B_i
+            M = np.tril(CB * dec * dt[bi, None, :, h])
+            y[bi, :, h, :] = M @ x[bi, :, h, :] + D[h] * x[bi, :, h, :]
+            if h0 is not None:
+                y[bi, :, h, :] += carry[:, None] * (Cm[bi, :, g, :] @ h0[bi, h].T)
+            w = dec[L - 1, :] * dt[bi, :, h]                  # weight of token i in the final state
+            fin[bi, h] = (x[bi, :, h, :] * w[:, None]).T @ Bm[bi, :, g, :]
+            if h0 is not None:
+                fin[bi, h] += carry[L - 1] * h0[bi, h]
+    return y, fin
+
+
+# ----------------------------------------------------------------------------------------------
+def pin_dense_quadratic_form(lib=None):
+    """P1: recurrence == dense quadratic form (G in {1, 2}, with/without init)."""
+    for seed, G, init in ((1, 1, False), (2, 2, True), (3, 4, True)):
+        x, dt, A, Bm, Cm, D, h0 = rand_problem(seed, G=G, init=init)
+        y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+        y_ref, fin_ref = dense_mixer(x, dt, A, Bm, Cm, D, h0)
+        assert _rel(y, y_ref) < TOL, f"dense form y seed={seed}: {_rel(y, y_ref)}"
+        assert _rel(fin, fin_ref) < TOL, f"dense form final seed={seed}: {_rel(fin, fin_ref)}"
+
+
+def pin_linear_attention(lib=None):
+    """P2: A = 0 (unit decay) is causal linear attention:
+    y = tril(C B^T) (dt * x) + C h0^T + D x  ("Mamba-2" wiki note, mixer table;
+    "Transformers are SSMs" paper card, "How It Works")."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(11, b=1, L=40, H=2, P=4, N=6, G=1, init=True, A_zero=True)
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+    for h in range(2):
+        Q_ = Cm[0, :, 0, :]
+        K_ = Bm[0, :, 0, :]
+        V_ = dt[0, :, h, None] * x[0, :, h, :]
+        ref = np.tril(Q_ @ K_.T) @ V_ + Q_ @ h0[0, h].T + D[h] * x[0, :, h, :]
+        assert _rel(y[0, :, h, :], ref) < TOL, f"linear attention head {h}: {_rel(y[0, :, h, :], ref)}"
+        fin_ref = h0[0, h] + V_.T @ K_
+        assert _rel(fin[0, h], fin_ref) < TOL
+
+
+def pin_scalar_closed_forms(lib=None):
+    """P3: N = 1 (the scalar SSM of the mohakchugh blog, "The Duality").
+    (i) constant dt, A; x = B = C = 1: geometric series y_t = dt (1 - a^{t+1}) / (1 - a) + D.
+    (ii) constant coefficients, random x: a first-order IIR filter, scipy.signal.lfilter."""
+    from scipy.signal import lfilter
+    L = 50
+    dtc, Ac, Dc = 0.3, -1.7, 0.25
+    a = np.exp(dtc * Ac)
+    ones = np.ones((1, L, 1, 1))
+    y, fin = oracle.forward(ones, np.full((1, L, 1), dtc), np.array([Ac]), ones, ones, np.array([Dc]), None, lib=lib)
+    t = np.arange(L)
+    ref = dtc * (1 - a ** (t + 1)) / (1 - a) + Dc
+    assert _rel(y[0, :, 0, 0], ref) < TOL, f"geometric series: {_rel(y[0, :, 0, 0], ref)}"
+    assert _rel(fin[0, 0, 0, 0], ref[-1] - Dc) < TOL
+    rng = np.random.default_rng(5)
+    xs = rng.standard_normal(L)
+    b0, c0 = 0.7, -1.3
+    y, _ = oracle.forward(xs.reshape(1, L, 1, 1), np.full((1, L, 1), dtc), np.array([Ac]),
+                          np.full((1, L, 1, 1), b0), np.full((1, L, 1, 1), c0), np.array([Dc]), None, lib=lib)
+    ref = lfilter([c0 * dtc * b0], [1.0, -a], xs) + Dc * xs
+    assert _rel(y[0, :, 0, 0], ref) < TOL, f"lfilter: {_rel(y[0, :, 0, 0], ref)}"
+
+
+def _impulse_matrix(dt, A, Bm, Cm, L, lib=None):
+    """Probe the mixing matrix column by column with unit impulses (P = 1, D = 0, zero state)."""
+    M = np.zeros((L, L))
+    for i in range(L):
+        x = np.zeros((1, L, 1, 1))
+        x[0, i, 0, 0] = 1.0
+        y, _ = oracle.forward(x, dt, A, Bm, Cm, np.zeros(1), None, lib=lib)
+        M[:, i] = y[0, :, 0, 0]
+    return M
+
+
+def pin_semiseparable_rank(lib=None):
+    """P4: the mixing matrix is lower triangular and every block M[i:, :i+1] of
+    its lower triangle has rank <= N ("Mamba-2" wiki note, "Structured
+    Semiseparable Matrices"; mohakchugh blog, "The Duality")."""
+    L = 24
+    for N in (1, 2, 3):
+        x, dt, A, Bm, Cm, D, _ = rand_problem(20 + N, b=1, L=L, H=1, P=1, N=N, G=1, init=False)
+        A = 0.05 * A          # mild decay, so the far blocks keep a clean numerical rank
+        M = _impulse_matrix(dt, A, Bm, Cm, L, lib=lib)
+        assert np.all(np.triu(M, 1) == 0.0), "mixing matrix must be causal (lower triangular)"
+        for i in range(L - 1):
+            blk = M[i:, :i + 1]
+            s = np.linalg.svd(blk, compute_uv=False)
+            rank = int(np.sum(s > 1e-10 * max(s[0], 1e-300)))
+            assert rank <= N, f"N={N} block at {i} has rank {rank}"
+        # generic blocks reach rank N
+        s = np.linalg.svd(M[L // 2:, :L // 2], compute_uv=False)
+        assert int(np.sum(s > 1e-10 * s[0])) == min(N, L // 2)
+
+
+def pin_skip_only(lib=None):
+    """P5: with B = 0 (zero state) or C = 0, the output is exactly D x."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(31, init=True)
+    y, fin = oracle.forward(x, dt, A, np.zeros_like(Bm), Cm, D, None, lib=lib)
+    assert np.array_equal(y, D[None, None, :, None] * x), "B = 0 must give y = D x exactly"
+    assert np.array_equal(fin, np.zeros_like(fin))
+    y, _ = oracle.forward(x, dt, A, Bm, np.zeros_like(Cm), D, h0, lib=lib)
+    assert np.array_equal(y, D[None, None, :, None] * x + 0.0), "C = 0 must give y = D x exactly"
+
+
+def pin_zero_input(lib=None):
+    """P6: x = 0 leaves only the decayed initial state:
+    y_t = C_t . (prod_{j<=t} a_j) h0, final = prod_j a_j h0."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(41, init=True)
+    x[:] = 0.0
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+    b, L, H, P = x.shape
+    G = Bm.shape[2]
+    for bi in range(b):
+        for h in range(H):
+            g = h // (H // G)
+            carry = np.cumprod(np.exp(dt[bi, :, h] * A[h]))
+            ref = carry[:, None] * (Cm[bi, :, g, :] @ h0[bi, h].T)
+            assert _rel(y[bi, :, h, :], ref) < TOL
+            assert _rel(fin[bi, h], carry[-1] * h0[bi, h]) < TOL
+
+
+def pin_linearity_causality(lib=None):
+    """P7: linear in x for a zero state; causal (a change at t0 leaves y[:t0]
+    bit-identical); a NaN at t0 reaches only y[t0:] of its own (b, h, p) row."""
+    x1, dt, A, Bm, Cm, D, _ = rand_problem(51, init=False)
+    x2 = rand_problem(52, init=False)[0]
+    al, be = 0.75, -2.5
+    y1, _ = oracle.forward(x1, dt, A, Bm, Cm, D, None, lib=lib)
+    y2, _ = oracle.forward(x2, dt, A, Bm, Cm, D, None, lib=lib)
+    y12, _ = oracle.forward(al * x1 + be * x2, dt, A, Bm, Cm, D, None, lib=lib)
+    assert _rel(y12, al * y1 + be * y2) < TOL
+    t0 = 9
+    xp = x1.copy()
+    xp[:, t0] += 1.0
+    yp, _ = oracle.forward(xp, dt, A, Bm, Cm, D, None, lib=lib)
+    assert np.array_equal(yp[:, :t0], y1[:, :t0])
+    assert not np.array_equal(yp[:, t0:], y1[:, t0:])
+    xn = x1.copy()
+    xn[1, t0, 2, 1] = np.nan
+    yn, _ = oracle.forward(xn, dt, A, Bm, Cm, D, None, lib=lib)
+    bad = np.isnan(yn)
+    expect = np.zeros_like(bad)
+    expect[1, t0:, 2, 1] = True
+    assert np.array_equal(bad, expect), "NaN must poison exactly y[t0:] of its row"
+
+
+def pin_split_resume(lib=None):
+    """P8: running the first L1 tokens, then the rest from the returned state,
+    equals one pass ("Why Does Mamba-2 Resemble the Transformer?",
+    "Mamba-2 Changes More Than the Algorithm": the recurrent state is what
+    crosses a split of the sequence)."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(61, L=30, init=True)
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+    for L1 in (1, 13, 29):
+        ya, fa = oracle.forward(x[:, :L1], dt[:, :L1], A, Bm[:, :L1], Cm[:, :L1], D, h0, lib=lib)
+        yb, fb = oracle.forward(x[:, L1:], dt[:, L1:], A, Bm[:, L1:], Cm[:, L1:], D, fa, lib=lib)
+        assert _rel(np.concatenate([ya, yb], axis=1), y) < TOL
+        assert _rel(fb, fin) < TOL
+
+
+def pin_groups(lib=None):
+    """P9: G groups == one group per head after repeating B, C to the heads
+    that share them (heads are assigned to groups in contiguous blocks)."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(71, H=6, G=3, init=True)
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+    Br = np.repeat(Bm, 2, axis=2)
+    Cr = np.repeat(Cm, 2, axis=2)
+    y2, fin2 = oracle.forward(x, dt, A, Br, Cr, D, h0, lib=lib)
+    assert np.array_equal(y, y2) and np.array_equal(fin, fin2)
+    # and heads in different groups really see different B, C
+    y3, _ = oracle.forward(x, dt, A, Bm[:, :, ::-1].copy(), Cm[:, :, ::-1].copy(), D, h0, lib=lib)
+    assert not np.array_equal(y, y3)
+
+
+def pin_step_matches_forward(lib=None):
+    """P10: the recurrent mode, one token at a time, equals the whole-sequence
+    call ("Transformers are SSMs" paper card, "Why It Matters": O(1) decode)."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(81, init=True)
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=lib)
+    st = h0
+    for t in range(x.shape[1]):
+        yt, st = oracle.step(st, x[:, t], dt[:, t], A, Bm[:, t], Cm[:, t], D, lib=lib)
+        assert _rel(yt, y[:, t]) < TOL
+    assert _rel(st, fin) < TOL
+
+
+def load_hand_example():
+    vals = {}
+    with open(os.path.join(GOLDEN, "hand_example_n2.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            vals[k] = np.array([float(t) for t in v])
+    return vals
+
+
+def pin_hand_example(lib=None):
+    """P11: the hand-worked example in tests/golden/hand_example_n2.txt."""
+    v = load_hand_example()
+    L = 3
+    x = v["x"].reshape(1, L, 1, 1)
+    dt = v["dt"].reshape(1, L, 1)
+    Bm = np.stack([v["B0"], v["B1"], v["B2"]]).reshape(1, L, 1, 2)
+    Cm = np.stack([v["C0"], v["C1"], v["C2"]]).reshape(1, L, 1, 2)
+    h0 = v["init"].reshape(1, 1, 1, 2)
+    y, fin = oracle.forward(x, dt, v["A"], Bm, Cm, v["D"], h0, lib=lib)
+    assert np.max(np.abs(y.ravel() - v["y"])) < 1e-13, f"hand example y {y.ravel()} vs {v['y']}"
+    assert np.max(np.abs(fin.ravel() - v["final"])) < 1e-13
+    # the same example through the recurrent step
+    st = h0
+    for t in range(L):
+        yt, st = oracle.step(st, x[:, t], dt[:, t], v["A"], Bm[:, t], Cm[:, t], v["D"], lib=lib)
+        assert abs(yt.ravel()[0] - v["y"][t]) < 1e-13
+
+
+def pin_chunk_helpers(lib=None):
+    """P12: the chunk-level helpers against closed forms.
+    * exp(chunk_log_decay) is the decay product the recurrence applies to a
+      unit state (B = 0, C = 1, h0 = 1, D = 0: y_t = prod_{j<=t} a_j within the chunk);
+    * chunk_states and chunk_entry_states against the dense expansion
+      sum_i (prod_{j=i+1..end} a_j) dt_i x_i B_i^T (+ carried init)."""
+    Q = 8
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(91, b=2, L=29, H=4, P=3, N=5, G=2, init=True)
+    cs = oracle.chunk_log_decay(dt, A, Q)
+    b, L, H, P = x.shape
+    nc = oracle.n_chunks(L, Q)
+    for c in range(nc):
+        lo, hi = c * Q, min(L, (c + 1) * Q)
+        n = hi - lo
+        ones = np.ones((b, n, 1, 1))
+        for h in range(H):
+            yy, _ = oracle.forward(np.zeros((b, n, 1, 1)), dt[:, lo:hi, h:h + 1], A[h:h + 1],
+                                   np.zeros((b, n, 1, 1)), ones, np.zeros(1), np.ones((b, 1, 1, 1)), lib=lib)
+            assert _rel(np.exp(cs[:, h, c, :n]), yy[:, :, 0, 0]) < TOL
+    st = oracle.chunk_states(x, dt, A, Bm, Cm, D, Q)
+    entry, fin, _ = oracle.chunk_entry_states(x, dt, A, Bm, Cm, D, h0, Q)
+    G = Bm.shape[2]
+    for bi in range(b):
+        for h in range(H):
+            g = h // (H // G)
+            a = np.exp(dt[bi, :, h] * A[h])
+            for c in range(nc):
+                lo, hi = c * Q, min(L, (c + 1) * Q)
+                w = np.array([np.prod(a[i + 1:hi]) * dt[bi, i, h] for i in range(lo, hi)])
+                ref = (x[bi, lo:hi, h, :] * w[:, None]).T @ Bm[bi, lo:hi, g, :]
+                assert _rel(st[bi, c, h], ref) < TOL
+                w0 = np.array([np.prod(a[i + 1:lo]) * dt[bi, i, h] for i in range(0, lo)])
+                ref_in = np.prod(a[:lo]) * h0[bi, h]
+                if lo:
+                    ref_in = ref_in + (x[bi, :lo, h, :] * w0[:, None]).T @ Bm[bi, :lo, g, :]
+                assert _rel(entry[bi, c, h], ref_in) < TOL
+
+
+ALL_PINS = [
+    pin_dense_quadratic_form, pin_linear_attention, pin_scalar_closed_forms, pin_semiseparable_rank,
+    pin_skip_only, pin_zero_input, pin_linearity_causality, pin_split_resume, pin_groups,
+    pin_step_matches_forward, pin_hand_example, pin_chunk_helpers,
+]

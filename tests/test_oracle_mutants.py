@@ -1,0 +1,54 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that
+at least one pin catches each of them.  This guards the pins themselves: a
+pin set that a dropped term, a wrong sign or index, or a swapped operand
+slips through would not pin the oracle."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from oracle_pins import (pin_dense_quadratic_form, pin_groups, pin_hand_example, pin_skip_only,
+                         pin_step_matches_forward, pin_zero_input, pin_scalar_closed_forms)
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
+
+MUTANTS = {
+    "dropped_skip_term": [("acc + D[h] * xv", "acc")],
+    "decay_sign": [("exp(dtv * A[h])", "exp(-dtv * A[h])")],
+    "input_not_scaled_by_dt": [("const double u = dtv * xv;", "const double u = xv;")],
+    "B_C_swapped_in_update": [("S[n] = a * S[n] + u * Bt[n];", "S[n] = a * S[n] + u * Ct[n];")],
+    "B_C_swapped_in_readout": [("acc += Ct[n] * S[n];", "acc += Bt[n] * S[n];")],
+    "readout_before_update": [("S[n] = a * S[n] + u * Bt[n];\n                    acc += Ct[n] * S[n];",
+                               "acc += Ct[n] * S[n];\n                    S[n] = a * S[n] + u * Bt[n];")],
+    "decay_after_input": [("S[n] = a * S[n] + u * Bt[n];", "S[n] = a * (S[n] + u * Bt[n]);")],
+    "group_map_interleaved": [("const int64_t g = h / heads_per_group;", "const int64_t g = h % ngroups;")],
+    "init_ignored": [("init ? init[state_off + n] : 0.0", "0.0")],
+    "dt_of_neighbour_head": [("dt[(b * seqlen + t) * nheads + h]", "dt[(b * seqlen + t) * nheads + (h + 1) % nheads]")],
+    # forward only (the first occurrence): the step has no previous token
+    "decay_uses_previous_dt": [("const double a = exp(dtv * A[h]);",
+                                "const double a = exp((t ? dt[(b * seqlen + t - 1) * nheads + h] : dtv) * A[h]);", 1)],
+}
+
+PINS = [pin_hand_example, pin_skip_only, pin_zero_input, pin_scalar_closed_forms, pin_groups,
+        pin_dense_quadratic_form, pin_step_matches_forward]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    src = open(SRC).read()
+    for old, new, *count in MUTANTS[name]:
+        assert old in src, f"mutation site for {name} not found"
+        src = src.replace(old, new, *count)
+    path = tmp_path / "ssd_oracle_mutant.c"
+    path.write_text(src)
+    so = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(so), str(path), "-lm"])
+    lib = oracle.load_variant(str(so))
+    caught = []
+    for pin in PINS:
+        try:
+            pin(lib=lib)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
