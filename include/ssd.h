@@ -1,0 +1,184 @@
+/*
+ * ssd.h - C ABI of the MI355X (gfx950) Mamba-2 SSD layer core.
+ *
+ * The operation is the multi-head selective state-space transform with a
+ * scalar-times-identity transition per head:
+ *
+ *     a_t = exp(dt_t * A_h)
+ *     h_t = a_t * h_{t-1} + (dt_t * x_t) B_t^T          (state: headdim x dstate per head)
+ *     y_t = h_t C_t + D_h * x_t
+ *
+ * (the recurrence of the "Mamba-2" wiki note, section "Question"; the
+ * discretised decay of "Mamba-2: State Space Models and Linear-Time
+ * Sequence Modeling Without Attention", section "State Space Models: The
+ * Core Abstraction", where the continuous system also carries the D x
+ * term; the dt-scaled input of that page's multi-head block, section
+ * "Architecture: Multi-Head SSM"; one decay scalar per head, "Transformers
+ * are SSMs" paper card, section "How It Works").  B and C are shared by the
+ * heads of a group: head h reads group h / (nheads / ngroups).
+ *
+ * Two modes compute it ("Mamba-2" wiki note, section "Algorithmic Lesson";
+ * mohakchugh blog, section "Why This Matters for Hardware"):
+ *   ssd_forward - the chunked (dual) mode over a whole sequence: quadratic,
+ *                 matmul-shaped work inside chunks of chunk_size tokens and
+ *                 the recurrent state passed between chunks (mohakchugh blog,
+ *                 section "Block Decomposition"; ql.gl, "The Core of SSD").
+ *                 It runs the four stage kernels below in order.
+ *   ssd_step    - the recurrent mode: one token per call, O(1) in the
+ *                 sequence length (crackai.dev paper card, "Why It Matters").
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (current HIP device) to dense,
+ *     row-major arrays in the layouts given per call.  The caller owns every
+ *     buffer, including the workspace; the library allocates nothing, keeps
+ *     no mutable global state and is safe to call from several threads.
+ *   - "T" is the storage type of x, B, C, y and of the chunk-entry states:
+ *     dtype SSD_F32 (float) or SSD_BF16 (bfloat16, 2 bytes).  dt, A, D,
+ *     initial/final/step states and the fp32 workspace arrays are float.
+ *     Arithmetic accumulates in fp32; bf16 operands of the matrix-core
+ *     products are rounded to nearest even.
+ *   - dt must already be positive (softplus applied by the caller) and A
+ *     negative (or zero); neither is clamped.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and the call returns without synchronising.  SSD_OK means
+ *     "enqueued"; completion is the stream's business.
+ *   - Arguments are validated on the host before anything is enqueued: an
+ *     error status means no device memory was read or written.  A launch
+ *     failure reported by the runtime returns SSD_ERR_HIP.  No C++
+ *     exception crosses this interface.
+ *   - Shape limits: batch >= 0; seqlen >= 0; nheads >= 1; headdim in
+ *     {16, 32, 64, 128}; dstate a multiple of 16 in [16, 256]; ngroups >= 1
+ *     dividing nheads; chunk_size a multiple of 16 in [16, 256].  seqlen
+ *     need not be a multiple of chunk_size: the last chunk is then shorter.
+ *   - Outputs must not overlap inputs (the step state is the one in/out
+ *     argument); overlap is reported as SSD_ERR_ALIAS.
+ */
+#ifndef SSD_MI355X_H
+#define SSD_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,      /* a required pointer is NULL */
+    SSD_ERR_SHAPE = -2,     /* a size is out of the supported range */
+    SSD_ERR_DTYPE = -3,     /* dtype is not SSD_F32 or SSD_BF16 */
+    SSD_ERR_WORKSPACE = -4, /* workspace smaller than ssd_forward_workspace_bytes */
+    SSD_ERR_HIP = -5,       /* the HIP runtime reported an error at launch */
+    SSD_ERR_ALIAS = -6      /* an output overlaps an input */
+} ssd_status;
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* ssd_status_string(int status);
+
+/* Version of this interface: 100 * major + minor. */
+int ssd_abi_version(void);
+
+/* Number of chunks ceil(seqlen / chunk_size) (0 for seqlen 0); -1 on bad sizes. */
+int64_t ssd_num_chunks(int64_t seqlen, int64_t chunk_size);
+
+/* ---------------------------------------------------------------------------------------------
+ * Chunked (dual) mode.
+ * ------------------------------------------------------------------------------------------- */
+
+/* Bytes of device workspace ssd_forward needs for these sizes: at least 256
+ * for valid sizes, 0 when the sizes or dtype are invalid.
+ * Layout (each part 256-byte aligned, nc = number of chunks):
+ *   dA_cs      float (batch, nheads, nc, chunk_size)
+ *   dt_chunked float (batch, nheads, nc, chunk_size)
+ *   chunk_states float (batch, nc, nheads, headdim, dstate)
+ *   entry_states T   (batch, nc, nheads, headdim, dstate)          */
+size_t ssd_forward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                   int64_t dstate, int64_t chunk_size, int dtype);
+
+/* y, final_states = SSD(x, dt, A, B, C, D, init_states) in chunks of chunk_size.
+ *   x            T     (batch, seqlen, nheads, headdim)
+ *   dt           float (batch, seqlen, nheads)
+ *   A, D         float (nheads)
+ *   B, C         T     (batch, seqlen, ngroups, dstate)
+ *   init_states  float (batch, nheads, headdim, dstate), the state before
+ *                token 0 (h_{-1}); NULL means zeros
+ *   y            T     (batch, seqlen, nheads, headdim), written
+ *   final_states float (batch, nheads, headdim, dstate), written: the state
+ *                after the last token (equal to init_states when seqlen = 0)
+ *   workspace    device buffer of at least ssd_forward_workspace_bytes()
+ * Runs ssd_dA_cumsum, ssd_chunk_state, ssd_state_passing, ssd_chunk_scan. */
+int ssd_forward(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                const float* D, const float* init_states, void* y, float* final_states,
+                int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
+                size_t workspace_bytes, void* stream);
+
+/* Stage 1 (segment decays).  For every chunk c and position l inside it:
+ *   dA_cs[b,h,c,l]      = sum_{j = cQ .. cQ+l} dt[b,j,h] * A[h]
+ *   dt_chunked[b,h,c,l] = dt[b, cQ+l, h]
+ * so that exp(dA_cs[l] - dA_cs[s]) is the decay product prod_{j=s+1..l} a_j
+ * of the matrix-mixer entries ("Mamba-2" wiki note, "Matrix Mixer View").
+ * Positions past seqlen in a short last chunk get dt 0 (the sum stays flat).
+ *   dt float (batch, seqlen, nheads); A float (nheads)
+ *   dA_cs, dt_chunked float (batch, nheads, nc, chunk_size), written */
+int ssd_dA_cumsum(const float* dt, const float* A, float* dA_cs, float* dt_chunked, int64_t batch,
+                  int64_t seqlen, int64_t nheads, int64_t chunk_size, void* stream);
+
+/* Stage 2 (chunk states).  The state each chunk reaches from a zero state,
+ * the rank-dstate factor of the off-diagonal blocks of the mixing matrix
+ * ("Mamba-2" wiki note, "Structured Semiseparable Matrices"):
+ *   chunk_states[b,c,h,p,n] = sum_l x[b,cQ+l,h,p] * dt_l * exp(dA_cs[Q-1] - dA_cs[l]) * B[b,cQ+l,g(h),n]
+ *   x T (batch, seqlen, nheads, headdim); B T (batch, seqlen, ngroups, dstate)
+ *   dt_chunked, dA_cs float (batch, nheads, nc, chunk_size) as written by stage 1
+ *   chunk_states float (batch, nc, nheads, headdim, dstate), written */
+int ssd_chunk_state(const void* x, const void* B, const float* dt_chunked, const float* dA_cs,
+                    float* chunk_states, int64_t batch, int64_t seqlen, int64_t nheads,
+                    int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype,
+                    void* stream);
+
+/* Stage 3 (state passing).  The recurrence between chunks (ql.gl, "The Core
+ * of SSD"; mohakchugh blog, "Block Decomposition"), sequential over chunks:
+ *   S = init (or 0); for c: entry_states[b,c] = S; S = exp(dA_cs[b,h,c,Q-1]) * S + chunk_states[b,c]
+ *   final_states = S
+ *   chunk_states float (batch, nc, nheads, headdim, dstate); dA_cs float (batch, nheads, nc, chunk_size)
+ *   init_states float (batch, nheads, headdim, dstate) or NULL (zeros)
+ *   entry_states T (batch, nc, nheads, headdim, dstate), written (rounded to T)
+ *   final_states float (batch, nheads, headdim, dstate), written */
+int ssd_state_passing(const float* chunk_states, const float* dA_cs, const float* init_states,
+                      void* entry_states, float* final_states, int64_t batch, int64_t seqlen,
+                      int64_t nheads, int64_t headdim, int64_t dstate, int64_t chunk_size,
+                      int dtype, void* stream);
+
+/* Stage 4 (chunk scan).  The output of every chunk: the masked quadratic
+ * (attention-like) form inside the chunk plus the entering state read out
+ * by C, plus the skip term (mohakchugh blog, "Block Decomposition" and "The
+ * Tensor Core Connection"):
+ *   y[l,p] = sum_{s<=l} (C_l . B_s) exp(dA_cs[l] - dA_cs[s]) dt_s x[s,p]
+ *          + exp(dA_cs[l]) * sum_n C_l[n] entry_states[c,p,n] + D[h] x[l,p]
+ *   x, y T (batch, seqlen, nheads, headdim); B, C T (batch, seqlen, ngroups, dstate)
+ *   dt_chunked, dA_cs float (batch, nheads, nc, chunk_size); entry_states T (batch, nc, nheads, headdim, dstate)
+ *   D float (nheads) */
+int ssd_chunk_scan(const void* x, const void* B, const void* C, const float* dt_chunked,
+                   const float* dA_cs, const void* entry_states, const float* D, void* y,
+                   int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                   int64_t ngroups, int64_t chunk_size, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Recurrent mode.
+ * ------------------------------------------------------------------------------------------- */
+
+/* One token: a = exp(dt*A); state = a*state + (dt*x) B^T; y = state C + D x.
+ *   state float (batch, nheads, headdim, dstate), read and written IN PLACE
+ *   x T (batch, nheads, headdim); dt float (batch, nheads); A, D float (nheads)
+ *   B, C T (batch, ngroups, dstate); y T (batch, nheads, headdim), written */
+int ssd_step(float* state, const void* x, const float* dt, const float* A, const void* B,
+             const void* C, const float* D, void* y, int64_t batch, int64_t nheads,
+             int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SSD_MI355X_H */

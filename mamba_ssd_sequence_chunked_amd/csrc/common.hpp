@@ -1,0 +1,139 @@
+// common.hpp - device helpers shared by the SSD kernels (gfx950 / CDNA4).
+//
+// * element types: T is float or __bf16; bf16 <-> fp32 conversion uses the
+//   hardware round-to-nearest-even convert (v_cvt_pk_bf16_f32) and a shift.
+// * matrix-core fragments: every product runs on 16x16 output tiles with a
+//   contraction block of 32.  A lane holds 8 contraction slots of its row
+//   (A operand) or column (B operand):  lane = 16 * g + r, slots (g, 0..7).
+//   For bf16 this is one v_mfma_f32_16x16x32_bf16; for fp32 it is eight
+//   v_mfma_f32_16x16x4_f32, the i-th taking slot (g, i) of every lane.  Both
+//   contract the same 32 (g, i) slots, so which index a slot stands for is
+//   the caller's choice as long as A and B agree.  The accumulator layout
+//   (both types) is: lane 16 * g + c holds rows 4g .. 4g+3 of column c.
+// * a wavefront inclusive prefix sum built from DPP row shifts and row
+//   broadcasts (64 lanes, no LDS).
+// * an XCD-aware block index: the dispatcher hands consecutive workgroups
+//   to the 8 XCDs in turn, so related tiles are renumbered to share an XCD
+//   (and its L2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return static_cast<float>(v); }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return static_cast<bf16>(v); }
+
+// 8 consecutive elements of T, as one operand fragment.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ float get(int i) const { return static_cast<float>(v[i]); }
+    __device__ __forceinline__ void set(int i, float f) { v[i] = static_cast<bf16>(f); }
+    __device__ __forceinline__ void zero() {
+        *reinterpret_cast<uint4*>(&v) = make_uint4(0u, 0u, 0u, 0u);
+    }
+};
+template <> struct Vec8<float> {
+    float v[8];
+    __device__ __forceinline__ float get(int i) const { return v[i]; }
+    __device__ __forceinline__ void set(int i, float f) { v[i] = f; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = 0.f;
+    }
+};
+
+// Load / store 8 consecutive elements (16 B for bf16, 32 B for fp32); the
+// address must be aligned to the vector size.
+__device__ __forceinline__ void load8(Vec8<bf16>& d, const bf16* p) {
+    d.v = *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void load8(Vec8<float>& d, const float* p) {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    d.v[0] = a.x; d.v[1] = a.y; d.v[2] = a.z; d.v[3] = a.w;
+    d.v[4] = b.x; d.v[5] = b.y; d.v[6] = b.z; d.v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16* p, const Vec8<bf16>& d) {
+    *reinterpret_cast<bf16x8*>(p) = d.v;
+}
+__device__ __forceinline__ void store8(float* p, const Vec8<float>& d) {
+    reinterpret_cast<float4*>(p)[0] = make_float4(d.v[0], d.v[1], d.v[2], d.v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(d.v[4], d.v[5], d.v[6], d.v[7]);
+}
+
+// 4 consecutive elements (8 B bf16 / 16 B fp32), used for half fragments.
+__device__ __forceinline__ void load4(Vec8<bf16>& d, int half, const bf16* p) {
+    const bf16x4 q = *reinterpret_cast<const bf16x4*>(p);
+    d.v[4 * half + 0] = q[0]; d.v[4 * half + 1] = q[1];
+    d.v[4 * half + 2] = q[2]; d.v[4 * half + 3] = q[3];
+}
+__device__ __forceinline__ void load4(Vec8<float>& d, int half, const float* p) {
+    const float4 q = *reinterpret_cast<const float4*>(p);
+    d.v[4 * half + 0] = q.x; d.v[4 * half + 1] = q.y;
+    d.v[4 * half + 2] = q.z; d.v[4 * half + 3] = q.w;
+}
+__device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
+    bf16x4 q;
+    q[0] = static_cast<bf16>(a); q[1] = static_cast<bf16>(b);
+    q[2] = static_cast<bf16>(c); q[3] = static_cast<bf16>(d);
+    *reinterpret_cast<bf16x4*>(p) = q;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+}
+
+// acc (16x16 fp32 tile) += A (16 x 32) * B (32 x 16).
+__device__ __forceinline__ void mma(f32x4& acc, const Vec8<bf16>& a, const Vec8<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Vec8<float>& a, const Vec8<float>& b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (lane order).
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+    // rows of 16: shift right by 1, 2, 4, 8 (lanes shifted in from outside the row read 0)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x111, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x112, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x114, 0xf, 0xf, true));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x118, 0xf, 0xf, true));
+    // lane 15 of rows 0 and 2 into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and 3 (row_bcast:31)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false));
+    return v;
+}
+
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of a group gets the sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+    for (int m = 1; m < W; m <<= 1) v += __shfl_xor(v, m, kWave);
+    return v;
+}
+
+// Renumber a linear workgroup index so that consecutive logical indices run on the same XCD.
+__device__ __forceinline__ int xcd_logical_block(int bid, int nblocks) {
+    const int q = nblocks / kNumXcd, r = nblocks % kNumXcd;
+    const int xcd = bid % kNumXcd, local = bid / kNumXcd;
+    const int base = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return base + local;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+}  // namespace ssd

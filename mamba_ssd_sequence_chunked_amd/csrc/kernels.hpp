@@ -1,0 +1,35 @@
+// kernels.hpp - host-side launchers of the SSD kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Dims {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int64_t nchunks() const { return (seqlen + chunk - 1) / chunk; }
+};
+
+hipError_t launch_dA_cumsum(const float* dt, const float* A, float* dA_cs, float* dt_chunked,
+                            const Dims& d, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_chunk_state(const T* x, const T* B, const float* dt_chunked, const float* dA_cs,
+                              float* chunk_states, const Dims& d, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, const float* init,
+                                T* entry_states, float* final_states, const Dims& d,
+                                hipStream_t stream);
+
+template <typename T>
+hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt_chunked,
+                             const float* dA_cs, const T* entry_states, const float* D, T* y,
+                             const Dims& d, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
+                           const T* C, const float* D, T* y, const Dims& d, hipStream_t stream);
+
+}  // namespace ssd

@@ -1,0 +1,82 @@
+// state_passing.hip - stage 3: the recurrence between chunks.
+//
+//   S = init (or 0);  for c = 0 .. nc-1:  entry[c] = S;  S = exp(cs_c[Q-1]) * S + S_c
+//   final = S
+//
+// The chunk-level form of the same linear recurrence, with the whole chunk's
+// decay as the transition (ql.gl, "The Core of SSD"; the state update of the
+// mohakchugh blog's block-decomposition outline, which reads the state
+// entering a chunk before updating it).  It is sequential over chunks and
+// embarrassingly parallel over (batch, head, headdim, dstate), and it does
+// almost no arithmetic: one read of every chunk state and one write of every
+// entry state, so it is bound by HBM bandwidth.
+//
+// Each thread owns 4 consecutive state elements of one (batch, head) and
+// walks the chunks with 16-byte loads and stores; the loads of the next
+// chunks do not depend on the running state, so unrolling lets several be
+// in flight.  A workgroup covers 1024 elements of a single (batch, head), so
+// the chunk decay is one uniform value per chunk.  The running state stays
+// in fp32; entry states are rounded to T once, as the next stage consumes
+// them as matrix-core operands.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kElemsPerBlock = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(256) void state_passing_kernel(
+    const float* __restrict__ chunk_states, const float* __restrict__ dA_cs,
+    const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_states,
+    int nheads, int PN, int Q, int nc)
+{
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int e = blockIdx.x * kElemsPerBlock + 4 * threadIdx.x;
+    if (e >= PN) return;
+    const int64_t bh = b * nheads + h;
+
+    float4 s = init ? *reinterpret_cast<const float4*>(init + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* cs = dA_cs + bh * (int64_t)nc * Q + (Q - 1);
+    const int64_t stride = (int64_t)nheads * PN;               // one chunk
+    const float* src = chunk_states + (b * nc * nheads + h) * (int64_t)PN + e;
+    T* dst = entry + (b * nc * nheads + h) * (int64_t)PN + e;
+
+#pragma unroll 4
+    for (int c = 0; c < nc; ++c) {
+        const float4 sc = *reinterpret_cast<const float4*>(src + c * stride);
+        const float dec = __expf(cs[(int64_t)c * Q]);
+        store4(dst + c * stride, s.x, s.y, s.z, s.w);
+        s.x = fmaf(dec, s.x, sc.x);
+        s.y = fmaf(dec, s.y, sc.y);
+        s.z = fmaf(dec, s.z, sc.z);
+        s.w = fmaf(dec, s.w, sc.w);
+    }
+    *reinterpret_cast<float4*>(final_states + bh * PN + e) = s;
+}
+
+}  // namespace
+
+template <typename T>
+hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, const float* init,
+                                T* entry_states, float* final_states, const Dims& d,
+                                hipStream_t stream)
+{
+    if (d.batch == 0) return hipSuccess;
+    const int PN = (int)(d.headdim * d.dstate);
+    dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads,
+              (unsigned)d.batch);
+    hipLaunchKernelGGL((state_passing_kernel<T>), grid, dim3(256), 0, stream, chunk_states, dA_cs, init,
+                       entry_states, final_states, (int)d.nheads, PN, (int)d.chunk, (int)d.nchunks());
+    return hipGetLastError();
+}
+
+template hipError_t launch_state_passing<float>(const float*, const float*, const float*, float*,
+                                                float*, const Dims&, hipStream_t);
+template hipError_t launch_state_passing<bf16>(const float*, const float*, const float*, bf16*,
+                                               float*, const Dims&, hipStream_t);
+
+}  // namespace ssd

@@ -1,0 +1,147 @@
+"""Host-side tests of the C ABI (no GPU needed): the library loads, exports
+every function include/ssd.h declares, and rejects bad arguments with the
+documented status before touching any memory.
+
+The pointers passed here are never dereferenced: every call is one that the
+host-side validation must reject, so nothing is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_sequence_chunked_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS = 0, -1, -2, -3, -4, -5, -6
+P = ctypes.c_void_p
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_A-Z0-9]+)\s*\(", text)))
+
+
+def fake(i):
+    """A distinct, 256-aligned, never-dereferenced address."""
+    return P(0x10000000 + 0x1000000 * i)
+
+
+def test_library_exports_every_declared_function():
+    lib = ssd.load_library()
+    names = declared_functions()
+    assert {"ssd_forward", "ssd_step", "ssd_forward_workspace_bytes", "ssd_status_string", "ssd_dA_cumsum",
+            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} is declared in include/ssd.h but not exported"
+
+
+def test_status_strings():
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS):
+        assert ssd.status_string(code).startswith("SSD_")
+    assert "unknown" in ssd.status_string(123)
+    assert ssd.load_library().ssd_abi_version() == 100
+
+
+def test_num_chunks_and_workspace():
+    assert ssd.num_chunks(4096, 256) == 16
+    assert ssd.num_chunks(4097, 256) == 17
+    assert ssd.num_chunks(0, 64) == 0
+    assert ssd.num_chunks(-1, 64) == -1
+    ws = ssd.workspace_bytes(4, 4096, 80, 64, 128, 256, 1)
+    nc = 16
+    expect = 2 * 4 * 80 * nc * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4 + 4 * nc * 80 * 64 * 128 * 2
+    assert ws == expect
+    assert ssd.workspace_bytes(1, 0, 4, 16, 16, 64, 0) >= 256
+    assert ssd.workspace_bytes(1, 100, 4, 48, 16, 64, 0) == 0     # headdim 48 unsupported
+    assert ssd.workspace_bytes(1, 100, 4, 16, 16, 64, 7) == 0     # bad dtype
+
+
+def _forward(lib, **kw):
+    args = dict(x=fake(1), dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), init=None, y=fake(7),
+                final=fake(8), batch=2, seqlen=100, nheads=4, headdim=16, dstate=16, ngroups=1, chunk=64,
+                dtype=0, ws=fake(9), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return lib.ssd_forward(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"], args["init"],
+                           args["y"], args["final"], args["batch"], args["seqlen"], args["nheads"],
+                           args["headdim"], args["dstate"], args["ngroups"], args["chunk"], args["dtype"],
+                           args["ws"], args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(headdim=48), ERR_SHAPE),
+    (dict(headdim=256), ERR_SHAPE),
+    (dict(dstate=8), ERR_SHAPE),
+    (dict(dstate=264), ERR_SHAPE),
+    (dict(dstate=40), ERR_SHAPE),
+    (dict(ngroups=3), ERR_SHAPE),
+    (dict(ngroups=0), ERR_SHAPE),
+    (dict(chunk=24), ERR_SHAPE),
+    (dict(chunk=512), ERR_SHAPE),
+    (dict(chunk=0), ERR_SHAPE),
+    (dict(seqlen=-1), ERR_SHAPE),
+    (dict(batch=-1), ERR_SHAPE),
+    (dict(nheads=0), ERR_SHAPE),
+    (dict(dtype=2), ERR_DTYPE),
+    (dict(x=None), ERR_NULL),
+    (dict(final=None), ERR_NULL),
+    (dict(ws=None), ERR_NULL),
+    (dict(ws_bytes=100), ERR_WS),
+    (dict(y=fake(1)), ERR_ALIAS),                    # y == x
+    (dict(final=P(0x10000000 + 0x1000000 * 9 + 4096)), ERR_ALIAS),   # final inside the workspace
+    (dict(x=P(0x10000008)), ERR_SHAPE),             # misaligned
+])
+def test_forward_rejects(kw, code):
+    assert _forward(ssd.load_library(), **kw) == code
+
+
+def test_step_rejects():
+    lib = ssd.load_library()
+
+    def call(**kw):
+        a = dict(state=fake(1), x=fake(2), dt=fake(3), A=fake(4), B=fake(5), C=fake(6), D=fake(7), y=fake(8),
+                 batch=2, nheads=4, headdim=16, dstate=16, ngroups=1, dtype=1)
+        a.update(kw)
+        return lib.ssd_step(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["y"], a["batch"],
+                            a["nheads"], a["headdim"], a["dstate"], a["ngroups"], a["dtype"], None)
+
+    assert call(headdim=20) == ERR_SHAPE
+    assert call(dstate=0) == ERR_SHAPE
+    assert call(ngroups=3) == ERR_SHAPE
+    assert call(dtype=-1) == ERR_DTYPE
+    assert call(state=None) == ERR_NULL
+    assert call(y=fake(2)) == ERR_ALIAS
+    assert call(state=P(0x10000004)) == ERR_SHAPE
+    assert call(batch=0) == OK                     # nothing to do, nothing enqueued
+
+
+def test_stage_entry_points_reject():
+    lib = ssd.load_library()
+    assert lib.ssd_dA_cumsum(fake(1), fake(2), fake(3), fake(4), 1, 100, 4, 20, None) == ERR_SHAPE
+    assert lib.ssd_dA_cumsum(None, fake(2), fake(3), fake(4), 1, 100, 4, 64, None) == ERR_NULL
+    assert lib.ssd_dA_cumsum(fake(1), fake(2), fake(1), fake(4), 1, 100, 4, 64, None) == ERR_ALIAS
+    assert lib.ssd_chunk_state(fake(1), fake(2), fake(3), fake(4), fake(5), 1, 100, 4, 16, 16, 1, 64, 5,
+                               None) == ERR_DTYPE
+    assert lib.ssd_state_passing(fake(1), fake(2), None, fake(3), None, 1, 100, 4, 16, 16, 64, 0,
+                                 None) == ERR_NULL
+    assert lib.ssd_chunk_scan(fake(1), fake(2), fake(3), fake(4), fake(5), fake(6), fake(7), fake(1), 1, 100, 4,
+                              16, 16, 1, 64, 0, None) == ERR_ALIAS
+
+
+def test_no_device_reports_hip_error():
+    """With no GPU, a valid call reaches the runtime and reports SSD_ERR_HIP (never crashes)."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; this checks the no-device path")
+    assert _forward(ssd.load_library()) == ERR_HIP
+
+
+def test_python_binding_validates_before_calling():
+    import torch
+    x = torch.zeros(1, 8, 2, 16)
+    with pytest.raises(ValueError):
+        ssd.forward(x, torch.zeros(1, 8, 2), torch.zeros(2), torch.zeros(1, 8, 1, 16), torch.zeros(1, 8, 1, 16),
+                    torch.zeros(2), 16)        # CPU tensors are refused
