@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Throughput of the SSD layer core on one MI355X.
+
+A step is one ssd_forward call (the four chunked-mode kernels) over one batch
+of the 2.7B-layer-shape workload (batch 4 x 4096 tokens, 80 heads of dim 64,
+state 128, one group, chunk 256, bf16 x/B/C, fp32 dt/A/D), inputs resident in
+HBM.  The JSON line reports tokens/s of the whole call, the roofline of its
+dominant kernel measured with HIP events on the library's stream, the
+recurrent-mode kernel on the decode workload (batch 256, fp32 state
+256x80x64x128, single-token steps), and the fp64 CPU oracle timed on the
+host beside it.
+
+    python bench.py [--steps K] [--warmup W] [--workload l2p7b|l130m|long64k]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, published
+KERNELS = ("dA_cumsum", "chunk_state", "state_passing", "chunk_scan")
+KERNEL_SOURCES = {"dA_cumsum": "dA_cumsum.hip", "chunk_state": "chunk_state.hip",
+                  "state_passing": "state_passing.hip", "chunk_scan": "chunk_scan.hip", "ssd_step": "ssd_step.hip"}
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="l2p7b", choices=["l130m", "l2p7b", "long64k"])
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-mode leg")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (scale for HBM byte counters) and exit")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------------------------------------
+# Algorithmic work per launch (bytes that must cross HBM at least once; flops the method needs)
+
+def kernel_work(b, L, H, P, N, G, Q, es, init):
+    nc = -(-L // Q)
+    x = b * L * H * P * es
+    bc = b * L * G * N * es
+    cs = b * H * nc * Q * 4
+    st32 = b * nc * H * P * N * 4
+    stT = b * nc * H * P * N * es
+    fin = b * H * P * N * 4
+    causal = Q * (Q + 1) // 2
+    work = {
+        "dA_cumsum": dict(bytes=b * L * H * 4 + 2 * cs, flops=2 * b * L * H),
+        "chunk_state": dict(bytes=x + bc + 2 * cs + st32, flops=2 * b * L * H * P * N),
+        "state_passing": dict(bytes=st32 + b * H * nc * 4 + (fin if init else 0) + stT + fin,
+                              flops=2 * b * nc * H * P * N),
+        # y = x + (causal C B^T once per group) masked @ X + C . S_in, plus D x
+        "chunk_scan": dict(bytes=2 * x + 2 * bc + 2 * cs + stT + H * 4,
+                           flops=2 * b * nc * G * causal * N + 2 * b * nc * H * causal * P
+                           + 2 * b * L * H * N * P + 2 * b * L * H * P),
+    }
+    return work
+
+
+def step_work(b, H, P, N, G, es):
+    return dict(bytes=2 * b * H * P * N * 4 + 2 * b * H * P * es + 2 * b * G * N * es + b * H * 4 + 2 * H * 4,
+                flops=5 * b * H * P * N)
+
+
+def source_digest(name):
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[name], "common.hpp"):
+        with open(os.path.join(ROOT, "mamba_ssd_sequence_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, name):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None when
+    there is none for this kernel and workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    m_b = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_src or not m_b or m_src.group(1) != source_digest(name):
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------------------------------------------
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the SSD layer core has no multi-GPU path in this library", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_sequence_chunked_amd as ssd
+    from mamba_ssd_sequence_chunked_amd.inputs import CONFIGS, make_inputs
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    lib = ssd.load_library()
+    dev = torch.device("cuda:0")
+    cfg = CONFIGS[args.workload]
+    inp = make_inputs(args.workload)
+    b, L, H, P, N, G = inp.dims
+    Q = inp.chunk_size
+    es = 2 if inp.dtype == "bf16" else 4
+    code = ssd.SSD_BF16 if inp.dtype == "bf16" else ssd.SSD_F32
+    tdt = torch.bfloat16 if inp.dtype == "bf16" else torch.float32
+
+    def t(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    x, dt, A, B, C, D, init = (t(inp.x), t(inp.dt), t(inp.A), t(inp.B), t(inp.C), t(inp.D), t(inp.init))
+    y = torch.empty_like(x)
+    final = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws_bytes = ssd.workspace_bytes(b, L, H, P, N, Q, code)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    nc = ssd.num_chunks(L, Q)
+    cs = torch.empty((b, H, nc, Q), dtype=torch.float32, device=dev)
+    dtc = torch.empty_like(cs)
+    states = torch.empty((b, nc, H, P, N), dtype=torch.float32, device=dev)
+    entry = torch.empty((b, nc, H, P, N), dtype=tdt, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    p = lambda tt: None if tt is None else ctypes.c_void_p(tt.data_ptr())  # noqa: E731
+
+    def forward():
+        rc = lib.ssd_forward(p(x), p(dt), p(A), p(B), p(C), p(D), p(init), p(y), p(final), b, L, H, P, N, G, Q,
+                             code, p(ws), ws_bytes, sp)
+        if rc:
+            raise ssd.SSDError("ssd_forward", rc)
+
+    stage_calls = {
+        "dA_cumsum": lambda: lib.ssd_dA_cumsum(p(dt), p(A), p(cs), p(dtc), b, L, H, Q, sp),
+        "chunk_state": lambda: lib.ssd_chunk_state(p(x), p(B), p(dtc), p(cs), p(states), b, L, H, P, N, G, Q, code,
+                                                   sp),
+        "state_passing": lambda: lib.ssd_state_passing(p(states), p(cs), p(init), p(entry), p(final), b, L, H, P, N,
+                                                       Q, code, sp),
+        "chunk_scan": lambda: lib.ssd_chunk_scan(p(x), p(B), p(C), p(dtc), p(cs), p(entry), p(D), p(y), b, L, H, P,
+                                                 N, G, Q, code, sp),
+    }
+
+    # ---- warmup and the timed region (whole ssd_forward calls)
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        forward()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tokens = b * L
+    value = tokens / (ms_per_step / 1e3)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)",
+          file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: the same four launches with events between them
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        for k, name in enumerate(KERNELS):
+            rc = stage_calls[name]()
+            if rc:
+                raise ssd.SSDError(name, rc)
+            evs[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    kern_us = {name: 1e3 * sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
+               for k, name in enumerate(KERNELS)}
+    work = kernel_work(b, L, H, P, N, G, Q, es, init is not None)
+    kernels = {}
+    for name in KERNELS:
+        us = kern_us[name]
+        w = work[name]
+        kernels[name] = dict(us=round(us, 2), alg_bytes=w["bytes"], alg_flops=w["flops"],
+                             gbs=round(w["bytes"] / us / 1e3, 1), hbm_frac=round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
+                             tflops=round(w["flops"] / us / 1e6, 2),
+                             mfma_frac=round(w["flops"] / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
+    dominant = max(KERNELS, key=lambda n: kern_us[n])
+    dk = kernels[dominant]
+    traffic = measured_traffic(args.workload, dominant)
+    roofline = dict(kernel=dominant, bound="hbm", achieved=dk["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    alg_bytes_per_launch=dk["alg_bytes"], us_per_launch=dk["us"])
+    print(f"[bench] per-kernel us: {json.dumps(kern_us)}", file=sys.stderr, flush=True)
+
+    # ---- recurrent mode on the decode workload
+    decode = None
+    if not args.no_decode:
+        dc = CONFIGS["decode"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(dc.seed)
+        db, dH, dP, dN, dG = dc.batch, dc.nheads, dc.headdim, dc.dstate, dc.ngroups
+        state = 0.1 * torch.randn((db, dH, dP, dN), generator=g, device=dev, dtype=torch.float32)
+        dA = -torch.exp(torch.rand(dH, generator=g, device=dev) * float(np.log(16.0)))
+        dD = torch.randn(dH, generator=g, device=dev)
+        nset = 8
+        sx = [torch.randn((db, dH, dP), generator=g, device=dev).to(torch.bfloat16) for _ in range(nset)]
+        sdt = [torch.nn.functional.softplus(torch.randn((db, dH), generator=g, device=dev) - 2.0) for _ in range(nset)]
+        sB = [(torch.randn((db, dG, dN), generator=g, device=dev) / dN ** 0.5).to(torch.bfloat16) for _ in range(nset)]
+        sC = [(torch.randn((db, dG, dN), generator=g, device=dev) / dN ** 0.5).to(torch.bfloat16) for _ in range(nset)]
+        yd = torch.empty((db, dH, dP), dtype=torch.bfloat16, device=dev)
+
+        def one(i):
+            k = i % nset
+            rc = lib.ssd_step(p(state), p(sx[k]), p(sdt[k]), p(dA), p(sB[k]), p(sC[k]), p(dD), p(yd), db, dH, dP, dN,
+                              dG, ssd.SSD_BF16, sp)
+            if rc:
+                raise ssd.SSDError("ssd_step", rc)
+
+        for i in range(16):
+            one(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.decode_steps):
+            one(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.decode_steps
+        sw = step_work(db, dH, dP, dN, dG, 2)
+        gbs = sw["bytes"] / us / 1e3
+        decode = dict(workload="decode: batch 256, 80 heads x 64, state 128, bf16 tokens, fp32 state",
+                      steps=args.decode_steps, us_per_step=round(us, 2), tokens_per_s=round(db / (us / 1e6), 1),
+                      alg_bytes_per_step=sw["bytes"], gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                      traffic=measured_traffic("decode", "ssd_step"))
+        print(f"[bench] ssd_step: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+
+    # ---- the fp64 CPU oracle on the host, beside it
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        heads = H if args.workload != "long64k" else 8
+        X64 = inp.f64("x")[:, :, :heads]
+        B64, C64 = inp.f64("B"), inp.f64("C")
+        hpg = H // G
+        gsel = sorted({h // hpg for h in range(heads)})
+        t0 = time.perf_counter()
+        oracle.forward(X64, inp.dt[:, :, :heads], inp.A[:heads], B64[:, :, gsel], C64[:, :, gsel], inp.D[:heads],
+                       None if inp.init is None else inp.init[:, :heads], nthreads=0)
+        el = time.perf_counter() - t0
+        # tokens/s of the whole workload = (token-heads per second) / heads
+        cpu = dict(value=round(b * L * heads / el / H, 1), unit="tokens/s", cores=oracle.max_threads(),
+                   kind="oracle",
+                   sample=f"{args.workload}: all {b}x{L} tokens, {heads} of {H} heads, fp64 token-by-token "
+                          f"recurrence, {el:.2f} s wall")
+        print(f"[bench] oracle: {el:.2f} s for {heads} heads", file=sys.stderr, flush=True)
+
+    out = {
+        "metric": "SSD fwd tokens/s at 2.7B-layer shape; % MFMA peak, % HBM BW for ssd_step",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if inp.dtype == "bf16" else "f32", "data": "synthetic (seeded numpy, inputs resident in HBM)",
+        "config": {"workload": f"{args.workload}: batch {b}, seqlen {L}, {H} heads x {P}, dstate {N}, "
+                               f"{G} group(s), chunk {Q}, {inp.dtype} x/B/C",
+                   "global_batch": b, "seq_len": L, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "ssd_step": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

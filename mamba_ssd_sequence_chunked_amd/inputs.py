@@ -70,9 +70,14 @@ CONFIGS = {
 
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round to bf16 (nearest-even on the fp32 bit pattern); returns uint16 bit patterns."""
-    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    u = np.array(a, dtype=np.float32, copy=True, order="C").view(np.uint32)
+    bias = np.right_shift(u, 16)
+    np.bitwise_and(bias, 1, out=bias)
+    bias += np.uint32(0x7FFF)
+    u += bias
+    del bias
+    np.right_shift(u, 16, out=u)
+    return u.astype(np.uint16)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
