@@ -9,28 +9,31 @@
 // entering the chunk, decayed to position l (that blog's block-decomposition
 // outline adds it before the state moves on); the third is the skip term.
 //
-// Workgroup = (batch, chunk, head, 64-row tile of the chunk); 4 wavefronts,
-// each owning 16 rows x all P columns of y.  Everything runs on the matrix
-// cores with fp32 accumulation:
+// Workgroup = (batch, chunk, group, 64-row tile of the chunk, up to HB heads
+// of the group); 4 wavefronts, each owning 16 rows x all P columns of y for
+// every one of those heads.  Everything runs on the matrix cores with fp32
+// accumulation:
 //   * C rows of a wavefront are read once from global memory straight into
-//     operand fragments (the state axis is contiguous, which is the
+//     operand fragments (the state axis is contiguous, and it is the
 //     contraction axis of both C.B^T and C.S^T) and kept in registers.
-//   * inter term: S_in is staged through LDS 64 state columns at a time and
+//   * inter term, head by head: S_in of the head is staged through LDS and
 //     multiplied against those fragments; rows are scaled by exp(cs[l]).
 //   * intra term, 32 source tokens at a time: G^T (tokens x rows) = B_s C^T
-//     comes out of the matrix core with each lane holding 4 consecutive
-//     source tokens of one row; two such tiles are exactly one A operand for
-//     G @ X_s once the 32 contraction slots are assigned to tokens in the
-//     same order on the X side, so G never leaves registers.  The decay and
-//     causal mask are applied in fp32 between the two products (entries above
-//     the diagonal are selected to zero, never multiplied), then rounded once
-//     to T.
+//     is computed ONCE for all the heads of the workgroup (B and C belong to
+//     the group), then each head applies its own decay and dt in fp32 and
+//     multiplies by its x tile.  G^T comes out of the matrix core with each
+//     lane holding 4 consecutive source tokens of one row; two such tiles
+//     are exactly one A operand for G @ X_s once the 32 contraction slots
+//     are assigned to tokens in the same order on the X side, so G never
+//     leaves registers.  Entries above the diagonal are selected to zero,
+//     never multiplied.
+//   * the next 32 tokens' B and x (and the next head's S_in) are loaded into
+//     registers while the current tile is being multiplied, so global
+//     latency overlaps matrix-core work.
 //   * y tiles are staged through LDS so every store, and the x read of the
 //     skip term, is a 16-byte vector access along the head dimension.
-// Workgroups are numbered row-tile fastest, then head, then chunk, and
-// renumbered so that consecutive ones share an XCD and its L2 (the row
-// tiles of a (chunk, head) re-read the same x, B and S_in; the heads of a
-// group the same B and C).
+// Workgroups are numbered row-tile fastest, then head block, group, chunk,
+// and renumbered so that consecutive ones share an XCD and its L2.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -40,101 +43,136 @@ namespace {
 
 constexpr int kRows = 64;     // rows of y per workgroup
 constexpr int kSB = 32;       // source tokens per intra step
-constexpr int kSlab = 64;     // state columns of S_in per LDS stage
 constexpr int kMaxQ = 256;
 
-template <typename T, int P, int NK>
+// heads per workgroup: bounded by the accumulator registers (HB * P <= 512)
+// and, for the widest state, by the fragment registers it keeps live.
+constexpr int heads_per_block(int P, int NK) {
+    return (NK >= 8 ? 5 : 8) < 512 / P ? (NK >= 8 ? 5 : 8) : 512 / P;
+}
+
+template <typename T, int P, int NK, int HB>
 struct ScanSmem {
-    static constexpr int NP = 32 * NK;                           // padded state width
+    static constexpr int NP = 32 * NK;                       // state width padded to the contraction block
+    static constexpr bool kFullS = sizeof(T) * P * (NP + 8) <= 40 * 1024;
+    static constexpr int SW = kFullS ? NP : 64;              // state columns of S_in per LDS stage
+    static constexpr int ss_pitch = SW + 8;
     static constexpr int bs_pitch = NP + 8;
     static constexpr int xt_pitch = kSB + 8;
-    static constexpr int ss_pitch = kSlab + 8;
     static constexpr int out_pitch = P + 4;
-    static constexpr size_t bs_bytes = sizeof(T) * kSB * bs_pitch;
-    static constexpr size_t xt_bytes = sizeof(T) * P * xt_pitch;
     static constexpr size_t ss_bytes = sizeof(T) * P * ss_pitch;
+    static constexpr size_t bs_bytes = sizeof(T) * kSB * bs_pitch;
+    static constexpr size_t xt_bytes = sizeof(T) * HB * P * xt_pitch;
     static constexpr size_t out_bytes = sizeof(float) * kRows * out_pitch;
     static constexpr size_t m1 = ss_bytes > bs_bytes + xt_bytes ? ss_bytes : bs_bytes + xt_bytes;
     static constexpr size_t region = m1 > out_bytes ? m1 : out_bytes;
-    static constexpr size_t total = 2 * sizeof(float) * kMaxQ + region;
+    static constexpr size_t dec_bytes = 2 * sizeof(float) * HB * kMaxQ;
+    static constexpr size_t total = dec_bytes + region;
+    // register-prefetch shares per thread (256 threads)
+    static constexpr int s_items = (P * SW / 8 + 255) / 256;           // Vec8 of one S_in stage
+    static constexpr int x_items = (HB * P + 255) / 256;               // 4 x 8 blocks of x
+    static constexpr int b_items = (kSB * NP / 8 + 255) / 256;         // Vec8 of B
 };
 
-template <typename T, int P, int NK>
-__global__ __launch_bounds__(256) void chunk_scan_kernel(
+template <typename T, int P, int NK, int HB>
+__global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, const float* __restrict__ Dv, T* __restrict__ y, int seqlen,
-    int nheads, int ngroups, int N, int Q, int nc, int nlt, int nblocks)
+    int nheads, int ngroups, int N, int Q, int nc, int nlt, int nhb, int hpw, int nblocks)
 {
-    using S = ScanSmem<T, P, NK>;
+    using S = ScanSmem<T, P, NK, HB>;
+    constexpr int NP = S::NP, SW = S::SW;
     __shared__ __attribute__((aligned(16))) unsigned char smem[S::total];
-    float* cs_s = reinterpret_cast<float*>(smem);
-    float* dt_s = cs_s + kMaxQ;
-    unsigned char* region = smem + 2 * sizeof(float) * kMaxQ;
-    T* SS = reinterpret_cast<T*>(region);                       // inter phase
-    T* BS = reinterpret_cast<T*>(region);                       // intra phase
-    T* XT = reinterpret_cast<T*>(region + S::bs_bytes);         // intra phase
-    float* OUT = reinterpret_cast<float*>(region);              // epilogue
+    float* csh = reinterpret_cast<float*>(smem);                    // [HB][kMaxQ]
+    float* dth = csh + HB * kMaxQ;                                  // [HB][kMaxQ]
+    unsigned char* region = smem + S::dec_bytes;
+    T* SS = reinterpret_cast<T*>(region);                           // inter phase
+    T* BS = reinterpret_cast<T*>(region);                           // intra phase
+    T* XT = reinterpret_cast<T*>(region + S::bs_bytes);             // intra phase [HB][P][xt_pitch]
+    float* OUT = reinterpret_cast<float*>(region);                  // epilogue
 
     int id = xcd_logical_block(blockIdx.x, nblocks);
     const int lt = id % nlt; id /= nlt;
-    const int h = id % nheads; id /= nheads;
+    const int hb = id % nhb; id /= nhb;
+    const int g = id % ngroups; id /= ngroups;
     const int c = id % nc;
     const int64_t b = id / nc;
-    const int g = h / (nheads / ngroups);
+    const int hpg = nheads / ngroups;
+    const int h0 = g * hpg + hb * hpw;
+    const int nh = min(hpw, hpg - hb * hpw);                       // heads of this workgroup (<= HB)
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, (int64_t)seqlen - t0);
     const int row0 = lt * kRows;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int r16 = lane & 15, grp = lane >> 4;
-    const int lw0 = row0 + 16 * wave;                 // first row of this wavefront
-    const int lrow = lw0 + r16;                       // the row this lane feeds into the products
+    const int lw0 = row0 + 16 * wave;
+    const int lrow = lw0 + r16;
 
-    const int64_t dbase = (((int64_t)b * nheads + h) * nc + c) * Q;
-    for (int i = tid; i < kMaxQ; i += 256) {
-        cs_s[i] = i < Q ? dA_cs[dbase + i] : 0.f;
-        dt_s[i] = i < Q ? dt_chunked[dbase + i] : 0.f;
+    for (int i = tid; i < HB * kMaxQ; i += 256) {
+        const int hh = i / kMaxQ, l = i % kMaxQ;
+        float cv = 0.f, dv = 0.f;
+        if (hh < nh && l < Q) {
+            const int64_t o = (((int64_t)b * nheads + h0 + hh) * nc + c) * Q + l;
+            cv = dA_cs[o];
+            dv = dt_chunked[o];
+        }
+        csh[i] = cv;
+        dth[i] = dv;
     }
 
-    // C rows of this wavefront as operand fragments (state axis = contraction slots).
     Vec8<T> cf[NK];
 #pragma unroll
     for (int ks = 0; ks < NK; ++ks) {
         const int n = 32 * ks + 8 * grp;
-        if (lrow < len && n < N)
-            load8(cf[ks], Cm + ((b * seqlen + t0 + lrow) * ngroups + g) * N + n);
-        else
-            cf[ks].zero();
+        if (lrow < len && n < N) load8(cf[ks], Cm + ((b * seqlen + t0 + lrow) * ngroups + g) * N + n);
+        else cf[ks].zero();
     }
 
-    f32x4 acc[P / 16];
+    f32x4 acc[HB][P / 16];
 #pragma unroll
-    for (int i = 0; i < P / 16; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+        for (int pt = 0; pt < P / 16; ++pt) acc[hh][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // ---- inter-chunk term: exp(cs[l]) * C_l . S_in[p, :]
+    // ---------------- inter-chunk term, head by head: exp(cs[l]) * C_l . S_in[p, :]
     {
-        f32x4 ai[P / 16];
+        const int64_t ent0 = (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
+        constexpr int nslab = NP / SW;
+        Vec8<T> pf[S::s_items];
+        auto fetch_s = [&](int hh, int sl) {
+            const T* src = entry + ent0 + (int64_t)hh * P * N;
 #pragma unroll
-        for (int i = 0; i < P / 16; ++i) ai[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* ent = entry + (((int64_t)b * nc + c) * nheads + h) * (int64_t)P * N;
-        constexpr int nslab = (NK + 1) / 2;
-#pragma unroll
-        for (int sl = 0; sl < nslab; ++sl) {
-            __syncthreads();
-            for (int i = tid; i < P * (kSlab / 8); i += 256) {
-                const int p = i / (kSlab / 8), o = i % (kSlab / 8);
-                const int n = sl * kSlab + 8 * o;
-                Vec8<T> v;
-                if (n < N) load8(v, ent + (int64_t)p * N + n);
-                else v.zero();
-                store8(SS + p * S::ss_pitch + 8 * o, v);
+            for (int k = 0; k < S::s_items; ++k) {
+                const int i = tid + 256 * k;
+                const int p = i / (SW / 8), o = i % (SW / 8);
+                const int n = sl * SW + 8 * o;
+                if (i < P * SW / 8 && n < N) load8(pf[k], src + (int64_t)p * N + n);
+                else pf[k].zero();
             }
-            __syncthreads();
+        };
+        fetch_s(0, 0);
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int ks = 2 * sl + kk;
-                if (ks < NK) {
+        for (int hh = 0; hh < HB; ++hh) {
+            if (hh >= nh) break;
+            f32x4 ai[P / 16];
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) ai[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sl = 0; sl < nslab; ++sl) {
+                __syncthreads();
+#pragma unroll
+                for (int k = 0; k < S::s_items; ++k) {
+                    const int i = tid + 256 * k;
+                    if (i < P * SW / 8) store8(SS + (i / (SW / 8)) * S::ss_pitch + 8 * (i % (SW / 8)), pf[k]);
+                }
+                __syncthreads();
+                if (sl + 1 < nslab) fetch_s(hh, sl + 1);
+                else if (hh + 1 < nh) fetch_s(hh + 1, 0);
+#pragma unroll
+                for (int kk = 0; kk < SW / 32; ++kk) {
+                    const int ks = sl * (SW / 32) + kk;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> bf;
@@ -143,110 +181,133 @@ __global__ __launch_bounds__(256) void chunk_scan_kernel(
                     }
                 }
             }
+            float sc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sc[j] = __expf(csh[hh * kMaxQ + lw0 + 4 * grp + j]);
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[hh][pt][j] = sc[j] * ai[pt][j];
         }
-        float sc[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sc[j] = __expf(cs_s[lw0 + 4 * grp + j]);
-#pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[pt][j] += sc[j] * ai[pt][j];
     }
 
-    // ---- intra-chunk term: sum_{s <= l} G[l, s] x[s, :]
-    const int s_end = min(len, row0 + kRows);
-    const float cl = cs_s[lrow];
-    for (int s0 = 0; s0 < s_end; s0 += kSB) {
-        __syncthreads();
-        constexpr int nXb = (kSB / 4) * (P / 8);
-        const int nBb = kSB * ((N + 7) / 8);
-        for (int i = tid; i < nXb + nBb; i += 256) {
-            if (i < nXb) {
-                const int q = i / (P / 8), o = i % (P / 8);
-                float v[4][8];
+    // ---------------- intra-chunk term: sum_{s <= l} G[l, s] x[s, :]
+    {
+        const int s_end = min(len, row0 + kRows);
+        const int nsb = (s_end + kSB - 1) / kSB;
+        Vec8<T> px[S::x_items][4];
+        Vec8<T> pb[S::b_items];
+        auto fetch = [&](int s0) {
+#pragma unroll
+            for (int k = 0; k < S::x_items; ++k) {
+                const int i = tid + 256 * k;                 // (head, 4-token group, 8-column group)
+                const int hh = i / P, q = (i % P) / (P / 8), o = i % (P / 8);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = s0 + 4 * q + r;
-                    Vec8<T> row;
-                    if (s < len) load8(row, x + ((b * seqlen + t0 + s) * nheads + h) * P + 8 * o);
-                    else row.zero();
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[r][e] = row.get(e);
+                    if (i < HB * P && hh < nh && s < len)
+                        load8(px[k][r], x + ((b * seqlen + t0 + s) * nheads + h0 + hh) * P + 8 * o);
+                    else
+                        px[k][r].zero();
                 }
+            }
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    store4(XT + (8 * o + e) * S::xt_pitch + 4 * q, v[0][e], v[1][e], v[2][e], v[3][e]);
-            } else {
-                const int j = i - nXb;
-                const int r = j / ((N + 7) / 8), o = j % ((N + 7) / 8);
+            for (int k = 0; k < S::b_items; ++k) {
+                const int i = tid + 256 * k;                 // (token, 8-column group)
+                const int r = i / (NP / 8), o = i % (NP / 8);
                 const int s = s0 + r;
-                Vec8<T> v;
-                if (s < len) load8(v, Bm + ((b * seqlen + t0 + s) * ngroups + g) * N + 8 * o);
-                else v.zero();
-                store8(BS + r * S::bs_pitch + 8 * o, v);
+                if (i < kSB * NP / 8 && s < len && 8 * o < N)
+                    load8(pb[k], Bm + ((b * seqlen + t0 + s) * ngroups + g) * N + 8 * o);
+                else
+                    pb[k].zero();
             }
-        }
-        // zero the padded state columns N .. 32*NK of the B tile
-        if (32 * NK > N) {
-            const int padw = 32 * NK - N;
-            for (int i = tid; i < kSB * (padw / 8); i += 256) {
-                const int r = i / (padw / 8), o = i % (padw / 8);
-                Vec8<T> z;
-                z.zero();
-                store8(BS + r * S::bs_pitch + N + 8 * o, z);
-            }
-        }
-        __syncthreads();
-        if (s0 <= lw0 + 15 && lw0 < len) {
-            f32x4 gt[2];
+        };
+        const float* csl = csh;
+        if (nsb > 0) fetch(0);
+        for (int sb = 0; sb < nsb; ++sb) {
+            const int s0 = sb * kSB;
+            __syncthreads();
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                gt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < S::x_items; ++k) {
+                const int i = tid + 256 * k;
+                if (i < HB * P) {
+                    const int hh = i / P, q = (i % P) / (P / 8), o = i % (P / 8);
+                    T* dst = XT + (hh * P + 8 * o) * S::xt_pitch + 4 * q;
 #pragma unroll
-                for (int ks = 0; ks < NK; ++ks) {
-                    Vec8<T> af;
-                    load8(af, BS + (16 * st + r16) * S::bs_pitch + 32 * ks + 8 * grp);
-                    mma(gt[st], af, cf[ks]);
+                    for (int e = 0; e < 8; ++e)
+                        store4(dst + e * S::xt_pitch, px[k][0].get(e), px[k][1].get(e), px[k][2].get(e),
+                               px[k][3].get(e));
                 }
             }
-            Vec8<T> gf;
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+            for (int k = 0; k < S::b_items; ++k) {
+                const int i = tid + 256 * k;
+                if (i < kSB * NP / 8) store8(BS + (i / (NP / 8)) * S::bs_pitch + 8 * (i % (NP / 8)), pb[k]);
+            }
+            __syncthreads();
+            if (sb + 1 < nsb) fetch(s0 + kSB);
+            if (s0 <= lw0 + 15 && lw0 < len) {
+                f32x4 gt[2];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int s = s0 + 16 * st + 4 * grp + j;
-                    const float dec = __expf(cl - cs_s[s]) * dt_s[s];
-                    gf.set(4 * st + j, (s <= lrow && s < len) ? gt[st][j] * dec : 0.f);
+                for (int st = 0; st < 2; ++st) {
+                    gt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NK; ++ks) {
+                        Vec8<T> af;
+                        load8(af, BS + (16 * st + r16) * S::bs_pitch + 32 * ks + 8 * grp);
+                        mma(gt[st], af, cf[ks]);
+                    }
                 }
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                Vec8<T> xf;
-                load4(xf, 0, XT + (16 * pt + r16) * S::xt_pitch + 4 * grp);
-                load4(xf, 1, XT + (16 * pt + r16) * S::xt_pitch + 16 + 4 * grp);
-                mma(acc[pt], gf, xf);
+                for (int hh = 0; hh < HB; ++hh) {
+                    if (hh >= nh) break;
+                    const float cl = csl[hh * kMaxQ + lrow];
+                    Vec8<T> gf;
+#pragma unroll
+                    for (int st = 0; st < 2; ++st)
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int s = s0 + 16 * st + 4 * grp + j;
+                            const float dec = __expf(cl - csl[hh * kMaxQ + s]) * dth[hh * kMaxQ + s];
+                            gf.set(4 * st + j, (s <= lrow && s < len) ? gt[st][j] * dec : 0.f);
+                        }
+#pragma unroll
+                    for (int pt = 0; pt < P / 16; ++pt) {
+                        Vec8<T> xf;
+                        const T* xr = XT + (hh * P + 16 * pt + r16) * S::xt_pitch;
+                        load4(xf, 0, xr + 4 * grp);
+                        load4(xf, 1, xr + 16 + 4 * grp);
+                        mma(acc[hh][pt], gf, xf);
+                    }
+                }
             }
         }
     }
 
-    // ---- epilogue: y = acc + D x, staged through LDS for 16-byte accesses
-    __syncthreads();
+    // ---------------- epilogue, head by head: y = acc + D x through LDS for 16-byte accesses
 #pragma unroll
-    for (int pt = 0; pt < P / 16; ++pt)
+    for (int hh = 0; hh < HB; ++hh) {
+        if (hh >= nh) break;
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) OUT[(16 * wave + 4 * grp + j) * S::out_pitch + 16 * pt + r16] = acc[pt][j];
-    __syncthreads();
-    const float dh = Dv[h];
-    for (int i = tid; i < kRows * (P / 8); i += 256) {
-        const int r = i / (P / 8), o = i % (P / 8);
-        const int l = row0 + r;
-        if (l >= len) continue;
-        const int64_t off = ((b * seqlen + t0 + l) * nheads + h) * P + 8 * o;
-        Vec8<T> xv, yv;
-        load8(xv, x + off);
-        const float* src = OUT + r * S::out_pitch + 8 * o;
+        for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) yv.set(e, src[e] + dh * xv.get(e));
-        store8(y + off, yv);
+            for (int j = 0; j < 4; ++j) OUT[(16 * wave + 4 * grp + j) * S::out_pitch + 16 * pt + r16] = acc[hh][pt][j];
+        __syncthreads();
+        const int h = h0 + hh;
+        const float dh = Dv[h];
+        for (int i = tid; i < kRows * (P / 8); i += 256) {
+            const int r = i / (P / 8), o = i % (P / 8);
+            const int l = row0 + r;
+            if (l >= len) continue;
+            const int64_t off = ((b * seqlen + t0 + l) * nheads + h) * P + 8 * o;
+            Vec8<T> xv, yv;
+            load8(xv, x + off);
+            const float* src = OUT + r * S::out_pitch + 8 * o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) yv.set(e, src[e] + dh * xv.get(e));
+            store8(y + off, yv);
+        }
     }
 }
 
@@ -254,13 +315,17 @@ template <typename T, int P, int NK>
 hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
                   const float* D, T* y, const Dims& d, hipStream_t stream)
 {
+    constexpr int HB = heads_per_block(P, NK);
     const int nc = (int)d.nchunks();
     const int nlt = (int)((d.chunk + kRows - 1) / kRows);
-    const int64_t nblocks = d.batch * nc * d.nheads * nlt;
+    const int hpg = (int)(d.nheads / d.ngroups);
+    const int nhb = (hpg + HB - 1) / HB;                 // head blocks per group
+    const int hpw = (hpg + nhb - 1) / nhb;               // heads per workgroup, balanced
+    const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nlt;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK>), dim3((unsigned)nblocks), dim3(256), 0, stream, x, B,
-                       C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
-                       (int)d.dstate, (int)d.chunk, nc, nlt, (int)nblocks);
+    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, HB>), dim3((unsigned)nblocks), dim3(256), 0, stream, x,
+                       B, C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
+                       (int)d.dstate, (int)d.chunk, nc, nlt, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 
