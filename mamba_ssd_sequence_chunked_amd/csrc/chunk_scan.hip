@@ -29,7 +29,12 @@
 //     never multiplied.
 //   * the next 32 tokens' B and x (and the next head's S_in) are loaded into
 //     registers while the current tile is being multiplied, so global
-//     latency overlaps matrix-core work.
+//     latency overlaps matrix-core work.  Those loads are unconditional
+//     (indices clamped into the tensor) and the masks are applied when the
+//     registers are written to LDS, so no branch ever waits on a load.
+//   * x is kept in LDS in its natural (token, column) order; the G @ X
+//     operand, whose contraction runs over tokens, is read with the gfx950
+//     LDS transpose read, so no thread transposes data by hand.
 //   * y tiles are staged through LDS so every store, and the x read of the
 //     skip term, is a 16-byte vector access along the head dimension.
 // Workgroups are numbered row-tile fastest, then head block, group, chunk,
@@ -56,22 +61,25 @@ struct ScanSmem {
     static constexpr int NP = 32 * NK;                       // state width padded to the contraction block
     static constexpr bool kFullS = sizeof(T) * P * (NP + 8) <= 40 * 1024;
     static constexpr int SW = kFullS ? NP : 64;              // state columns of S_in per LDS stage
-    static constexpr int ss_pitch = SW + 8;
+    static constexpr int ss_pitch = SW + 8;                  // rows read as 16-byte fragments
     static constexpr int bs_pitch = NP + 8;
-    static constexpr int xt_pitch = kSB + 8;
+    static constexpr int xs_pitch = tr_pitch<T>(P);          // x tile read down its rows
     static constexpr int out_pitch = P + 4;
     static constexpr size_t ss_bytes = sizeof(T) * P * ss_pitch;
     static constexpr size_t bs_bytes = sizeof(T) * kSB * bs_pitch;
-    static constexpr size_t xt_bytes = sizeof(T) * HB * P * xt_pitch;
+    static constexpr size_t xs_bytes = sizeof(T) * HB * kSB * xs_pitch;
     static constexpr size_t out_bytes = sizeof(float) * kRows * out_pitch;
-    static constexpr size_t m1 = ss_bytes > bs_bytes + xt_bytes ? ss_bytes : bs_bytes + xt_bytes;
+    static constexpr size_t m1 = ss_bytes > bs_bytes + xs_bytes ? ss_bytes : bs_bytes + xs_bytes;
     static constexpr size_t region = m1 > out_bytes ? m1 : out_bytes;
     static constexpr size_t dec_bytes = 2 * sizeof(float) * HB * kMaxQ;
     static constexpr size_t total = dec_bytes + region;
-    // register-prefetch shares per thread (256 threads)
-    static constexpr int s_items = (P * SW / 8 + 255) / 256;           // Vec8 of one S_in stage
-    static constexpr int x_items = (HB * P + 255) / 256;               // 4 x 8 blocks of x
-    static constexpr int b_items = (kSB * NP / 8 + 255) / 256;         // Vec8 of B
+    // register-prefetch shares per thread (256 threads), 8 elements each
+    static constexpr int s_n = P * SW / 8;
+    static constexpr int x_n = HB * kSB * P / 8;
+    static constexpr int b_n = kSB * NP / 8;
+    static constexpr int s_items = (s_n + 255) / 256;
+    static constexpr int x_items = (x_n + 255) / 256;
+    static constexpr int b_items = (b_n + 255) / 256;
 };
 
 template <typename T, int P, int NK, int HB>
@@ -87,10 +95,10 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
     float* csh = reinterpret_cast<float*>(smem);                    // [HB][kMaxQ]
     float* dth = csh + HB * kMaxQ;                                  // [HB][kMaxQ]
     unsigned char* region = smem + S::dec_bytes;
-    T* SS = reinterpret_cast<T*>(region);                           // inter phase
-    T* BS = reinterpret_cast<T*>(region);                           // intra phase
-    T* XT = reinterpret_cast<T*>(region + S::bs_bytes);             // intra phase [HB][P][xt_pitch]
-    float* OUT = reinterpret_cast<float*>(region);                  // epilogue
+    T* SS = reinterpret_cast<T*>(region);                           // inter phase [P][ss_pitch]
+    T* BS = reinterpret_cast<T*>(region);                           // intra phase [kSB][bs_pitch]
+    T* XS = reinterpret_cast<T*>(region + S::bs_bytes);             // intra phase [HB][kSB][xs_pitch]
+    float* OUT = reinterpret_cast<float*>(region);                  // epilogue [kRows][out_pitch]
 
     int id = xcd_logical_block(blockIdx.x, nblocks);
     const int lt = id % nlt; id /= nlt;
@@ -112,22 +120,24 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
 
     for (int i = tid; i < HB * kMaxQ; i += 256) {
         const int hh = i / kMaxQ, l = i % kMaxQ;
-        float cv = 0.f, dv = 0.f;
-        if (hh < nh && l < Q) {
-            const int64_t o = (((int64_t)b * nheads + h0 + hh) * nc + c) * Q + l;
-            cv = dA_cs[o];
-            dv = dt_chunked[o];
-        }
-        csh[i] = cv;
-        dth[i] = dv;
+        const int64_t o = (((int64_t)b * nheads + h0 + min(hh, nh - 1)) * nc + c) * Q + min(l, Q - 1);
+        const float cv = dA_cs[o], dv = dt_chunked[o];
+        const bool ok = hh < nh && l < Q;
+        csh[i] = select(ok, cv, 0.f);
+        dth[i] = select(ok, dv, 0.f);
     }
 
+    // C rows of this wavefront as operand fragments (state axis = contraction slots)
     Vec8<T> cf[NK];
+    {
+        const T* crow = Cm + ((b * seqlen + t0 + min(lrow, len - 1)) * ngroups + g) * N;
 #pragma unroll
-    for (int ks = 0; ks < NK; ++ks) {
-        const int n = 32 * ks + 8 * grp;
-        if (lrow < len && n < N) load8(cf[ks], Cm + ((b * seqlen + t0 + lrow) * ngroups + g) * N + n);
-        else cf[ks].zero();
+        for (int ks = 0; ks < NK; ++ks) {
+            const int n = 32 * ks + 8 * grp;
+            load8(cf[ks], crow + min(n, N - 8));
+        }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) cf[ks] = masked(cf[ks], lrow < len && 32 * ks + 8 * grp < N);
     }
 
     f32x4 acc[HB][P / 16];
@@ -145,11 +155,9 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
             const T* src = entry + ent0 + (int64_t)hh * P * N;
 #pragma unroll
             for (int k = 0; k < S::s_items; ++k) {
-                const int i = tid + 256 * k;
+                const int i = min(tid + 256 * k, S::s_n - 1);
                 const int p = i / (SW / 8), o = i % (SW / 8);
-                const int n = sl * SW + 8 * o;
-                if (i < P * SW / 8 && n < N) load8(pf[k], src + (int64_t)p * N + n);
-                else pf[k].zero();
+                load8(pf[k], src + (int64_t)p * N + min(sl * SW + 8 * o, N - 8));
             }
         };
         fetch_s(0, 0);
@@ -165,7 +173,8 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
 #pragma unroll
                 for (int k = 0; k < S::s_items; ++k) {
                     const int i = tid + 256 * k;
-                    if (i < P * SW / 8) store8(SS + (i / (SW / 8)) * S::ss_pitch + 8 * (i % (SW / 8)), pf[k]);
+                    const int p = i / (SW / 8), o = i % (SW / 8);
+                    if (i < S::s_n) store8(SS + p * S::ss_pitch + 8 * o, masked(pf[k], sl * SW + 8 * o < N));
                 }
                 __syncthreads();
                 if (sl + 1 < nslab) fetch_s(hh, sl + 1);
@@ -181,9 +190,8 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
                     }
                 }
             }
-            float sc[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) sc[j] = __expf(csh[hh * kMaxQ + lw0 + 4 * grp + j]);
+            const float4 c4 = *reinterpret_cast<const float4*>(csh + hh * kMaxQ + lw0 + 4 * grp);
+            const float sc[4] = {__expf(c4.x), __expf(c4.y), __expf(c4.z), __expf(c4.w)};
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
@@ -195,34 +203,25 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
     {
         const int s_end = min(len, row0 + kRows);
         const int nsb = (s_end + kSB - 1) / kSB;
-        Vec8<T> px[S::x_items][4];
+        Vec8<T> px[S::x_items];
         Vec8<T> pb[S::b_items];
+        // loads always hit valid addresses (indices clamped); masks are applied when storing to LDS
         auto fetch = [&](int s0) {
 #pragma unroll
             for (int k = 0; k < S::x_items; ++k) {
-                const int i = tid + 256 * k;                 // (head, 4-token group, 8-column group)
-                const int hh = i / P, q = (i % P) / (P / 8), o = i % (P / 8);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int s = s0 + 4 * q + r;
-                    if (i < HB * P && hh < nh && s < len)
-                        load8(px[k][r], x + ((b * seqlen + t0 + s) * nheads + h0 + hh) * P + 8 * o);
-                    else
-                        px[k][r].zero();
-                }
+                const int i = min(tid + 256 * k, S::x_n - 1);     // (head, token, 8-column group)
+                const int hh = i / (kSB * P / 8), r = (i / (P / 8)) % kSB, o = i % (P / 8);
+                const int s = min(s0 + r, len - 1);
+                load8(px[k], x + ((b * seqlen + t0 + s) * nheads + h0 + min(hh, nh - 1)) * P + 8 * o);
             }
 #pragma unroll
             for (int k = 0; k < S::b_items; ++k) {
-                const int i = tid + 256 * k;                 // (token, 8-column group)
+                const int i = min(tid + 256 * k, S::b_n - 1);     // (token, 8-column group)
                 const int r = i / (NP / 8), o = i % (NP / 8);
-                const int s = s0 + r;
-                if (i < kSB * NP / 8 && s < len && 8 * o < N)
-                    load8(pb[k], Bm + ((b * seqlen + t0 + s) * ngroups + g) * N + 8 * o);
-                else
-                    pb[k].zero();
+                const int s = min(s0 + r, len - 1);
+                load8(pb[k], Bm + ((b * seqlen + t0 + s) * ngroups + g) * N + min(8 * o, N - 8));
             }
         };
-        const float* csl = csh;
         if (nsb > 0) fetch(0);
         for (int sb = 0; sb < nsb; ++sb) {
             const int s0 = sb * kSB;
@@ -230,19 +229,15 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
 #pragma unroll
             for (int k = 0; k < S::x_items; ++k) {
                 const int i = tid + 256 * k;
-                if (i < HB * P) {
-                    const int hh = i / P, q = (i % P) / (P / 8), o = i % (P / 8);
-                    T* dst = XT + (hh * P + 8 * o) * S::xt_pitch + 4 * q;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        store4(dst + e * S::xt_pitch, px[k][0].get(e), px[k][1].get(e), px[k][2].get(e),
-                               px[k][3].get(e));
-                }
+                const int hh = i / (kSB * P / 8), r = (i / (P / 8)) % kSB, o = i % (P / 8);
+                if (i < S::x_n)
+                    store8(XS + (hh * kSB + r) * S::xs_pitch + 8 * o, masked(px[k], hh < nh && s0 + r < len));
             }
 #pragma unroll
             for (int k = 0; k < S::b_items; ++k) {
                 const int i = tid + 256 * k;
-                if (i < kSB * NP / 8) store8(BS + (i / (NP / 8)) * S::bs_pitch + 8 * (i % (NP / 8)), pb[k]);
+                const int r = i / (NP / 8), o = i % (NP / 8);
+                if (i < S::b_n) store8(BS + r * S::bs_pitch + 8 * o, masked(pb[k], s0 + r < len && 8 * o < N));
             }
             __syncthreads();
             if (sb + 1 < nsb) fetch(s0 + kSB);
@@ -261,22 +256,27 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
                     if (hh >= nh) break;
-                    const float cl = csl[hh * kMaxQ + lrow];
+                    const float* csr = csh + hh * kMaxQ;
+                    const float* dtr = dth + hh * kMaxQ;
+                    const float cl = csr[lrow];
                     Vec8<T> gf;
 #pragma unroll
-                    for (int st = 0; st < 2; ++st)
+                    for (int st = 0; st < 2; ++st) {
+                        const int sb4 = s0 + 16 * st + 4 * grp;
+                        const float4 c4 = *reinterpret_cast<const float4*>(csr + sb4);
+                        const float4 d4 = *reinterpret_cast<const float4*>(dtr + sb4);
+                        const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
-                            const int s = s0 + 16 * st + 4 * grp + j;
-                            const float dec = __expf(cl - csl[hh * kMaxQ + s]) * dth[hh * kMaxQ + s];
-                            gf.set(4 * st + j, (s <= lrow && s < len) ? gt[st][j] * dec : 0.f);
+                            const float v = gt[st][j] * (__expf(cl - cv[j]) * dv[j]);
+                            gf.set(4 * st + j, select(sb4 + j <= lrow, v, 0.f));
                         }
+                    }
+                    const T* xh = XS + hh * kSB * S::xs_pitch;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> xf;
-                        const T* xr = XT + (hh * P + 16 * pt + r16) * S::xt_pitch;
-                        load4(xf, 0, xr + 4 * grp);
-                        load4(xf, 1, xr + 16 + 4 * grp);
+                        load_row_slots(xf, xh, S::xs_pitch, 0, 16 * pt);
                         mma(acc[hh][pt], gf, xf);
                     }
                 }

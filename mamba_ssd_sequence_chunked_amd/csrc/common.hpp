@@ -10,6 +10,9 @@
 //   contract the same 32 (g, i) slots, so which index a slot stands for is
 //   the caller's choice as long as A and B agree.  The accumulator layout
 //   (both types) is: lane 16 * g + c holds rows 4g .. 4g+3 of column c.
+// * contraction slots along the rows of a row-major LDS tile: for bf16 two
+//   gfx950 transpose reads (ds_read_b64_tr_b16) deliver them directly in
+//   operand order; for fp32, eight scalar LDS reads.
 // * a wavefront inclusive prefix sum built from DPP row shifts and row
 //   broadcasts (64 lanes, no LDS).
 // * an XCD-aware block index: the dispatcher hands consecutive workgroups
@@ -103,6 +106,62 @@ __device__ __forceinline__ void mma(f32x4& acc, const Vec8<bf16>& a, const Vec8<
 __device__ __forceinline__ void mma(f32x4& acc, const Vec8<float>& a, const Vec8<float>& b) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// Operand fragment whose 8 contraction slots run down the ROWS of a row-major
+// LDS tile: lane 16 * g + r receives column c0 + r of rows k0 + 4g + m (slots
+// 0..3) and k0 + 16 + 4g + m (slots 4..7), m = 0..3.  The bf16 form uses the
+// gfx950 transpose read: in every 16-lane group, lane i receives element i % 4
+// of the 8-byte chunks read by lanes i / 4 + 4 m, so lane j of the group reads
+// row k0 + 4g + j / 4 at columns c0 + 4 (j % 4) .. + 3.  Rows k0 .. k0 + 31 and
+// columns c0 .. c0 + 15 must lie inside the tile; the row pitch must keep
+// 8-byte alignment.
+__device__ __forceinline__ void load_row_slots(Vec8<bf16>& f, const bf16* tile, int pitch, int k0, int c0) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const bf16* p0 = tile + (k0 + 4 * g + (r >> 2)) * pitch + c0 + 4 * (r & 3);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(p0 + 16 * pitch));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = __builtin_bit_cast(bf16x8, ab);
+}
+__device__ __forceinline__ void load_row_slots(Vec8<float>& f, const float* tile, int pitch, int k0, int c0) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const float* p0 = tile + (k0 + 4 * g) * pitch + c0 + r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        f.v[m] = p0[m * pitch];
+        f.v[4 + m] = p0[(16 + m) * pitch];
+    }
+}
+
+// Row pitch (elements) for a tile read with load_row_slots: the 16-byte row
+// segments of 8 consecutive rows then fall in distinct LDS banks.
+template <typename T>
+constexpr int tr_pitch(int width) {
+    return sizeof(T) == 2 ? ((width / 16) % 2 == 0 ? width + 16 : width) : width + 4;
+}
+
+// Select without a branch (the masked value is computed but discarded).
+__device__ __forceinline__ float select(bool c, float a, float b) { return c ? a : b; }
+
+// v if ok, else zeros, without a branch (so a load into v never has to be
+// waited for on a path that overwrites the same registers).
+__device__ __forceinline__ Vec8<bf16> masked(const Vec8<bf16>& v, bool ok) {
+    Vec8<bf16> r;
+    const uint4 u = __builtin_bit_cast(uint4, v.v);
+    const uint4 z = make_uint4(ok ? u.x : 0u, ok ? u.y : 0u, ok ? u.z : 0u, ok ? u.w : 0u);
+    r.v = __builtin_bit_cast(bf16x8, z);
+    return r;
+}
+__device__ __forceinline__ Vec8<float> masked(const Vec8<float>& v, bool ok) {
+    Vec8<float> r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r.v[i] = ok ? v.v[i] : 0.f;
+    return r;
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (lane order).
