@@ -164,6 +164,114 @@ __device__ __forceinline__ Vec8<float> masked(const Vec8<float>& v, bool ok) {
     return r;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Swizzled LDS tiles filled by asynchronous global->LDS loads.
+//
+// A tile is R rows of CH 16-byte chunks (CH a power of two).  Logical chunk c
+// of row r lives at slot c ^ (r & M), M = min(CH, 16) - 1, so 16 rows read at
+// one column, or 8 rows read 8 bytes apiece through the transpose read, fall
+// in distinct banks.  The tile is filled with gfx950 global_load_lds_dwordx4:
+// one wavefront instruction writes 64 consecutive chunks (lane i -> chunk
+// slot i of that 1 KB), so each lane loads the global chunk that belongs in
+// its slot.  R * CH must be a multiple of 64.
+template <int CH>
+struct SwzTile {
+    static constexpr int kMask = (CH < 16 ? CH : 16) - 1;
+    static constexpr int kRowBytes = CH * 16;
+    __device__ __forceinline__ static int offset(int r, int c) { return r * kRowBytes + ((c ^ (r & kMask)) << 4); }
+};
+
+// One 16-byte global->LDS load per lane: lane i's data goes to lds_base +
+// 16 i (lds_base wave-uniform).  Issued through inline asm so that the
+// compiler's wait-count bookkeeping does not treat every later LDS read as
+// possibly aliasing the in-flight copy (it cannot tell the two stage buffers
+// apart and would wait for the prefetch before any LDS read); the kernels
+// order these copies explicitly with wait_vmem() and a barrier.  M0 carries
+// the LDS address and is restored right after the issue.
+__device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_base) {
+    const unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+    unsigned saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(gsrc), "s"(a)
+                 : "memory");
+}
+
+// Issue the loads of one tile: src(r, c) returns the global address of logical
+// chunk c of row r (it must always be a valid address).  Returns nothing; the
+// data is in LDS once this wave's vmcnt reaches zero and a barrier has passed.
+template <int CH, int R, class F>
+__device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
+    using TL = SwzTile<CH>;
+    constexpr int kInst = R * CH / 64;                 // wavefront instructions for the tile
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int q = wave; q < kInst; q += 4) {
+        const int pos = q * 64 + lane;
+        const int r = pos / CH, slot = pos % CH;
+        const int c = slot ^ (r & TL::kMask);
+        dma16(src(r, c), tile + q * 1024);
+    }
+}
+
+// Wait for all of this wavefront's outstanding vector-memory operations.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Fragment of 8 consecutive elements along a row of a swizzled tile (columns
+// c0 .. c0+7, c0 a multiple of 8 for bf16 / 4 for fp32).
+template <int CH>
+__device__ __forceinline__ void swz_load8(Vec8<bf16>& f, const unsigned char* tile, int r, int c0) {
+    f.v = *reinterpret_cast<const bf16x8*>(tile + SwzTile<CH>::offset(r, c0 >> 3));
+}
+template <int CH>
+__device__ __forceinline__ void swz_load8(Vec8<float>& f, const unsigned char* tile, int r, int c0) {
+    const float4 a = *reinterpret_cast<const float4*>(tile + SwzTile<CH>::offset(r, c0 >> 2));
+    const float4 b = *reinterpret_cast<const float4*>(tile + SwzTile<CH>::offset(r, (c0 >> 2) + 1));
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// 4 consecutive elements along a row (c0 a multiple of 4), as floats.
+template <int CH>
+__device__ __forceinline__ float4 swz_load4f(const bf16* tile_, int r, int c0) {
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(tile_);
+    const bf16x4 q = *reinterpret_cast<const bf16x4*>(tile + SwzTile<CH>::offset(r, c0 >> 3) + 2 * (c0 & 7));
+    return make_float4((float)q[0], (float)q[1], (float)q[2], (float)q[3]);
+}
+template <int CH>
+__device__ __forceinline__ float4 swz_load4f(const float* tile_, int r, int c0) {
+    const unsigned char* tile = reinterpret_cast<const unsigned char*>(tile_);
+    return *reinterpret_cast<const float4*>(tile + SwzTile<CH>::offset(r, c0 >> 2));
+}
+
+// Fragment whose 8 contraction slots run down the rows of a swizzled tile
+// (the slot layout of load_row_slots): lane 16 g + r gets column c0 + r of
+// rows k0 + 4g + m and k0 + 16 + 4g + m, m = 0..3.
+template <int CH>
+__device__ __forceinline__ void swz_row_slots(Vec8<bf16>& f, const unsigned char* tile, int k0, int c0) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int row = k0 + 4 * g + (r >> 2);
+    const int col = c0 + 4 * (r & 3);                          // 4 elements = 8 bytes, inside one chunk
+    const unsigned char* p0 = tile + SwzTile<CH>::offset(row, col >> 3) + 2 * (col & 7);
+    const unsigned char* p1 = tile + SwzTile<CH>::offset(row + 16, col >> 3) + 2 * (col & 7);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p1));
+    const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    f.v = __builtin_bit_cast(bf16x8, ab);
+}
+template <int CH>
+__device__ __forceinline__ void swz_row_slots(Vec8<float>& f, const unsigned char* tile, int k0, int c0) {
+    const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+    const int col = c0 + r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int r0 = k0 + 4 * g + m, r1 = r0 + 16;
+        f.v[m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r0, col >> 2) + 4 * (col & 3));
+        f.v[4 + m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r1, col >> 2) + 4 * (col & 3));
+    }
+}
+
 // Inclusive prefix sum over the 64 lanes of a wavefront (lane order).
 __device__ __forceinline__ float wave_inclusive_sum(float v) {
     // rows of 16: shift right by 1, 2, 4, 8 (lanes shifted in from outside the row read 0)

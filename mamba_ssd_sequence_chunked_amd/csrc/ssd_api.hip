@@ -4,7 +4,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "common.hpp"
 #include "kernels.hpp"
 
