@@ -9,36 +9,40 @@
 // entering the chunk, decayed to position l (that blog's block-decomposition
 // outline adds it before the state moves on); the third is the skip term.
 //
-// Workgroup = (batch, chunk, group, 64-row tile of the chunk, up to 256/P
-// heads of the group); 4 wavefronts, each owning 16 rows of y for every one
-// of those heads.  Everything runs on the matrix cores with fp32
-// accumulation, and the products are formed transposed (y^T = X^T G^T and
-// S_in C^T), so each lane ends up holding 4 consecutive head-dimension values
-// of one row:
+// Workgroup = (batch, chunk, group, up to HB heads of the group): all rows of
+// the chunk.  8 wavefronts; wavefront w owns row blocks w and nrb-1-w (16 rows
+// each), which gives every wavefront the same amount of causal work.  All
+// products run on the matrix cores with fp32 accumulation and are formed
+// transposed (y^T = X^T G^T and S_in C^T), so a lane holds 4 consecutive
+// head-dimension values of one row:
 //   * C rows of a wavefront are read once from global memory straight into
 //     operand fragments (the state axis is contiguous, and it is the
 //     contraction axis of both C.B^T and S_in.C^T) and kept in registers.
-//   * inter term, head by head: S_in of the head is the A operand, read from
-//     LDS; columns (rows of y) are scaled by exp(cs[l]).
-//   * intra term, 32 source tokens per stage: G^T (tokens x rows) = B_s C^T
-//     is computed ONCE for all the heads of the workgroup (B and C belong to
-//     the group), then each head applies its own decay and dt in fp32, and
-//     the result, still in the accumulator layout, is the B operand of
-//     X_s^T G^T: no shuffle, no LDS round trip.  Entries above the diagonal
-//     are selected to zero, never multiplied.
-//   * every tile (S_in, x, B) reaches LDS through asynchronous global->LDS
-//     loads into two alternating buffers: the next stage is in flight while
-//     the current one is multiplied, and no register holds staged data.
-//     Tiles are XOR-swizzled by 16-byte chunk, so the 16-byte operand reads
-//     and the transpose reads (x is kept in natural token-major order and
-//     read token-wise with ds_read_b64_tr_b16) are bank-conflict free.
-//     Out-of-range rows are loaded from a clamped, valid address; their
-//     products are removed by the causal mask or by zero C entries.
-//   * the skip term D x reads x from the last two stages' tiles, which hold
-//     exactly this workgroup's rows; y is then staged through LDS so it
-//     leaves as full 16-byte row segments (8 lanes per 128-byte row).
-// Workgroups are numbered row-tile fastest, then head block, group, chunk,
-// and renumbered so that consecutive ones share an XCD and its L2.
+//   * the heads' S_in tiles and the source tokens' x and B tiles reach LDS
+//     through asynchronous global->LDS copies; source tokens stream through a
+//     3-deep ring of 32-token stages, so two stages are in flight while one
+//     is multiplied, and every byte of x, B and S_in is read once per
+//     workgroup.  Tiles are XOR-swizzled by 16-byte chunk, so the 16-byte
+//     operand reads and the transpose reads (x is kept token-major and read
+//     token-wise with ds_read_b64_tr_b16) are bank-conflict free.  Rows past
+//     the sequence are copied from a clamped, valid address; their products
+//     are removed by the causal mask or by zero C entries.
+//   * intra term, per stage and row block: G^T (tokens x rows) = B_s C^T is
+//     computed once for all the heads of the workgroup (B and C belong to the
+//     group); each head applies its decay and dt in fp32 and the result, still
+//     in the accumulator layout, is the B operand of X_s^T G^T.  For a stage
+//     wholly before the row block the decay is split at the stage's last
+//     token e: exp(cs[l] - cs[e]) per row times a per-token factor
+//     exp(cs[e] - cs[s]) dt_s tabulated once per workgroup (both exponents
+//     are <= 0); the stage holding the rows uses the full per-entry decay and
+//     the causal mask (entries above the diagonal are selected to zero, never
+//     multiplied).
+//   * the epilogue stages y^T of one head at a time through LDS, adds D x with
+//     16-byte reads of x and writes full 16-byte segments of y rows.
+// Workgroups are numbered head block fastest and renumbered so that
+// consecutive ones share an XCD (and the chunk's B and C in its L2).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -46,58 +50,78 @@ namespace ssd {
 
 namespace {
 
-constexpr int kRows = 64;     // rows of y per workgroup
-constexpr int kSB = 32;       // source tokens per intra step
+constexpr int kSB = 32;        // source tokens per stage
 constexpr int kMaxQ = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
-template <typename T, int P, int NK, int HB> struct ScanCfg;
-
-// heads per workgroup: 256 / P (at most 8), so the y accumulators stay at
-// 64 registers per lane whatever the head dimension, halved while the
-// workgroup's LDS would not fit twice in a CU (bf16) or once (fp32).
-template <typename T, int P, int NK, int HB = (256 / P > 8 ? 8 : 256 / P)>
-constexpr int heads_per_block() {
-    if constexpr (HB > 1 && ScanCfg<T, P, NK, HB>::total > (sizeof(T) == 2 ? 80 : 160) * 1024)
-        return heads_per_block<T, P, NK, HB / 2>();
-    else
-        return HB;
-}
-
-template <typename T, int P, int NK, int HB>
+template <typename T, int P, int NK, int HB, int STG, int SW>
 struct ScanCfg {
+    static constexpr int kHeads = HB;
+    static constexpr int kStages = STG;                            // depth of the source-token ring
     static constexpr int EPC = 16 / (int)sizeof(T);               // elements per 16-byte chunk
     static constexpr int NP = 32 * NK;                             // state width padded to the contraction block
-    static constexpr int SW = (P * NP * (int)sizeof(T) <= 32 * 1024) ? NP
-                            : (P * 128 * (int)sizeof(T) <= 32 * 1024 ? 128 : 64);
-    static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in row
+    static constexpr int SWD = SW;                                 // state columns of S_in per LDS slab
+    static constexpr int NSL = NP / SW;                            // slabs
     static constexpr int X_CH = P * (int)sizeof(T) / 16;           // chunks per x row
     static constexpr int B_CH = NP * (int)sizeof(T) / 16;          // chunks per B row
-    static constexpr int s_bytes = P * SW * (int)sizeof(T);        // one S_in stage
+    static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in slab row
+    static constexpr int O_CH = P * 4 / 16;                        // chunks per fp32 y row
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
-    static constexpr int xb_bytes = HB * xh_bytes + kSB * NP * (int)sizeof(T);
-    static constexpr int region = 2 * (s_bytes > xb_bytes ? s_bytes : xb_bytes);
-    static constexpr int dec_bytes = 3 * (int)sizeof(float) * HB * kMaxQ;    // cs, dt, source factors
-    static constexpr int total = dec_bytes + region;
+    static constexpr int b_bytes = kSB * NP * (int)sizeof(T);
+    static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
+    static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head
+    static constexpr int ring_bytes = STG * stage_bytes;
+    static constexpr int main_bytes = ring_bytes + HB * sh_bytes;
+    static constexpr int out_bytes = kMaxQ * P * 4;                 // one head's fp32 y^T staging
+    static constexpr int region = main_bytes > out_bytes ? main_bytes : out_bytes;
+    static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ;           // cs, dt, per-token decay factor
+    static constexpr int total = tab_bytes + region;
+    static constexpr bool fits = total <= 160 * 1024;
+    // asynchronous copy instructions per wavefront per stage (uniform when divisible)
+    static constexpr int x_inst = HB * kSB * X_CH / 64;             // dealt over all waves as one sequence
+    static constexpr int b_inst = kSB * B_CH / 64;
+    static constexpr bool uniform = x_inst % kWaves == 0 && b_inst % kWaves == 0;
+    static constexpr int per_wave = uniform ? (x_inst + b_inst) / kWaves : 0;
 };
 
-template <typename T, int P, int NK, int HB>
-__global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
+// Launch shape for (T, P, NK): heads per workgroup keep the y accumulators
+// (2 row blocks x HB heads x P columns) at 128 registers per lane (64 with the
+// widest state, whose C fragments take the room); while the LDS does not fit
+// in a CU, first the heads, then the ring depth, then the S_in slab width are
+// halved.
+template <class C> struct TypeBox { using type = C; };
+
+template <typename T, int P, int NK, int HB, int STG, int SW>
+constexpr auto pick_shape() {
+    using C = ScanCfg<T, P, NK, HB, STG, SW>;
+    if constexpr (C::fits) return TypeBox<C>{};
+    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2, STG, SW>();
+    else if constexpr (STG > 2) return pick_shape<T, P, NK, 1, STG - 1, SW>();
+    else if constexpr (SW > 32) return pick_shape<T, P, NK, 1, 2, SW / 2>();
+    else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
+}
+
+template <typename T, int P, int NK>
+using ScanShape = typename decltype(pick_shape<T, P, NK,
+    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), 3, 32 * NK>())::type;
+
+template <typename T, int P, int NK, class S>
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, const float* __restrict__ Dv, T* __restrict__ y, int seqlen,
-    int nheads, int ngroups, int N, int Q, int nc, int nlt, int nhb, int hpw, int nblocks)
+    int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nblocks)
 {
-    using S = ScanCfg<T, P, NK, HB>;
-    constexpr int EPC = S::EPC, SW = S::SW, NP = S::NP;
-    __shared__ float csh[HB * kMaxQ];
-    __shared__ float dth[HB * kMaxQ];
-    // vsrc[hh][s] = exp(cs[row0] - cs[s]) dt[s] for s < row0: the source side of the decay of
-    // every source block before this workgroup's first row (0 elsewhere)
-    __shared__ float vsrc[HB * kMaxQ];
-    __shared__ __attribute__((aligned(1024))) unsigned char region[S::region];   // two stage buffers
+    constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
+    __shared__ float cst[HB * kMaxQ];
+    __shared__ float dtt[HB * kMaxQ];
+    __shared__ float vst[HB * kMaxQ];          // exp(cs[e(s)] - cs[s]) dt[s], e(s) = last token of s's stage
+    __shared__ __attribute__((aligned(1024))) unsigned char region[S::region];
+    unsigned char* const ring = region;
+    unsigned char* const stile = region + S::ring_bytes;
 
     int id = xcd_logical_block(blockIdx.x, nblocks);
-    const int lt = id % nlt; id /= nlt;
     const int hb = id % nhb; id /= nhb;
     const int g = id % ngroups; id /= ngroups;
     const int c = id % nc;
@@ -107,237 +131,231 @@ __global__ __launch_bounds__(256, 2) void chunk_scan_kernel(
     const int nh = min(hpw, hpg - hb * hpw);                       // heads of this workgroup (<= HB)
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, (int64_t)seqlen - t0);
-    const int row0 = lt * kRows;
+    const int nsb = (len + kSB - 1) / kSB;
+    const int nrb = Q / 16;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int r16 = lane & 15, grp = lane >> 4;
-    const int lw0 = row0 + 16 * wave;
-    const int lrow = lw0 + r16;                                     // the y row this lane owns
+    // this wavefront's row blocks (wave-uniform)
+    const int rbk[2] = {wave, nrb - 1 - wave};
+    const bool has[2] = {wave < nrb, nrb - 1 - wave > wave};
 
-    for (int i = tid; i < HB * kMaxQ; i += 256) {
+    // ---- asynchronous copies: the heads' S_in tiles (first slab), then the first stages of the ring
+    const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
+    auto issue_s = [&](int sl) {
+        tiles_load_async<S::S_CH, P, HB, kWaves>(stile, S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
+            return ent + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N + min(sl * SW + ch * EPC, N - EPC);
+        });
+    };
+    issue_s(0);
+    auto issue_stage = [&](int sb) {
+        const int s0 = sb * kSB;
+        unsigned char* stg = ring + (sb % kStages) * S::stage_bytes;
+        const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
+        tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
+            return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(hh, nh - 1) * P + ch * EPC;
+        });
+        const T* bg = Bm + (int64_t)g * N;
+        tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
+            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
+        });
+    };
+#pragma unroll
+    for (int sb = 0; sb < kStages - 1; ++sb)
+        if (sb < nsb) issue_stage(sb);
+
+    // ---- decay tables
+    for (int i = tid; i < HB * kMaxQ; i += kThreads) {
         const int hh = i / kMaxQ, l = i % kMaxQ;
         const int64_t o = (((int64_t)b * nheads + h0 + min(hh, nh - 1)) * nc + c) * Q + min(l, Q - 1);
         const float cv = dA_cs[o], dv = dt_chunked[o];
         const bool ok = hh < nh && l < Q;
-        csh[i] = select(ok, cv, 0.f);
-        dth[i] = select(ok, dv, 0.f);
+        cst[i] = select(ok, cv, 0.f);
+        dtt[i] = select(ok, dv, 0.f);
     }
-
+    // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots)
+    Vec8<T> cf[2][S::NP / 32];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int l = 16 * rbk[j] + r16;
+        const T* crow = Cm + ((b * seqlen + t0 + max(0, min(l, len - 1))) * ngroups + g) * N;
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) load8(cf[j][ks], crow + min(32 * ks + 8 * grp, N - 8));
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks) cf[j][ks] = masked(cf[j][ks], has[j] && l < len && 32 * ks + 8 * grp < N);
+    }
     __syncthreads();
-    for (int i = tid; i < HB * kMaxQ; i += 256) {
+    for (int i = tid; i < HB * kMaxQ; i += kThreads) {
         const int hh = i / kMaxQ, sidx = i % kMaxQ;
-        const float v = __expf(csh[hh * kMaxQ + row0] - csh[i]) * dth[i];
-        vsrc[i] = select(sidx < row0, v, 0.f);
+        const int e = min(kSB * (sidx / kSB) + kSB - 1, kMaxQ - 1);
+        vst[i] = __expf(cst[hh * kMaxQ + e] - cst[i]) * dtt[i];
     }
+    wait_vmem();                   // S_in tiles, the first stages, the tables' and C's loads
+    __syncthreads();
 
-    // C rows of this wavefront as operand fragments (state axis = contraction slots)
-    Vec8<T> cf[NK];
-    {
-        const T* crow = Cm + ((b * seqlen + t0 + min(lrow, len - 1)) * ngroups + g) * N;
+    // y^T accumulators: acc[j][hh][pt] lane (r16, grp) holds y[16 rb_j + r16][16 pt + 4 grp + q]
+    f32x4 acc[2][HB][P / 16];
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) load8(cf[ks], crow + min(32 * ks + 8 * grp, N - 8));
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int ks = 0; ks < NK; ++ks) cf[ks] = masked(cf[ks], lrow < len && 32 * ks + 8 * grp < N);
-    }
+        for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt) acc[j][hh][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // y^T accumulators: lane (r16, grp) holds y[lrow][16 pt + 4 grp + j]
-    f32x4 acc[HB][P / 16];
+    // ---- inter-chunk term: exp(cs[l]) * S_in[p, :] . C_l (slab by slab when S_in does not fit whole)
 #pragma unroll
-    for (int hh = 0; hh < HB; ++hh)
+    for (int sl = 0; sl < S::NSL; ++sl) {
+        if (sl > 0) {
+            __syncthreads();
+            issue_s(sl);
+            wait_vmem();
+            __syncthreads();
+        }
 #pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) acc[hh][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // ---------------- inter-chunk term, head by head: exp(cs[l]) * S_in[p, :] . C_l
-    {
-        const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
-        constexpr int nslab = NP / SW;
-        auto issue = [&](int hh, int sl, int buf) {
-            const T* src = ent + (int64_t)hh * P * N;
-            tile_load_async<S::S_CH, P>(region + buf * S::s_bytes, [&](int r, int ch) -> const void* {
-                return src + (int64_t)r * N + min(sl * SW + ch * EPC, N - EPC);
-            });
-        };
-        issue(0, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+            if (!has[j]) continue;
 #pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-            if (hh >= nh) break;
-            f32x4 ai[P / 16];
+            for (int hh = 0; hh < HB; ++hh) {
+                if (hh >= nh) break;
+                const unsigned char* stl = stile + hh * S::sh_bytes;
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) ai[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int sl = 0; sl < nslab; ++sl) {
-                const int j = hh * nslab + sl;
-                wait_vmem();
-                __syncthreads();
-                if (sl + 1 < nslab) issue(hh, sl + 1, (j + 1) & 1);
-                else if (hh + 1 < nh) issue(hh + 1, 0, (j + 1) & 1);
-                const unsigned char* tile = region + (j & 1) * S::s_bytes;
-#pragma unroll
-                for (int kk = 0; kk < SW / 32; ++kk) {
-                    const int ks = sl * (SW / 32) + kk;
+                for (int kk = 0; kk < SW / 32; ++kk)
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> af;
-                        swz_load8<S::S_CH>(af, tile, 16 * pt + r16, 32 * kk + 8 * grp);
-                        mma(ai[pt], af, cf[ks]);
+                        swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
+                        mma(acc[j][hh][pt], af, cf[j][sl * (SW / 32) + kk]);
                     }
-                }
             }
-            // exp(cs[l]) = exp(cs[row0]) * exp(cs[l] - cs[row0]); the second factor is applied with
-            // the source blocks before row0 (both exponents are <= 0)
-            const float e = __expf(csh[hh * kMaxQ + row0]);
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        if (!has[j]) continue;
+        const int l = min(16 * rbk[j] + r16, kMaxQ - 1);
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+            if (hh >= nh) break;
+            const float e = __expf(cst[hh * kMaxQ + l]);
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[hh][pt][q] = e * ai[pt][q];
+                for (int q = 0; q < 4; ++q) acc[j][hh][pt][q] *= e;
         }
     }
 
-    // ---------------- intra-chunk term: y^T += X_s^T G^T, 32 source tokens per stage
-    const int s_end = min(len, row0 + kRows);
-    const int nsb = (s_end + kSB - 1) / kSB;
-    auto xtile = [&](int buf, int hh) { return region + buf * S::xb_bytes + hh * S::xh_bytes; };
-    auto issue_xb = [&](int s0, int buf) {
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-            const T* xh = x + (int64_t)(h0 + min(hh, nh - 1)) * P;
-            tile_load_async<S::X_CH, kSB>(xtile(buf, hh), [&](int r, int ch) -> const void* {
-                return xh + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)nheads * P + ch * EPC;
-            });
-        }
-        const T* bg = Bm + (int64_t)g * N;
-        tile_load_async<S::B_CH, kSB>(region + buf * S::xb_bytes + HB * S::xh_bytes,
-                                      [&](int r, int ch) -> const void* {
-            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
-        });
-    };
-    __syncthreads();                                  // the inter phase's buffers are free
-    if (nsb > 0) issue_xb(0, 0);
+    // ---- intra-chunk term, one 32-token stage at a time
     for (int sb = 0; sb < nsb; ++sb) {
         const int s0 = sb * kSB;
-        wait_vmem();
-        __syncthreads();
-        if (sb + 1 < nsb) issue_xb(s0 + kSB, (sb + 1) & 1);
-        if (s0 <= lw0 + 15 && lw0 < len) {
-            const unsigned char* bt = region + (sb & 1) * S::xb_bytes + HB * S::xh_bytes;
+        if (sb > 0) {
+            if (S::uniform && sb + 1 < nsb) wait_vmem_below<S::per_wave>();   // stage sb landed; sb+1 may fly
+            else wait_vmem();
+            __syncthreads();
+        }
+        if (sb + kStages - 1 < nsb) issue_stage(sb + kStages - 1);
+        const unsigned char* stg = ring + (sb % kStages) * S::stage_bytes;
+        const unsigned char* bt = stg + HB * S::xh_bytes;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int lb = 16 * rbk[j];                           // first row of the block
+            if (!has[j] || lb + 15 < s0 || lb >= len) continue;   // block not reached yet / empty
+            const int lrow = lb + r16;
             f32x4 gt[2];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                gt[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int st2 = 0; st2 < 2; ++st2) {
+                gt[st2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NK; ++ks) {
                     Vec8<T> af;
-                    swz_load8<S::B_CH>(af, bt, 16 * st + r16, 32 * ks + 8 * grp);
-                    mma(gt[st], af, cf[ks]);
+                    swz_load8<S::B_CH>(af, bt, 16 * st2 + r16, 32 * ks + 8 * grp);
+                    mma(gt[st2], af, cf[j][ks]);
                 }
             }
-            if (s0 + kSB <= row0) {
-                // a block strictly before this workgroup's rows: G = C.B * vsrc[s]
+            if (s0 + kSB <= lb) {
+                // the stage lies wholly before the block: G = C.B * exp(cs[l] - cs[e]) * vst[s]
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
                     if (hh >= nh) break;
-                    const float* vr = vsrc + hh * kMaxQ;
+                    const float u = __expf(cst[hh * kMaxQ + lrow] - cst[hh * kMaxQ + s0 + kSB - 1]);
+                    const float* vr = vst + hh * kMaxQ + s0 + 4 * grp;
+                    const float4 va = *reinterpret_cast<const float4*>(vr);
+                    const float4 vb = *reinterpret_cast<const float4*>(vr + 16);
                     Vec8<T> gf;
-#pragma unroll
-                    for (int st = 0; st < 2; ++st) {
-                        const float4 v4 = *reinterpret_cast<const float4*>(vr + s0 + 16 * st + 4 * grp);
-                        gf.set(4 * st + 0, gt[st][0] * v4.x);
-                        gf.set(4 * st + 1, gt[st][1] * v4.y);
-                        gf.set(4 * st + 2, gt[st][2] * v4.z);
-                        gf.set(4 * st + 3, gt[st][3] * v4.w);
-                    }
-                    const unsigned char* xt = xtile(sb & 1, hh);
+                    gf.set(0, gt[0][0] * (u * va.x)); gf.set(1, gt[0][1] * (u * va.y));
+                    gf.set(2, gt[0][2] * (u * va.z)); gf.set(3, gt[0][3] * (u * va.w));
+                    gf.set(4, gt[1][0] * (u * vb.x)); gf.set(5, gt[1][1] * (u * vb.y));
+                    gf.set(6, gt[1][2] * (u * vb.z)); gf.set(7, gt[1][3] * (u * vb.w));
+                    const unsigned char* xt = stg + hh * S::xh_bytes;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> xf;
                         swz_row_slots<S::X_CH>(xf, xt, 0, 16 * pt);
-                        mma(acc[hh][pt], xf, gf);
+                        mma(acc[j][hh][pt], xf, gf);
                     }
                 }
             } else {
-                // a block inside this workgroup's 64 rows: on the first one, apply the row side
-                // exp(cs[l] - cs[row0]) to everything accumulated so far; then add the block with the
-                // full per-entry decay and the causal mask
-                if (s0 == row0) {
-#pragma unroll
-                    for (int hh = 0; hh < HB; ++hh) {
-                        if (hh >= nh) break;
-                        const float u = __expf(csh[hh * kMaxQ + lrow] - csh[hh * kMaxQ + row0]);
-#pragma unroll
-                        for (int pt = 0; pt < P / 16; ++pt)
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) acc[hh][pt][q] *= u;
-                    }
-                }
+                // the stage holding the block's rows: full per-entry decay and the causal mask
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
                     if (hh >= nh) break;
-                    const float* csr = csh + hh * kMaxQ;
-                    const float* dtr = dth + hh * kMaxQ;
+                    const float* csr = cst + hh * kMaxQ;
+                    const float* dtr = dtt + hh * kMaxQ;
                     const float cl = csr[lrow];
-                    Vec8<T> gf;                                   // G[lrow][s], s = s0 + 16 st + 4 grp + j
+                    Vec8<T> gf;                                   // G[lrow][s], s = s0 + 16 st2 + 4 grp + i
 #pragma unroll
-                    for (int st = 0; st < 2; ++st) {
-                        const int sb4 = s0 + 16 * st + 4 * grp;
+                    for (int st2 = 0; st2 < 2; ++st2) {
+                        const int sb4 = s0 + 16 * st2 + 4 * grp;
                         const float4 c4 = *reinterpret_cast<const float4*>(csr + sb4);
                         const float4 d4 = *reinterpret_cast<const float4*>(dtr + sb4);
                         const float cv[4] = {c4.x, c4.y, c4.z, c4.w}, dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const float v = gt[st][j] * (__expf(cl - cv[j]) * dv[j]);
-                            gf.set(4 * st + j, select(sb4 + j <= lrow, v, 0.f));
+                        for (int i = 0; i < 4; ++i) {
+                            const float v = gt[st2][i] * (__expf(cl - cv[i]) * dv[i]);
+                            gf.set(4 * st2 + i, select(sb4 + i <= lrow, v, 0.f));
                         }
                     }
-                    const unsigned char* xt = xtile(sb & 1, hh);
+                    const unsigned char* xt = stg + hh * S::xh_bytes;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> xf;
                         swz_row_slots<S::X_CH>(xf, xt, 0, 16 * pt);
-                        mma(acc[hh][pt], xf, gf);
+                        mma(acc[j][hh][pt], xf, gf);
                     }
                 }
             }
         }
     }
 
-    // ---------------- epilogue: y = acc + D x (x from the tiles of the last two stages), then
-    // through LDS so every global store is a full 16-byte segment of a y row
-    float yv[HB][P / 16][4];
-    {
-        const int sbl = min(lrow, len - 1) / kSB;
-#pragma unroll
-        for (int hh = 0; hh < HB; ++hh) {
-            const float dh = Dv[h0 + min(hh, nh - 1)];
-            const T* xt = reinterpret_cast<const T*>(xtile(sbl & 1, hh));
-#pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) {
-                const float4 xv = swz_load4f<S::X_CH>(xt, min(lrow, len - 1) % kSB, 16 * pt + 4 * grp);
-                yv[hh][pt][0] = acc[hh][pt][0] + dh * xv.x;
-                yv[hh][pt][1] = acc[hh][pt][1] + dh * xv.y;
-                yv[hh][pt][2] = acc[hh][pt][2] + dh * xv.z;
-                yv[hh][pt][3] = acc[hh][pt][3] + dh * xv.w;
-            }
-        }
-    }
-    __syncthreads();                                  // every wave is done with the x tiles
-    constexpr int out_bytes = kRows * P * (int)sizeof(T);           // one head's y tile
-    static_assert(HB * out_bytes <= S::region, "y staging fits the stage buffers");
+    // ---- epilogue, head by head: y^T through LDS (fp32), + D x, full 16-byte row segments of y
+    unsigned char* const out = region;
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) {
-        unsigned char* ot = region + hh * out_bytes;
+        if (hh >= nh) break;
+        __syncthreads();                                     // the ring / the previous head's pass are done
 #pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) {
-            const int col = 16 * pt + 4 * grp;
-            unsigned char* dst = ot + SwzTile<S::X_CH>::offset(16 * wave + r16, col / EPC) + (int)sizeof(T) * (col % EPC);
-            store4(reinterpret_cast<T*>(dst), yv[hh][pt][0], yv[hh][pt][1], yv[hh][pt][2], yv[hh][pt][3]);
+        for (int j = 0; j < 2; ++j) {
+            if (!has[j]) continue;
+            const int l = 16 * rbk[j] + r16;
+#pragma unroll
+            for (int pt = 0; pt < P / 16; ++pt)
+                *reinterpret_cast<f32x4*>(out + SwzTile<S::O_CH>::offset(l, 4 * pt + grp)) = acc[j][hh][pt];
         }
-    }
-    __syncthreads();
-    for (int i = tid; i < nh * kRows * S::X_CH; i += 256) {
-        const int hh = i / (kRows * S::X_CH), r = (i / S::X_CH) % kRows, ch = i % S::X_CH;
-        if (row0 + r >= len) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(region + hh * out_bytes + SwzTile<S::X_CH>::offset(r, ch));
-        *reinterpret_cast<uint4*>(y + ((b * seqlen + t0 + row0 + r) * nheads + h0 + hh) * P + ch * EPC) = v;
+        __syncthreads();
+        const int h = h0 + hh;
+        const float dh = Dv[h];
+        for (int i = tid; i < len * (P / 8); i += kThreads) {         // 8 elements per item
+            const int r = i / (P / 8), c8 = i % (P / 8);
+            const int64_t off = ((b * seqlen + t0 + r) * nheads + h) * P + 8 * c8;
+            Vec8<T> xv, yv;
+            load8(xv, x + off);
+            const float4 a = *reinterpret_cast<const float4*>(out + SwzTile<S::O_CH>::offset(r, 2 * c8));
+            const float4 a2 = *reinterpret_cast<const float4*>(out + SwzTile<S::O_CH>::offset(r, 2 * c8 + 1));
+            yv.set(0, a.x + dh * xv.get(0));  yv.set(1, a.y + dh * xv.get(1));
+            yv.set(2, a.z + dh * xv.get(2));  yv.set(3, a.w + dh * xv.get(3));
+            yv.set(4, a2.x + dh * xv.get(4)); yv.set(5, a2.y + dh * xv.get(5));
+            yv.set(6, a2.z + dh * xv.get(6)); yv.set(7, a2.w + dh * xv.get(7));
+            store8(y + off, yv);
+        }
     }
 }
 
@@ -345,18 +363,18 @@ template <typename T, int P, int NK>
 hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
                   const float* D, T* y, const Dims& d, hipStream_t stream)
 {
-    constexpr int HB = heads_per_block<T, P, NK>();
-    static_assert(ScanCfg<T, P, NK, HB>::total <= 160 * 1024, "LDS budget");
+    using S = ScanShape<T, P, NK>;
+    static_assert(S::fits, "LDS budget");
+    constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
-    const int nlt = (int)((d.chunk + kRows - 1) / kRows);
     const int hpg = (int)(d.nheads / d.ngroups);
     const int nhb = (hpg + HB - 1) / HB;                 // head blocks per group
     const int hpw = (hpg + nhb - 1) / nhb;               // heads per workgroup, balanced
-    const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nlt;
+    const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, HB>), dim3((unsigned)nblocks), dim3(256), 0, stream, x,
-                       B, C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
-                       (int)d.dstate, (int)d.chunk, nc, nlt, nhb, hpw, (int)nblocks);
+    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, S>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                       x, B, C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
+                       (int)d.dstate, (int)d.chunk, nc, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 

@@ -200,12 +200,12 @@ __device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds
 // Issue the loads of one tile: src(r, c) returns the global address of logical
 // chunk c of row r (it must always be a valid address).  Returns nothing; the
 // data is in LDS once this wave's vmcnt reaches zero and a barrier has passed.
-template <int CH, int R, class F>
+template <int CH, int R, int NW = 4, class F>
 __device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
     using TL = SwzTile<CH>;
     constexpr int kInst = R * CH / 64;                 // wavefront instructions for the tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int q = wave; q < kInst; q += 4) {
+    for (int q = wave; q < kInst; q += NW) {
         const int pos = q * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
         const int c = slot ^ (r & TL::kMask);
@@ -213,8 +213,34 @@ __device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
     }
 }
 
+// The same for NT tiles of one shape laid out every `stride` bytes: their
+// copies are dealt round-robin over the NW wavefronts as one sequence, so
+// every wavefront issues (NT * R * CH / 64) / NW of them when that divides.
+// src(t, r, c) returns the global address of logical chunk c of row r of tile t.
+template <int CH, int R, int NT, int NW, class F>
+__device__ __forceinline__ void tiles_load_async(unsigned char* base, int stride, F src) {
+    using TL = SwzTile<CH>;
+    constexpr int kPer = R * CH / 64;                  // wavefront instructions per tile
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int q = wave; q < NT * kPer; q += NW) {
+        const int t = q / kPer, qq = q % kPer;
+        const int pos = qq * 64 + lane;
+        const int r = pos / CH, slot = pos % CH;
+        const int c = slot ^ (r & TL::kMask);
+        dma16(src(t, r, c), base + t * stride + qq * 1024);
+    }
+}
+
 // Wait for all of this wavefront's outstanding vector-memory operations.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Wait until at most N of this wavefront's vector-memory operations are outstanding
+// (they complete in issue order for this counter), N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmem_below() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // Fragment of 8 consecutive elements along a row of a swizzled tile (columns
 // c0 .. c0+7, c0 a multiple of 8 for bf16 / 4 for fp32).
