@@ -46,10 +46,11 @@
  *     error status means no device memory was read or written.  A launch
  *     failure reported by the runtime returns SSD_ERR_HIP.  No C++
  *     exception crosses this interface.
- *   - Shape limits: batch >= 0; seqlen >= 0; nheads >= 1; headdim in
- *     {16, 32, 64, 128}; dstate a multiple of 16 in [16, 256]; ngroups >= 1
- *     dividing nheads; chunk_size a multiple of 16 in [16, 256].  seqlen
- *     need not be a multiple of chunk_size: the last chunk is then shorter.
+ *   - Shape limits: 0 <= batch <= 65535; seqlen >= 0; 1 <= nheads <= 65535
+ *     with nheads * headdim <= 2^20; headdim in {16, 32, 64, 128}; dstate a
+ *     multiple of 16 in [16, 256]; ngroups >= 1 dividing nheads; chunk_size
+ *     a multiple of 16 in [16, 256].  seqlen need not be a multiple of
+ *     chunk_size: the last chunk is then shorter.
  *   - Outputs must not overlap inputs (the step state is the one in/out
  *     argument); overlap is reported as SSD_ERR_ALIAS.
  */

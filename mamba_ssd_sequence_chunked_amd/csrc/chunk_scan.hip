@@ -36,9 +36,15 @@
 //     exp(cs[e] - cs[s]) dt_s tabulated once per workgroup (both exponents
 //     are <= 0); the stage holding the rows uses the full per-entry decay and
 //     the causal mask (entries above the diagonal are selected to zero, never
-//     multiplied).
-//   * the epilogue stages y^T of one head at a time through LDS, adds D x with
-//     16-byte reads of x and writes full 16-byte segments of y rows.
+//     multiplied).  The heads run as one straight-line sequence (heads past
+//     the workgroup compute on clamped data and are never stored), so the
+//     compiler can overlap one head's LDS reads with another's products.
+//   * the skip term D x is added in the stage holding the rows, from the x
+//     tile already in LDS, in fp32.
+//   * y leaves straight from the accumulators through buffer stores (4
+//     consecutive values per lane); stores of rows past the sequence or of
+//     heads past the workgroup fall outside the buffer's range and are
+//     dropped.
 // Workgroups are numbered head block fastest and renumbered so that
 // consecutive ones share an XCD (and the chunk's B and C in its L2).
 #include <type_traits>
@@ -66,14 +72,14 @@ struct ScanCfg {
     static constexpr int X_CH = P * (int)sizeof(T) / 16;           // chunks per x row
     static constexpr int B_CH = NP * (int)sizeof(T) / 16;          // chunks per B row
     static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in slab row
-    static constexpr int O_CH = P * 4 / 16;                        // chunks per fp32 y row
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
     static constexpr int b_bytes = kSB * NP * (int)sizeof(T);
     static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
     static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head
     static constexpr int ring_bytes = STG * stage_bytes;
     static constexpr int main_bytes = ring_bytes + HB * sh_bytes;
-    static constexpr int out_bytes = kMaxQ * P * 4;                 // one head's fp32 y^T staging
+    static constexpr int ot_bytes = 16 * P * (int)sizeof(T);       // one wavefront's y tile (16 rows)
+    static constexpr int out_bytes = kWaves * ot_bytes;
     static constexpr int region = main_bytes > out_bytes ? main_bytes : out_bytes;
     static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ;           // cs, dt, per-token decay factor
     static constexpr int total = tab_bytes + region;
@@ -143,14 +149,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
     // ---- asynchronous copies: the heads' S_in tiles (first slab), then the first stages of the ring
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
     auto issue_s = [&](int sl) {
-        tiles_load_async<S::S_CH, P, HB, kWaves>(stile, S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
+        tiles_load_async<S::S_CH, P, HB, kWaves>(lds_addr(region) + S::ring_bytes, S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
             return ent + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N + min(sl * SW + ch * EPC, N - EPC);
         });
     };
     issue_s(0);
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
-        unsigned char* stg = ring + (sb % kStages) * S::stage_bytes;
+        const unsigned stg = lds_addr(region) + (sb % kStages) * S::stage_bytes;
         const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
         tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
             return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(hh, nh - 1) * P + ch * EPC;
@@ -163,6 +169,10 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
 #pragma unroll
     for (int sb = 0; sb < kStages - 1; ++sb)
         if (sb < nsb) issue_stage(sb);
+
+    float dsk[HB];                                                  // skip weights D of the heads
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) dsk[hh] = Dv[h0 + min(hh, nh - 1)];
 
     // ---- decay tables
     for (int i = tid; i < HB * kMaxQ; i += kThreads) {
@@ -211,22 +221,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
             wait_vmem();
             __syncthreads();
         }
+        // every S_in fragment serves both row blocks (a missing row block has zero C fragments)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (!has[j]) continue;
+        for (int hh = 0; hh < HB; ++hh) {
+            const unsigned char* stl = stile + hh * S::sh_bytes;
 #pragma unroll
-            for (int hh = 0; hh < HB; ++hh) {
-                if (hh >= nh) break;
-                const unsigned char* stl = stile + hh * S::sh_bytes;
+            for (int kk = 0; kk < SW / 32; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < SW / 32; ++kk)
-#pragma unroll
-                    for (int pt = 0; pt < P / 16; ++pt) {
-                        Vec8<T> af;
-                        swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
-                        mma(acc[j][hh][pt], af, cf[j][sl * (SW / 32) + kk]);
-                    }
-            }
+                for (int pt = 0; pt < P / 16; ++pt) {
+                    Vec8<T> af;
+                    swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
+                    mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
+                    mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
+                }
         }
     }
 #pragma unroll
@@ -235,7 +242,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
         const int l = min(16 * rbk[j] + r16, kMaxQ - 1);
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
-            if (hh >= nh) break;
             const float e = __expf(cst[hh * kMaxQ + l]);
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt)
@@ -275,7 +281,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
                 // the stage lies wholly before the block: G = C.B * exp(cs[l] - cs[e]) * vst[s]
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
-                    if (hh >= nh) break;
                     const float u = __expf(cst[hh * kMaxQ + lrow] - cst[hh * kMaxQ + s0 + kSB - 1]);
                     const float* vr = vst + hh * kMaxQ + s0 + 4 * grp;
                     const float4 va = *reinterpret_cast<const float4*>(vr);
@@ -297,7 +302,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
                 // the stage holding the block's rows: full per-entry decay and the causal mask
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
-                    if (hh >= nh) break;
                     const float* csr = cst + hh * kMaxQ;
                     const float* dtr = dtt + hh * kMaxQ;
                     const float cl = csr[lrow];
@@ -322,39 +326,40 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
                         mma(acc[j][hh][pt], xf, gf);
                     }
                 }
+                // skip term: x of the block's own rows is in this stage's tiles
+#pragma unroll
+                for (int hh = 0; hh < HB; ++hh) {
+                    const T* xt = reinterpret_cast<const T*>(stg + hh * S::xh_bytes);
+#pragma unroll
+                    for (int pt = 0; pt < P / 16; ++pt) {
+                        const float4 xl = swz_load4f<S::X_CH>(xt, lrow - s0, 16 * pt + 4 * grp);
+                        acc[j][hh][pt][0] += dsk[hh] * xl.x;
+                        acc[j][hh][pt][1] += dsk[hh] * xl.y;
+                        acc[j][hh][pt][2] += dsk[hh] * xl.z;
+                        acc[j][hh][pt][3] += dsk[hh] * xl.w;
+                    }
+                }
             }
         }
     }
 
-    // ---- epilogue, head by head: y^T through LDS (fp32), + D x, full 16-byte row segments of y
-    unsigned char* const out = region;
-#pragma unroll
-    for (int hh = 0; hh < HB; ++hh) {
-        if (hh >= nh) break;
-        __syncthreads();                                     // the ring / the previous head's pass are done
+    {
+        T* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(yb, 0, len * nheads * P * (int)sizeof(T), kBufferDword3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            if (!has[j]) continue;
-            const int l = 16 * rbk[j] + r16;
+            const int row = 16 * rbk[j] + r16;
+            const bool rok = has[j] && row < len;
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt)
-                *reinterpret_cast<f32x4*>(out + SwzTile<S::O_CH>::offset(l, 4 * pt + grp)) = acc[j][hh][pt];
-        }
-        __syncthreads();
-        const int h = h0 + hh;
-        const float dh = Dv[h];
-        for (int i = tid; i < len * (P / 8); i += kThreads) {         // 8 elements per item
-            const int r = i / (P / 8), c8 = i % (P / 8);
-            const int64_t off = ((b * seqlen + t0 + r) * nheads + h) * P + 8 * c8;
-            Vec8<T> xv, yv;
-            load8(xv, x + off);
-            const float4 a = *reinterpret_cast<const float4*>(out + SwzTile<S::O_CH>::offset(r, 2 * c8));
-            const float4 a2 = *reinterpret_cast<const float4*>(out + SwzTile<S::O_CH>::offset(r, 2 * c8 + 1));
-            yv.set(0, a.x + dh * xv.get(0));  yv.set(1, a.y + dh * xv.get(1));
-            yv.set(2, a.z + dh * xv.get(2));  yv.set(3, a.w + dh * xv.get(3));
-            yv.set(4, a2.x + dh * xv.get(4)); yv.set(5, a2.y + dh * xv.get(5));
-            yv.set(6, a2.z + dh * xv.get(6)); yv.set(7, a2.w + dh * xv.get(7));
-            store8(y + off, yv);
+            for (int hh = 0; hh < HB; ++hh) {
+                const bool ok = rok && hh < nh;
+#pragma unroll
+                for (int pt = 0; pt < P / 16; ++pt) {
+                    const int off = ok ? ((row * nheads + hh) * P + 16 * pt + 4 * grp) * (int)sizeof(T) : kDropped;
+                    buffer_store4(rs, off, 0, acc[j][hh][pt], T{});
+                }
+            }
         }
     }
 }

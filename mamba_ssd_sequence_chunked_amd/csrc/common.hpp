@@ -108,6 +108,14 @@ __device__ __forceinline__ void mma(f32x4& acc, const Vec8<float>& a, const Vec8
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
+// LDS pointer for a generic pointer known to point into LDS: the low 32 bits
+// of such a flat address are the LDS address (taken as an integer, so no
+// null-pointer check of a generic -> local cast is generated).
+template <typename V>
+__device__ __forceinline__ __attribute__((address_space(3))) V* as_lds(const void* p) {
+    return (__attribute__((address_space(3))) V*)(uintptr_t)(unsigned)(uintptr_t)p;
+}
+
 // Operand fragment whose 8 contraction slots run down the ROWS of a row-major
 // LDS tile: lane 16 * g + r receives column c0 + r of rows k0 + 4g + m (slots
 // 0..3) and k0 + 16 + 4g + m (slots 4..7), m = 0..3.  The bf16 form uses the
@@ -120,10 +128,8 @@ __device__ __forceinline__ void load_row_slots(Vec8<bf16>& f, const bf16* tile, 
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const bf16* p0 = tile + (k0 + 4 * g + (r >> 2)) * pitch + c0 + 4 * (r & 3);
-    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(p0));
-    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) v4i16*)(p0 + 16 * pitch));
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p0 + 16 * pitch));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     f.v = __builtin_bit_cast(bf16x8, ab);
@@ -181,15 +187,19 @@ struct SwzTile {
     __device__ __forceinline__ static int offset(int r, int c) { return r * kRowBytes + ((c ^ (r & kMask)) << 4); }
 };
 
-// One 16-byte global->LDS load per lane: lane i's data goes to lds_base +
-// 16 i (lds_base wave-uniform).  Issued through inline asm so that the
+// LDS address (an integer) of a __shared__ object, taken from its local
+// address-space form so that no generic pointer is materialised.
+#define lds_addr(obj) ((unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)(obj))
+
+// One 16-byte global->LDS load per lane: lane i's data goes to LDS address
+// lds_base + 16 i (lds_base wave-uniform; see lds_addr).  Issued through inline asm so that the
 // compiler's wait-count bookkeeping does not treat every later LDS read as
 // possibly aliasing the in-flight copy (it cannot tell the two stage buffers
 // apart and would wait for the prefetch before any LDS read); the kernels
 // order these copies explicitly with wait_vmem() and a barrier.  M0 carries
 // the LDS address and is restored right after the issue.
-__device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds_base) {
-    const unsigned a = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)lds_base);
+__device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
+    const unsigned a = __builtin_amdgcn_readfirstlane(lds_base);
     unsigned saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
@@ -201,7 +211,7 @@ __device__ __forceinline__ void dma16(const void* gsrc, const unsigned char* lds
 // chunk c of row r (it must always be a valid address).  Returns nothing; the
 // data is in LDS once this wave's vmcnt reaches zero and a barrier has passed.
 template <int CH, int R, int NW = 4, class F>
-__device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
+__device__ __forceinline__ void tile_load_async(unsigned tile, F src) {
     using TL = SwzTile<CH>;
     constexpr int kInst = R * CH / 64;                 // wavefront instructions for the tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -209,7 +219,7 @@ __device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
         const int pos = q * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
         const int c = slot ^ (r & TL::kMask);
-        dma16(src(r, c), tile + q * 1024);
+        dma16(src(r, c), tile + q * 1024u);
     }
 }
 
@@ -218,7 +228,7 @@ __device__ __forceinline__ void tile_load_async(unsigned char* tile, F src) {
 // every wavefront issues (NT * R * CH / 64) / NW of them when that divides.
 // src(t, r, c) returns the global address of logical chunk c of row r of tile t.
 template <int CH, int R, int NT, int NW, class F>
-__device__ __forceinline__ void tiles_load_async(unsigned char* base, int stride, F src) {
+__device__ __forceinline__ void tiles_load_async(unsigned base, int stride, F src) {
     using TL = SwzTile<CH>;
     constexpr int kPer = R * CH / 64;                  // wavefront instructions per tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -227,7 +237,7 @@ __device__ __forceinline__ void tiles_load_async(unsigned char* base, int stride
         const int pos = qq * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
         const int c = slot ^ (r & TL::kMask);
-        dma16(src(t, r, c), base + t * stride + qq * 1024);
+        dma16(src(t, r, c), base + t * stride + qq * 1024u);
     }
 }
 
@@ -281,8 +291,8 @@ __device__ __forceinline__ void swz_row_slots(Vec8<bf16>& f, const unsigned char
     const int col = c0 + 4 * (r & 3);                          // 4 elements = 8 bytes, inside one chunk
     const unsigned char* p0 = tile + SwzTile<CH>::offset(row, col >> 3) + 2 * (col & 7);
     const unsigned char* p1 = tile + SwzTile<CH>::offset(row + 16, col >> 3) + 2 * (col & 7);
-    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p0));
-    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p1));
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p0));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p1));
     const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     f.v = __builtin_bit_cast(bf16x8, ab);
 }
@@ -296,6 +306,26 @@ __device__ __forceinline__ void swz_row_slots(Vec8<float>& f, const unsigned cha
         f.v[m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r0, col >> 2) + 4 * (col & 3));
         f.v[4 + m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r1, col >> 2) + 4 * (col & 3));
     }
+}
+
+// Store 4 consecutive elements through a buffer resource: one instruction
+// whatever the offset; a store whose offset (voff + soff) reaches the
+// resource's size is dropped by the hardware, which masks rows (voff) and
+// heads (soff) without branching.  kDropped marks a dropped store: resources
+// here stay below 2^30 bytes, and two kDropped offsets still sum below 2^32.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format, range-checked
+constexpr int kDropped = 0x40000000;
+
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff, int soff, const f32x4& v, bf16) {
+    bf16x4 q;
+    q[0] = static_cast<bf16>(v[0]); q[1] = static_cast<bf16>(v[1]);
+    q[2] = static_cast<bf16>(v[2]); q[3] = static_cast<bf16>(v[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, q), r, voff, soff, 0);
+}
+__device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff, int soff, const f32x4& v, float) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, soff, 0);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wavefront (lane order).

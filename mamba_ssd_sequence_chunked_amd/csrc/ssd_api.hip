@@ -29,6 +29,7 @@ int check_common(int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
     if (headdim != 16 && headdim != 32 && headdim != 64 && headdim != 128) return SSD_ERR_SHAPE;
     if (dstate < 16 || dstate > 256 || dstate % 16 != 0) return SSD_ERR_SHAPE;
     if (ngroups < 1 || nheads % ngroups != 0) return SSD_ERR_SHAPE;
+    if (nheads * headdim > (int64_t(1) << 20)) return SSD_ERR_SHAPE;   // one chunk's rows of y stay <= 2^30 bytes
     return SSD_OK;
 }
 
