@@ -58,7 +58,7 @@ namespace {
 
 constexpr int kSB = 32;        // source tokens per stage
 constexpr int kMaxQ = 256;
-constexpr int kWaves = 8;
+constexpr int kWaves = 4;                      // one row-block pair per wavefront
 constexpr int kThreads = 64 * kWaves;
 
 template <typename T, int P, int NK, int HB, int STG, int SW>
@@ -78,11 +78,10 @@ struct ScanCfg {
     static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head
     static constexpr int ring_bytes = STG * stage_bytes;
     static constexpr int main_bytes = ring_bytes + HB * sh_bytes;
-    static constexpr int ot_bytes = 16 * P * (int)sizeof(T);       // one wavefront's y tile (16 rows)
-    static constexpr int out_bytes = kWaves * ot_bytes;
-    static constexpr int region = main_bytes > out_bytes ? main_bytes : out_bytes;
+    static constexpr int region = main_bytes;
     static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ;           // cs, dt, per-token decay factor
     static constexpr int total = tab_bytes + region;
+    static constexpr bool pair_fits = total <= 80 * 1024;           // two workgroups per CU
     static constexpr bool fits = total <= 160 * 1024;
     // asynchronous copy instructions per wavefront per stage (uniform when divisible)
     static constexpr int x_inst = HB * kSB * X_CH / 64;             // dealt over all waves as one sequence
@@ -93,31 +92,30 @@ struct ScanCfg {
 
 // Launch shape for (T, P, NK): heads per workgroup keep the y accumulators
 // (2 row blocks x HB heads x P columns) at 128 registers per lane (64 with the
-// widest state, whose C fragments take the room); while the LDS does not fit
-// in a CU, first the heads, then the ring depth, then the S_in slab width are
-// halved.
+// widest state, whose C fragments take the room), with a 2-deep ring and S_in
+// in 32-column slabs; the heads are halved until two workgroups fit in a CU's
+// LDS (one workgroup's loads and stores then overlap the other's products),
+// and a single head takes a CU alone when it must.
 template <class C> struct TypeBox { using type = C; };
 
-template <typename T, int P, int NK, int HB, int STG, int SW>
+template <typename T, int P, int NK, int HB>
 constexpr auto pick_shape() {
-    using C = ScanCfg<T, P, NK, HB, STG, SW>;
-    if constexpr (C::fits) return TypeBox<C>{};
-    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2, STG, SW>();
-    else if constexpr (STG > 2) return pick_shape<T, P, NK, 1, STG - 1, SW>();
-    else if constexpr (SW > 32) return pick_shape<T, P, NK, 1, 2, SW / 2>();
+    using C = ScanCfg<T, P, NK, HB, 2, 32>;
+    if constexpr (C::pair_fits || (HB == 1 && C::fits)) return TypeBox<C>{};
+    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2>();
     else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
 }
 
 template <typename T, int P, int NK>
 using ScanShape = typename decltype(pick_shape<T, P, NK,
-    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), 3, 32 * NK>())::type;
+    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P)>())::type;
 
 template <typename T, int P, int NK, class S>
-__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
+__global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, const float* __restrict__ Dv, T* __restrict__ y, int seqlen,
-    int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nblocks)
+    int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
     __shared__ float cst[HB * kMaxQ];
@@ -128,6 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
     unsigned char* const stile = region + S::ring_bytes;
 
     int id = xcd_logical_block(blockIdx.x, nblocks);
+    const int half = id % nhalf; id /= nhalf;
     const int hb = id % nhb; id /= nhb;
     const int g = id % ngroups; id /= ngroups;
     const int c = id % nc;
@@ -137,14 +136,18 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
     const int nh = min(hpw, hpg - hb * hpw);                       // heads of this workgroup (<= HB)
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, (int64_t)seqlen - t0);
-    const int nsb = (len + kSB - 1) / kSB;
     const int nrb = Q / 16;
+    // the workgroup's row-block pairs (p, nrb-1-p) for p in [half kWaves, half kWaves + kWaves): its last
+    // row lies in the first pair's second block, so it needs the stages up to that block's
+    const int last_rb = nrb - 1 - half * kWaves;
+    const int nsb = min((len + kSB - 1) / kSB, (16 * last_rb + 15) / kSB + 1);
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int r16 = lane & 15, grp = lane >> 4;
-    // this wavefront's row blocks (wave-uniform)
-    const int rbk[2] = {wave, nrb - 1 - wave};
-    const bool has[2] = {wave < nrb, nrb - 1 - wave > wave};
+    // this wavefront's row blocks: the pair (p, nrb-1-p), each block once
+    const int pair = half * kWaves + wave;
+    const int rbk[2] = {pair, nrb - 1 - pair};
+    const bool has[2] = {2 * pair < nrb, 2 * pair < nrb - 1};
 
     // ---- asynchronous copies: the heads' S_in tiles (first slab), then the first stages of the ring
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
@@ -254,7 +257,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(
     for (int sb = 0; sb < nsb; ++sb) {
         const int s0 = sb * kSB;
         if (sb > 0) {
-            if (S::uniform && sb + 1 < nsb) wait_vmem_below<S::per_wave>();   // stage sb landed; sb+1 may fly
+            // stage sb landed; the kStages - 2 stages issued after it may still fly
+            if (S::uniform && kStages > 2 && sb + kStages - 2 < nsb) wait_vmem_below<(kStages - 2) * S::per_wave>();
             else wait_vmem();
             __syncthreads();
         }
@@ -375,11 +379,13 @@ hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const fl
     const int hpg = (int)(d.nheads / d.ngroups);
     const int nhb = (hpg + HB - 1) / HB;                 // head blocks per group
     const int hpw = (hpg + nhb - 1) / nhb;               // heads per workgroup, balanced
-    const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
+    const int npairs = (int)(d.chunk / 16 + 1) / 2;
+    const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
+    const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
     hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, S>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        x, B, C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
-                       (int)d.dstate, (int)d.chunk, nc, nhb, hpw, (int)nblocks);
+                       (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
 

@@ -9,20 +9,21 @@
 // contraction over the chunk's tokens, run on the matrix cores with fp32
 // accumulation.
 //
-// Workgroup = (batch, chunk, head), all N state columns; 4 wavefronts, each
-// owning every 4th 16-column tile of S_c x all P rows.  Tokens are the
-// contraction axis of both operands but the slow axis in memory: x and B are
-// staged through LDS in their natural (token, column) order, 64 tokens at a
-// time, and both operands are read with the gfx950 LDS transpose read, which
-// delivers 8 consecutive-token slots per lane.  w_l is computed once per
-// chunk into LDS and applied to the B fragment in fp32 before it is rounded
-// to the operand type.  The next 64 tokens are loaded into registers while
-// the current ones are multiplied; those loads are unconditional (indices
-// clamped) and masks are applied when writing LDS.
-//
-// Workgroups are numbered head-fastest within a chunk and renumbered so
-// consecutive ones share an XCD: the heads of a group read the same B tile
-// from that XCD's L2.
+// Workgroup = (batch, chunk, up to HB heads of one group), 8 wavefronts;
+// wavefront w owns head w / NSPLIT of the tile and one NSPLIT-th of the state
+// columns, all P rows.  The product is formed transposed, S^T = (w B)^T x, so
+// a lane holds 4 consecutive state columns of one row and stores them as one
+// 16-byte segment.  Tokens are the contraction axis of both operands but the
+// slow axis in memory: the heads' x tiles and the group's B tile stream
+// through a 3-deep ring of 32-token stages filled by asynchronous
+// global->LDS copies (XOR-swizzled by 16-byte chunk), every byte read once
+// per workgroup -- so B is read once for all the heads that share it -- and
+// both operands are read with the gfx950 LDS transpose read, which delivers
+// 8 token slots per lane.  w is tabulated per head once per workgroup and
+// applied to the B fragment in fp32 before it is rounded to the operand type;
+// tokens past the sequence have w = 0 (their copies come from a clamped,
+// valid row).  Workgroups are numbered head block fastest and renumbered so
+// that consecutive ones share an XCD (and the chunk's B in its L2).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -30,137 +31,170 @@ namespace ssd {
 
 namespace {
 
-constexpr int kKB = 64;       // tokens per LDS stage
+constexpr int kSB = 32;        // tokens per stage
+constexpr int kStages = 3;
 constexpr int kMaxQ = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
 
-template <typename T, int P, int NT>     // NT = 16-column tiles per wavefront (4 * 16 * NT >= N)
-struct StateSmem {
-    static constexpr int NW = 64 * NT;                  // padded state width
-    static constexpr int x_pitch = tr_pitch<T>(P);
-    static constexpr int b_pitch = tr_pitch<T>(NW);
-    static constexpr int x_n = kKB * P / 8;             // 8-element items per stage
-    static constexpr int b_n = kKB * NW / 8;
-    static constexpr int x_items = (x_n + 255) / 256;
-    static constexpr int b_items = (b_n + 255) / 256;
+template <typename T, int P, int NK, int HB>
+struct StateCfg {
+    static constexpr int kHeads = HB;
+    static constexpr int NSPLIT = kWaves / HB;                     // wavefronts per head
+    static constexpr int NP = 32 * NK;                             // state width padded to 32
+    // a head's (NP / 16) x (P / 16) output tiles split over its wavefronts: NSN along the state
+    // columns, NSP along the rows; each wavefront takes NT x PT tiles
+    static constexpr int NSN = NSPLIT < NP / 16 ? NSPLIT : NP / 16;
+    static constexpr int NSP = NSPLIT / NSN;
+    static constexpr int NT = NP / 16 / NSN;
+    static constexpr int PT = P / 16 / NSP > 0 ? P / 16 / NSP : 1;
+    static constexpr int EPC = 16 / (int)sizeof(T);
+    static constexpr int X_CH = P * (int)sizeof(T) / 16;
+    static constexpr int B_CH = NP * (int)sizeof(T) / 16;
+    static constexpr int xh_bytes = kSB * P * (int)sizeof(T);
+    static constexpr int stage_bytes = HB * xh_bytes + kSB * NP * (int)sizeof(T);
+    static constexpr int lds = kStages * stage_bytes + 4 * HB * kMaxQ;
+    static constexpr int acc_regs = NT * PT * 4;
+    // asynchronous copy instructions per stage, dealt over the wavefronts (uniform when divisible)
+    static constexpr int x_inst = HB * kSB * X_CH / 64;
+    static constexpr int b_inst = kSB * B_CH / 64;
+    static constexpr bool uniform = x_inst % kWaves == 0 && b_inst % kWaves == 0;
+    static constexpr int per_wave = uniform ? (x_inst + b_inst) / kWaves : 0;
+    static constexpr bool fits = lds <= 160 * 1024 && NT >= 1;
 };
 
-template <typename T, int P, int NT>
-__global__ __launch_bounds__(256, 2) void chunk_state_kernel(
+// Heads per workgroup: as many as keep a wavefront's accumulators within 64
+// registers and two workgroups' LDS within a CU, so that one workgroup's
+// loads and stores overlap the other's products.
+template <typename T, int P, int NK, int HB>
+constexpr int pick_heads() {
+    using C = StateCfg<T, P, NK, HB>;
+    if constexpr (HB == 1 || (C::lds <= 80 * 1024 && C::acc_regs <= 64)) return HB;
+    else return pick_heads<T, P, NK, HB / 2>();
+}
+
+template <typename T, int P, int NK, int HB>
+__global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ dt_chunked,
     const float* __restrict__ dA_cs, float* __restrict__ chunk_states, int seqlen, int nheads,
-    int ngroups, int N, int Q, int nc, int nblocks)
+    int ngroups, int N, int Q, int nc, int nhb, int hpw, int nblocks)
 {
-    using S = StateSmem<T, P, NT>;
-    __shared__ __attribute__((aligned(16))) T XS[kKB * S::x_pitch];
-    __shared__ __attribute__((aligned(16))) T BS[kKB * S::b_pitch];
-    __shared__ __attribute__((aligned(16))) float ws[kMaxQ + kKB];
+    using S = StateCfg<T, P, NK, HB>;
+    constexpr int EPC = S::EPC, NT = S::NT, PT = S::PT;
+    __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * S::stage_bytes];
+    __shared__ __attribute__((aligned(16))) float wt[HB * kMaxQ];
 
     int id = xcd_logical_block(blockIdx.x, nblocks);
-    const int h = id % nheads; id /= nheads;
+    const int hb = id % nhb; id /= nhb;
+    const int g = id % ngroups; id /= ngroups;
     const int c = id % nc;
     const int64_t b = id / nc;
-    const int g = h / (nheads / ngroups);
+    const int hpg = nheads / ngroups;
+    const int h0 = g * hpg + hb * hpw;
+    const int nh = min(hpw, hpg - hb * hpw);                       // heads of this workgroup (<= HB)
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, (int64_t)seqlen - t0);
+    const int nsb = (len + kSB - 1) / kSB;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int r16 = lane & 15, grp = lane >> 4;
+    const int hh = wave / S::NSPLIT;                               // this wavefront's head in the tile,
+    const int n0 = (wave % S::NSPLIT % S::NSN) * NT * 16;          // its first state column
+    const int p0 = (wave % S::NSPLIT / S::NSN) * PT * 16;          // and its first row (>= P: no rows)
 
-    const int64_t dbase = (((int64_t)b * nheads + h) * nc + c) * Q;
-    const float cs_last = dA_cs[dbase + Q - 1];
-    for (int l = tid; l < kMaxQ + kKB; l += 256) {
-        const int lc = min(l, Q - 1);
-        const float w = dt_chunked[dbase + lc] * __expf(cs_last - dA_cs[dbase + lc]);
-        ws[l] = select(l < len, w, 0.f);
-    }
-
-    f32x4 acc[NT][P / 16];
-#pragma unroll
-    for (int j = 0; j < NT; ++j)
-#pragma unroll
-        for (int pt = 0; pt < P / 16; ++pt) acc[j][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    Vec8<T> px[S::x_items], pb[S::b_items];
-    auto fetch = [&](int l0) {
-#pragma unroll
-        for (int k = 0; k < S::x_items; ++k) {
-            const int i = min(tid + 256 * k, S::x_n - 1);
-            const int r = i / (P / 8), o = i % (P / 8);
-            const int l = min(l0 + r, len - 1);
-            load8(px[k], x + ((b * seqlen + t0 + l) * nheads + h) * P + 8 * o);
-        }
-#pragma unroll
-        for (int k = 0; k < S::b_items; ++k) {
-            const int i = min(tid + 256 * k, S::b_n - 1);
-            const int r = i / (S::NW / 8), o = i % (S::NW / 8);
-            const int l = min(l0 + r, len - 1);
-            load8(pb[k], Bm + ((b * seqlen + t0 + l) * ngroups + g) * N + min(8 * o, N - 8));
-        }
+    auto issue_stage = [&](int sb) {
+        const int s0 = sb * kSB;
+        const unsigned stg = lds_addr(ring) + (sb % kStages) * S::stage_bytes;
+        const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
+        tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int ht, int r, int ch) -> const void* {
+            return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(ht, nh - 1) * P + ch * EPC;
+        });
+        const T* bg = Bm + (int64_t)g * N;
+        tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
+            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
+        });
     };
+#pragma unroll
+    for (int sb = 0; sb < kStages - 1; ++sb)
+        if (sb < nsb) issue_stage(sb);
 
-    fetch(0);
-    for (int l0 = 0; l0 < len; l0 += kKB) {
-        __syncthreads();
+    // w_l = dt_l exp(cs[Q-1] - cs[l]) per head, 0 past the sequence and for heads past the workgroup
+    for (int i = tid; i < HB * kMaxQ; i += kThreads) {
+        const int ht = i / kMaxQ, l = i % kMaxQ;
+        const int64_t base = (((int64_t)b * nheads + h0 + min(ht, nh - 1)) * nc + c) * Q;
+        const float w = dt_chunked[base + min(l, Q - 1)] * __expf(dA_cs[base + Q - 1] - dA_cs[base + min(l, Q - 1)]);
+        wt[i] = select(l < len && ht < nh, w, 0.f);
+    }
+    wait_vmem();                       // the first stages and the tables' loads
+    __syncthreads();
+
+    // S^T accumulators: acc[nt][pt] lane (r16, grp) holds S[p0 + 16 pt + r16][n0 + 16 nt + 4 grp + q]
+    f32x4 acc[NT][PT];
 #pragma unroll
-        for (int k = 0; k < S::x_items; ++k) {
-            const int i = tid + 256 * k;
-            const int r = i / (P / 8), o = i % (P / 8);
-            if (i < S::x_n) store8(XS + r * S::x_pitch + 8 * o, masked(px[k], l0 + r < len));
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) acc[nt][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int pr = min(p0, P - 16 * PT);                            // rows read (a wavefront past P reads valid rows)
+
+    for (int sb = 0; sb < nsb; ++sb) {
+        if (sb > 0) {
+            // stage sb landed; the kStages - 2 stages issued after it may still fly
+            if (S::uniform && kStages > 2 && sb + kStages - 2 < nsb) wait_vmem_below<(kStages - 2) * S::per_wave>();
+            else wait_vmem();
+            __syncthreads();
         }
+        if (sb + kStages - 1 < nsb) issue_stage(sb + kStages - 1);
+        const unsigned char* stg = ring + (sb % kStages) * S::stage_bytes;
+        const unsigned char* xt = stg + hh * S::xh_bytes;
+        const unsigned char* bt = stg + HB * S::xh_bytes;
+        // w of this lane's 8 token slots (tokens 4 grp + m and 16 + 4 grp + m of the stage)
+        const float* wr = wt + hh * kMaxQ + sb * kSB + 4 * grp;
+        const float4 wa = *reinterpret_cast<const float4*>(wr);
+        const float4 wb = *reinterpret_cast<const float4*>(wr + 16);
+        const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+        Vec8<T> xf[PT];
 #pragma unroll
-        for (int k = 0; k < S::b_items; ++k) {
-            const int i = tid + 256 * k;
-            const int r = i / (S::NW / 8), o = i % (S::NW / 8);
-            if (i < S::b_n) store8(BS + r * S::b_pitch + 8 * o, masked(pb[k], l0 + r < len && 8 * o < N));
-        }
-        __syncthreads();
-        if (l0 + kKB < len) fetch(l0 + kKB);
+        for (int pt = 0; pt < PT; ++pt) swz_row_slots<S::X_CH>(xf[pt], xt, 0, pr + 16 * pt);
 #pragma unroll
-        for (int ks = 0; ks < kKB / 32; ++ks) {
-            Vec8<T> af[P / 16];
+        for (int nt = 0; nt < NT; ++nt) {
+            Vec8<T> bf;
+            swz_row_slots<S::B_CH>(bf, bt, 0, n0 + 16 * nt);
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt) load_row_slots(af[pt], XS, S::x_pitch, 32 * ks, 16 * pt);
-            const float4 wa = *reinterpret_cast<const float4*>(ws + l0 + 32 * ks + 4 * grp);
-            const float4 wb = *reinterpret_cast<const float4*>(ws + l0 + 32 * ks + 16 + 4 * grp);
-            const float wv[8] = {wa.x, wa.y, wa.z, wa.w, wb.x, wb.y, wb.z, wb.w};
+            for (int e = 0; e < 8; ++e) bf.set(e, bf.get(e) * wv[e]);
 #pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int nt = wave + 4 * j;
-                if (16 * nt < N) {
-                    Vec8<T> bf;
-                    load_row_slots(bf, BS, S::b_pitch, 32 * ks, 16 * nt);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bf.set(e, bf.get(e) * wv[e]);
-#pragma unroll
-                    for (int pt = 0; pt < P / 16; ++pt) mma(acc[j][pt], af[pt], bf);
-                }
-            }
+            for (int pt = 0; pt < PT; ++pt) mma(acc[nt][pt], bf, xf[pt]);
         }
     }
 
-    float* out = chunk_states + ((((int64_t)b * nc + c) * nheads + h) * P) * N;
+    if (hh < nh && p0 < P) {
+        float* out = chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + hh) * P) * N;
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-        const int n = 16 * (wave + 4 * j) + r16;
-        if (n < N) {
+        for (int nt = 0; nt < NT; ++nt) {
+            const int n = n0 + 16 * nt + 4 * grp;
+            if (n < N) {
 #pragma unroll
-            for (int pt = 0; pt < P / 16; ++pt)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) out[(int64_t)(16 * pt + 4 * grp + q) * N + n] = acc[j][pt][q];
+                for (int pt = 0; pt < PT; ++pt)
+                    *reinterpret_cast<f32x4*>(out + (int64_t)(p0 + 16 * pt + r16) * N + n) = acc[nt][pt];
+            }
         }
     }
 }
 
-template <typename T, int P, int NT>
+template <typename T, int P, int NK>
 hipError_t launch(const T* x, const T* B, const float* dtc, const float* cs, float* out, const Dims& d,
                   hipStream_t stream)
 {
+    constexpr int HB = pick_heads<T, P, NK, 8>();
+    static_assert(StateCfg<T, P, NK, HB>::fits, "LDS budget");
     const int nc = (int)d.nchunks();
-    const int64_t nblocks = d.batch * nc * d.nheads;
+    const int hpg = (int)(d.nheads / d.ngroups);
+    const int nhb = (hpg + HB - 1) / HB;
+    const int hpw = (hpg + nhb - 1) / nhb;
+    const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_state_kernel<T, P, NT>), dim3((unsigned)nblocks), dim3(256), 0, stream, x, B,
-                       dtc, cs, out, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
-                       (int)d.chunk, nc, (int)nblocks);
+    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, x,
+                       B, dtc, cs, out, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
+                       (int)d.chunk, nc, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 
@@ -168,9 +202,11 @@ template <typename T, int P>
 hipError_t launch_p(const T* x, const T* B, const float* dtc, const float* cs, float* out, const Dims& d,
                     hipStream_t stream)
 {
-    if (d.dstate <= 64) return launch<T, P, 1>(x, B, dtc, cs, out, d, stream);
-    if (d.dstate <= 128) return launch<T, P, 2>(x, B, dtc, cs, out, d, stream);
-    return launch<T, P, 4>(x, B, dtc, cs, out, d, stream);
+    const int64_t nk = (d.dstate + 31) / 32;
+    if (nk <= 1) return launch<T, P, 1>(x, B, dtc, cs, out, d, stream);
+    if (nk <= 2) return launch<T, P, 2>(x, B, dtc, cs, out, d, stream);
+    if (nk <= 4) return launch<T, P, 4>(x, B, dtc, cs, out, d, stream);
+    return launch<T, P, 8>(x, B, dtc, cs, out, d, stream);
 }
 
 }  // namespace
