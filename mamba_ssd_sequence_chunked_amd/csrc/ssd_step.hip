@@ -15,6 +15,9 @@
 // a thread keeps several 16-byte loads in flight.  B, C, x and the scalars
 // are read once into registers; the readout over N is a reduction inside
 // aligned groups of lanes (a power of two >= N/4; surplus lanes contribute 0).
+// The state is streamed with non-temporal loads and stores: it is touched
+// once per call and is larger than the last-level cache, so keeping it out
+// of the caches leaves them to the small operands.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -59,8 +62,9 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(
         const int p = k * kRowsPerPass + rsub;
         const bool live = p < P;
         xv[k] = live ? to_f32(xr[p]) : 0.f;
-        s[k] = (live && colok) ? *reinterpret_cast<const float4*>(S + (int64_t)p * N + col)
-                               : make_float4(0.f, 0.f, 0.f, 0.f);
+        f32x4 t4 = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (live && colok) t4 = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (int64_t)p * N + col));
+        s[k] = make_float4(t4[0], t4[1], t4[2], t4[3]);
     }
 #pragma unroll
     for (int k = 0; k < kPass; ++k) {
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void ssd_step_kernel(
         v.y = fmaf(a, v.y, u * bv[1]);
         v.z = fmaf(a, v.z, u * bv[2]);
         v.w = fmaf(a, v.w, u * bv[3]);
-        if (live && colok) *reinterpret_cast<float4*>(S + (int64_t)p * N + col) = v;
+        if (live && colok) __builtin_nontemporal_store(f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4*>(S + (int64_t)p * N + col));
         float part = (live && colok) ? cv[0] * v.x + cv[1] * v.y + cv[2] * v.z + cv[3] * v.w : 0.f;
         part = group_sum<W>(part);
         if ((tid % W) == 0 && live) yr[p] = from_f32<T>(part + dh * xv[k]);
