@@ -77,11 +77,19 @@ def step_work(b, H, P, N, G, es):
                 flops=5 * b * H * P * N)
 
 
+def _code_only(text):
+    """Source text with comments and blank lines removed, lines stripped: a change of
+    comments alone leaves a kernel's counters valid."""
+    text = re.sub(rb"/\*.*?\*/", b"", text, flags=re.S)
+    text = re.sub(rb"//[^\n]*", b"", text)
+    return b"\n".join(ln.strip() for ln in text.splitlines() if ln.strip())
+
+
 def source_digest(name):
     h = hashlib.sha256()
     for f in (KERNEL_SOURCES[name], "common.hpp"):
         with open(os.path.join(ROOT, "mamba_ssd_sequence_chunked_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            h.update(_code_only(fh.read()))
     return h.hexdigest()[:16]
 
 

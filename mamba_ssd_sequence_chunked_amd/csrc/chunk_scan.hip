@@ -9,24 +9,29 @@
 // entering the chunk, decayed to position l (that blog's block-decomposition
 // outline adds it before the state moves on); the third is the skip term.
 //
-// Workgroup = (batch, chunk, group, up to HB heads of the group): all rows of
-// the chunk.  8 wavefronts; wavefront w owns row blocks w and nrb-1-w (16 rows
-// each), which gives every wavefront the same amount of causal work.  All
-// products run on the matrix cores with fp32 accumulation and are formed
-// transposed (y^T = X^T G^T and S_in C^T), so a lane holds 4 consecutive
-// head-dimension values of one row:
+// Row blocks of 16 rows are paired (p, nrb-1-p), which gives every pair the
+// same amount of causal work.  Workgroup = (batch, chunk, group, up to HB
+// heads of the group, one half of the pairs): 4 wavefronts, one pair each;
+// at 256-token chunks a chunk's 8 pairs make two workgroups, and the LDS use
+// is held to 80 KB so that two workgroups share a CU and one's loads and
+// stores overlap the other's products.  All products run on the matrix cores
+// with fp32 accumulation and are formed transposed (y^T = X^T G^T and
+// S_in C^T), so a lane holds 4 consecutive head-dimension values of one row:
 //   * C rows of a wavefront are read once from global memory straight into
 //     operand fragments (the state axis is contiguous, and it is the
 //     contraction axis of both C.B^T and S_in.C^T) and kept in registers.
-//   * the heads' S_in tiles and the source tokens' x and B tiles reach LDS
-//     through asynchronous global->LDS copies; source tokens stream through a
-//     3-deep ring of 32-token stages, so two stages are in flight while one
-//     is multiplied, and every byte of x, B and S_in is read once per
-//     workgroup.  Tiles are XOR-swizzled by 16-byte chunk, so the 16-byte
-//     operand reads and the transpose reads (x is kept token-major and read
-//     token-wise with ds_read_b64_tr_b16) are bank-conflict free.  Rows past
-//     the sequence are copied from a clamped, valid address; their products
-//     are removed by the causal mask or by zero C entries.
+//   * the heads' S_in tiles (in slabs of 32 state columns) and the source
+//     tokens' x and B tiles reach LDS through asynchronous global->LDS
+//     copies; source tokens stream through a 2-deep ring of 32-token stages,
+//     the next stage in flight while the current one is multiplied, and
+//     every byte of x, B and S_in is read once per workgroup.  Tiles are
+//     XOR-swizzled by 16-byte chunk, so the 16-byte operand reads and the
+//     transpose reads (x is kept token-major and read token-wise with
+//     ds_read_b64_tr_b16) are bank-conflict free.  Rows past the sequence
+//     are copied from a clamped, valid address; their products are removed
+//     by the causal mask or by zero C entries.
+//   * inter term first: every S_in fragment read from LDS feeds both row
+//     blocks of the wavefront; the sum is then scaled by exp(cs[l]).
 //   * intra term, per stage and row block: G^T (tokens x rows) = B_s C^T is
 //     computed once for all the heads of the workgroup (B and C belong to the
 //     group); each head applies its decay and dt in fp32 and the result, still

@@ -85,6 +85,9 @@ def _forward(lib, **kw):
     (dict(seqlen=-1), ERR_SHAPE),
     (dict(batch=-1), ERR_SHAPE),
     (dict(nheads=0), ERR_SHAPE),
+    (dict(nheads=65536), ERR_SHAPE),
+    (dict(batch=65536), ERR_SHAPE),
+    (dict(nheads=8200, headdim=128), ERR_SHAPE),     # nheads * headdim above 2^20
     (dict(dtype=2), ERR_DTYPE),
     (dict(x=None), ERR_NULL),
     (dict(final=None), ERR_NULL),
@@ -111,6 +114,7 @@ def test_step_rejects():
     assert call(headdim=20) == ERR_SHAPE
     assert call(dstate=0) == ERR_SHAPE
     assert call(ngroups=3) == ERR_SHAPE
+    assert call(nheads=8200, headdim=128) == ERR_SHAPE
     assert call(dtype=-1) == ERR_DTYPE
     assert call(state=None) == ERR_NULL
     assert call(y=fake(2)) == ERR_ALIAS
