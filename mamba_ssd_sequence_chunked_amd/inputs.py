@@ -17,6 +17,14 @@ library is measured on:
   decode   bf16, batch 256 H=80 P=64 N=128 G=1, 1024 single-token steps on
            an fp32 state initialised N(0, 0.1^2)
 
+and, for the Mamba-1 selective scan the SSD layer is compared with,
+
+  scan2p7b bf16, B=4 L=4096 channels 5120 N=16 (the same 2.7B-class layer
+           width, with Mamba-1's state size), delta drawn like "l2p7b"'s dt
+           per (batch, token, channel), A[d, n] = -exp(U(0, log 16)) per
+           (channel, state), draw order x, delta noise, delta uniform, A, B,
+           C, D, initial state (if any)
+
 Distributions: x ~ N(0,1); dt = softplus(z) with z ~ N(0,1) - 2
 ("tiny", "l130m", "decode") or z ~ N(0,1) + log(expm1(U(1e-3, 1e-1)))
 ("l2p7b", "long64k"); A_h = -exp(U(0, log 16)); B, C ~ N(0,1)/sqrt(N);
@@ -34,8 +42,9 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "SSDConfig", "SSDInputs", "StepInputs", "bf16_bits", "bf16_to_f64",
-    "make_inputs", "make_step_params", "make_step_inputs", "make_random",
+    "CONFIGS", "SSDConfig", "SSDInputs", "StepInputs", "ScanInputs", "SCAN_CONFIGS", "bf16_bits",
+    "bf16_to_f64", "make_inputs", "make_step_params", "make_step_inputs", "make_random",
+    "make_scan_random", "make_scan_inputs",
 ]
 
 
@@ -199,3 +208,58 @@ def make_step_inputs(name: str, step: int, batch: Optional[int] = None) -> StepI
     b = c.batch if batch is None else batch
     return StepInputs(x=_store(x[:b], c.dtype), dt=dt[:b].astype(np.float32),
                       B=_store(Bm[:b], c.dtype), C=_store(Cm[:b], c.dtype), dtype=c.dtype)
+
+
+@dataclasses.dataclass
+class ScanInputs:
+    """One selective-scan problem.  x, B, C in the storage dtype (float32 or
+    uint16 bf16 bit patterns); delta, A, D, init float32."""
+    x: np.ndarray          # (batch, seqlen, dim)
+    delta: np.ndarray      # (batch, seqlen, dim), positive
+    A: np.ndarray          # (dim, dstate), negative
+    B: np.ndarray          # (batch, seqlen, dstate)
+    C: np.ndarray          # (batch, seqlen, dstate)
+    D: np.ndarray          # (dim,)
+    init: Optional[np.ndarray]   # (batch, dim, dstate) or None (zeros)
+    dtype: str
+
+    @property
+    def dims(self):
+        b, l, d = self.x.shape
+        return b, l, d, self.A.shape[1]
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if a is None:
+            return None
+        if name in ("x", "B", "C") and self.dtype == "bf16":
+            return bf16_to_f64(a)
+        return a.astype(np.float64)
+
+
+SCAN_CONFIGS = {
+    # name: (batch, seqlen, dim, dstate, dtype, dt_kind, init, seed)
+    "scan2p7b": (4, 4096, 5120, 16, "bf16", "ranged", False, 5),
+}
+
+
+def make_scan_random(batch, seqlen, dim, dstate, dtype="bf16", dt_kind="ranged", init=False,
+                     seed=0) -> ScanInputs:
+    """Draw one selective-scan problem of any shape with the workload distributions."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((batch, seqlen, dim))
+    delta = _draw_dt(rng, (batch, seqlen, dim), dt_kind)
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), size=(dim, dstate)))
+    Bm = rng.standard_normal((batch, seqlen, dstate)) / np.sqrt(dstate)
+    Cm = rng.standard_normal((batch, seqlen, dstate)) / np.sqrt(dstate)
+    D = rng.standard_normal(dim)
+    h0 = 0.1 * rng.standard_normal((batch, dim, dstate)) if init else None
+    return ScanInputs(
+        x=_store(x, dtype), delta=delta.astype(np.float32), A=A.astype(np.float32),
+        B=_store(Bm, dtype), C=_store(Cm, dtype), D=D.astype(np.float32),
+        init=None if h0 is None else h0.astype(np.float32), dtype=dtype)
+
+
+def make_scan_inputs(name: str) -> ScanInputs:
+    b, l, d, n, dtype, kind, init, seed = SCAN_CONFIGS[name]
+    return make_scan_random(b, l, d, n, dtype, kind, init, seed)

@@ -6,7 +6,8 @@ calls anything here, and nothing here imports the library.
 
 ``forward`` and ``step`` call the plain C recurrence in ``ssd_oracle.c``
 (token by token, double precision, one independent (b, h, p) row per
-OpenMP task).  The helpers below it are written on top of those two calls
+OpenMP task); ``selective_scan`` calls the Mamba-1 recurrence there (one
+(b, channel) row per task).  The helpers below it are written on top of those two calls
 and plain numpy indexing only:
 
 * ``chunk_log_decay`` - the exponent of the decay product of every prefix
@@ -59,6 +60,8 @@ def _bind(lib):
                                                                 ctypes.c_int]
     lib.ssd_oracle_step.restype = ctypes.c_int
     lib.ssd_oracle_step.argtypes = [_dp] * 8 + [_i64] * 5 + [ctypes.c_int]
+    lib.ssd_oracle_selective_scan.restype = ctypes.c_int
+    lib.ssd_oracle_selective_scan.argtypes = [_dp] * 9 + [_i64] * 4 + [ctypes.c_int]
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
     return lib
 
@@ -135,6 +138,27 @@ def step(state, x, dt, A, B, C, D, nthreads: int = 0, lib=None):
     if rc != 0:
         raise ValueError("ssd_oracle_step rejected its arguments")
     return y, st
+
+
+def selective_scan(x, delta, A, B, C, D, init=None, nthreads: int = 0, lib=None):
+    """The Mamba-1 selective scan (per-channel diagonal decays).
+
+    x, delta (b,L,Dm); A (Dm,N); B, C (b,L,N); D (Dm,); init (b,Dm,N) or None.
+    Returns (y (b,L,Dm), final (b,Dm,N)) in fp64."""
+    x, delta, A, B, C, D, init = (_f64(a) for a in (x, delta, A, B, C, D, init))
+    b, L, Dm = x.shape
+    N = A.shape[1]
+    assert delta.shape == (b, L, Dm) and A.shape == (Dm, N) and D.shape == (Dm,)
+    assert B.shape == (b, L, N) and C.shape == (b, L, N)
+    assert init is None or init.shape == (b, Dm, N)
+    y = np.empty((b, L, Dm))
+    final = np.empty((b, Dm, N))
+    rc = (lib or _load()).ssd_oracle_selective_scan(
+        _ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final),
+        b, L, Dm, N, int(nthreads))
+    if rc != 0:
+        raise ValueError("ssd_oracle_selective_scan rejected its arguments")
+    return y, final
 
 
 def n_chunks(seqlen: int, chunk_size: int) -> int:

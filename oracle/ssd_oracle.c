@@ -141,6 +141,62 @@ int ssd_oracle_step(double* state, const double* x, const double* dt, const doub
     return 0;
 }
 
+/* The Mamba-1 selective scan, the layer Mamba-2 replaces (mohakchugh blog,
+ * section "Mamba-1: Selective State Spaces"): every channel d of the input
+ * has its own diagonal N x N transition, so each of its N state entries
+ * decays at its own rate a_t[d, n] = exp(delta_t[d] A[d, n]) (the diagonal
+ * structure of "Transformers are SSMs" paper card, section "How It Works";
+ * Abar = exp(Delta A) of the same blog, section "The Core Abstraction"),
+ * while delta is per channel and B, C are per token, shared by all channels
+ * (that blog's selection listing gives B, C the shape (batch, seq_len,
+ * state_dim) and delta (batch, seq_len, d_model)):
+ *
+ *   h_t[d, n] = a_t[d, n] h_{t-1}[d, n] + (delta_t[d] x_t[d]) B_t[n]
+ *   y_t[d]    = sum_n C_t[n] h_t[d, n] + D[d] x_t[d]
+ *
+ * The input enters as delta * B * x, as in the SSD recurrence above.
+ * Layouts (row-major, all double): x, delta, y (B,L,Dm); A (Dm,N); D (Dm);
+ * B, C (B,L,N); init and final (B,Dm,N).  Every (b, d) row is independent. */
+int ssd_oracle_selective_scan(const double* x, const double* delta, const double* A, const double* Bm,
+                              const double* Cm, const double* D, const double* init, double* y,
+                              double* final_states, int64_t batch, int64_t seqlen, int64_t dim,
+                              int64_t dstate, int nthreads)
+{
+    if (batch < 0 || seqlen < 0 || dim <= 0 || dstate <= 0) return -1;
+    const int64_t rows = batch * dim;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel
+    {
+        double* S = (double*)malloc(sizeof(double) * (size_t)dstate);
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t r = 0; r < rows; ++r) {
+            const int64_t b = r / dim;
+            const int64_t d = r % dim;
+            for (int64_t n = 0; n < dstate; ++n) S[n] = init ? init[r * dstate + n] : 0.0;
+            for (int64_t t = 0; t < seqlen; ++t) {
+                const int64_t bt = b * seqlen + t;
+                const double dl = delta[bt * dim + d];
+                const double xv = x[bt * dim + d];
+                const double u = dl * xv;
+                double acc = 0.0;
+                for (int64_t n = 0; n < dstate; ++n) {
+                    const double a = exp(dl * A[d * dstate + n]);
+                    S[n] = a * S[n] + u * Bm[bt * dstate + n];
+                    acc += Cm[bt * dstate + n] * S[n];
+                }
+                y[bt * dim + d] = acc + D[d] * xv;
+            }
+            memcpy(final_states + r * dstate, S, sizeof(double) * (size_t)dstate);
+        }
+        free(S);
+    }
+    return 0;
+}
+
 int ssd_oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -318,3 +318,123 @@ ALL_PINS = [
     pin_skip_only, pin_zero_input, pin_linearity_causality, pin_split_resume, pin_groups,
     pin_step_matches_forward, pin_hand_example, pin_chunk_helpers,
 ]
+
+
+# ----------------------------------------------------------------------------------------------
+# The Mamba-1 selective scan (per-channel diagonal decays; mohakchugh blog, "Mamba-1: Selective
+# State Spaces").  Pins S1-S5.
+
+def rand_scan_problem(seed, b=2, L=20, Dm=5, N=4, init=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((b, L, Dm))
+    delta = np.logaddexp(0.0, rng.standard_normal((b, L, Dm)) - 1.0)
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), (Dm, N)))
+    Bm = rng.standard_normal((b, L, N)) / np.sqrt(N)
+    Cm = rng.standard_normal((b, L, N)) / np.sqrt(N)
+    D = rng.standard_normal(Dm)
+    h0 = 0.3 * rng.standard_normal((b, Dm, N)) if init else None
+    return x, delta, A, Bm, Cm, D, h0
+
+
+def dense_scan(x, delta, A, Bm, Cm, D, h0):
+    """y and final state of the selective scan from its explicit expansion: the
+    contribution of token i to y_t is sum_n C_t[n] B_i[n] delta_i x_i prod_{j=i+1..t} a_j[n],
+    a_j[n] = exp(delta_j A[d, n]), formed as explicit products (no recurrence)."""
+    b, L, Dm = x.shape
+    N = A.shape[1]
+    y = np.zeros((b, L, Dm))
+    fin = np.zeros((b, Dm, N))
+    for bi in range(b):
+        for d in range(Dm):
+            a = np.exp(delta[bi, :, d, None] * A[d][None, :])          # (L, N)
+            for t in range(L):
+                acc = D[d] * x[bi, t, d]
+                for i in range(t + 1):
+                    dec = np.prod(a[i + 1:t + 1], axis=0)             # (N,)
+                    acc += np.sum(Cm[bi, t] * Bm[bi, i] * dec) * delta[bi, i, d] * x[bi, i, d]
+                if h0 is not None:
+                    acc += np.sum(Cm[bi, t] * np.prod(a[:t + 1], axis=0) * h0[bi, d])
+                y[bi, t, d] = acc
+            for i in range(L):
+                fin[bi, d] += np.prod(a[i + 1:], axis=0) * Bm[bi, i] * delta[bi, i, d] * x[bi, i, d]
+            if h0 is not None:
+                fin[bi, d] += np.prod(a, axis=0) * h0[bi, d]
+    return y, fin
+
+
+def pin_scan_dense_form(lib=None):
+    """S1: selective scan == its explicit expansion (with and without an initial state)."""
+    for seed, init in ((21, False), (22, True)):
+        x, delta, A, Bm, Cm, D, h0 = rand_scan_problem(seed, init=init)
+        y, fin = oracle.selective_scan(x, delta, A, Bm, Cm, D, h0, lib=lib)
+        y_ref, fin_ref = dense_scan(x, delta, A, Bm, Cm, D, h0)
+        assert _rel(y, y_ref) < TOL, f"scan dense form y seed={seed}: {_rel(y, y_ref)}"
+        assert _rel(fin, fin_ref) < TOL, f"scan dense form final seed={seed}: {_rel(fin, fin_ref)}"
+
+
+def pin_scan_scalar_identity(lib=None):
+    """S2: with every state entry of a channel decaying at one rate (A[d, n] = A_d, the
+    scalar-times-identity restriction of the "Transformers are SSMs" paper card, "How It
+    Works"), the selective scan is the SSD layer with one head per channel, head dimension 1
+    and B, C shared: its dense matrix-mixer form (pin P1's builder)."""
+    x, delta, A, Bm, Cm, D, h0 = rand_scan_problem(23, b=2, L=16, Dm=3, N=4, init=True)
+    A_h = A[:, 0].copy()
+    A = np.repeat(A_h[:, None], A.shape[1], axis=1)
+    y, fin = oracle.selective_scan(x, delta, A, Bm, Cm, D, h0, lib=lib)
+    y_ref, fin_ref = dense_mixer(x[..., None], delta, A_h, Bm[:, :, None, :], Cm[:, :, None, :], D,
+                                 h0[:, :, None, :])
+    assert _rel(y, y_ref[..., 0]) < TOL, f"scalar identity y: {_rel(y, y_ref[..., 0])}"
+    assert _rel(fin, fin_ref[:, :, 0, :]) < TOL, f"scalar identity final: {_rel(fin, fin_ref[:, :, 0, :])}"
+
+
+def pin_scan_one_hot_filters(lib=None):
+    """S3: with delta constant per channel, B constant and C picking one state entry n0, every
+    channel is a first-order IIR filter with pole exp(delta_d A[d, n0]) (scipy.signal.lfilter);
+    this fixes which entry of A each (channel, state) pair decays with."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(24)
+    L, Dm, N = 40, 3, 5
+    x = rng.standard_normal((1, L, Dm))
+    dl = np.array([0.2, 0.45, 0.7])
+    delta = np.broadcast_to(dl, (1, L, Dm)).copy()
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), (Dm, N)))
+    D = rng.standard_normal(Dm)
+    b0, c0 = 0.8, -1.1
+    Bm = np.full((1, L, N), b0)
+    for n0 in range(N):
+        Cm = np.zeros((1, L, N))
+        Cm[0, :, n0] = c0
+        y, _ = oracle.selective_scan(x, delta, A, Bm, Cm, D, None, lib=lib)
+        for d in range(Dm):
+            ref = lfilter([c0 * dl[d] * b0], [1.0, -np.exp(dl[d] * A[d, n0])], x[0, :, d]) + D[d] * x[0, :, d]
+            assert _rel(y[0, :, d], ref) < TOL, f"one-hot filter n0={n0} d={d}: {_rel(y[0, :, d], ref)}"
+
+
+def pin_scan_zero_input(lib=None):
+    """S4: x = 0 leaves only the decayed initial state:
+    y_t[d] = sum_n C_t[n] exp(A[d, n] sum_{j<=t} delta_j[d]) h0[d, n] (a closed form through
+    the running sum of delta), and the final state is exp(A[d, n] sum_j delta_j[d]) h0[d, n]."""
+    x, delta, A, Bm, Cm, D, h0 = rand_scan_problem(25, b=2, L=30, Dm=4, N=3, init=True)
+    x = np.zeros_like(x)
+    y, fin = oracle.selective_scan(x, delta, A, Bm, Cm, D, h0, lib=lib)
+    cum = np.cumsum(delta, axis=1)                                     # (b, L, Dm)
+    dec = np.exp(cum[..., None] * A[None, None])                       # (b, L, Dm, N)
+    ref = np.einsum("btn,btdn,bdn->btd", Cm, dec, h0)
+    assert _rel(y, ref) < TOL, f"scan zero input: {_rel(y, ref)}"
+    assert _rel(fin, dec[:, -1] * h0) < TOL
+
+
+def pin_scan_split_resume(lib=None):
+    """S5: scanning a prefix, then the rest from the prefix's final state, equals one scan."""
+    x, delta, A, Bm, Cm, D, h0 = rand_scan_problem(26, b=2, L=33, Dm=4, N=6, init=True)
+    y, fin = oracle.selective_scan(x, delta, A, Bm, Cm, D, h0, lib=lib)
+    L1 = 14
+    y1, f1 = oracle.selective_scan(x[:, :L1], delta[:, :L1], A, Bm[:, :L1], Cm[:, :L1], D, h0, lib=lib)
+    y2, f2 = oracle.selective_scan(x[:, L1:], delta[:, L1:], A, Bm[:, L1:], Cm[:, L1:], D, f1, lib=lib)
+    assert _rel(np.concatenate([y1, y2], axis=1), y) < TOL
+    assert _rel(f2, fin) < TOL
+
+
+SCAN_PINS = [pin_scan_dense_form, pin_scan_scalar_identity, pin_scan_one_hot_filters, pin_scan_zero_input,
+             pin_scan_split_resume]
+ALL_PINS = ALL_PINS + SCAN_PINS

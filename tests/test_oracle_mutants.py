@@ -8,7 +8,7 @@ import subprocess
 import pytest
 
 import oracle
-from oracle_pins import (pin_dense_quadratic_form, pin_groups, pin_hand_example, pin_skip_only,
+from oracle_pins import (SCAN_PINS, pin_dense_quadratic_form, pin_groups, pin_hand_example, pin_skip_only,
                          pin_step_matches_forward, pin_zero_input, pin_scalar_closed_forms)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -30,14 +30,32 @@ MUTANTS = {
                                 "const double a = exp((t ? dt[(b * seqlen + t - 1) * nheads + h] : dtv) * A[h]);", 1)],
 }
 
+# mistakes planted in the selective scan (the Mamba-1 recurrence), caught by its own pins
+SCAN_MUTANTS = {
+    "scan_dropped_skip_term": [("y[bt * dim + d] = acc + D[d] * xv;", "y[bt * dim + d] = acc;")],
+    "scan_decay_sign": [("exp(dl * A[d * dstate + n])", "exp(-dl * A[d * dstate + n])")],
+    "scan_A_transposed": [("A[d * dstate + n]", "A[n * dim + d]")],
+    "scan_decay_shared_over_states": [("A[d * dstate + n]", "A[d * dstate]")],
+    "scan_input_not_scaled_by_delta": [("const double u = dl * xv;", "const double u = xv;")],
+    "scan_B_C_swapped_in_update": [("S[n] = a * S[n] + u * Bm[bt * dstate + n];",
+                                    "S[n] = a * S[n] + u * Cm[bt * dstate + n];")],
+    "scan_readout_before_update": [("S[n] = a * S[n] + u * Bm[bt * dstate + n];\n                    acc += Cm[bt * dstate + n] * S[n];",
+                                    "acc += Cm[bt * dstate + n] * S[n];\n                    S[n] = a * S[n] + u * Bm[bt * dstate + n];")],
+    "scan_decay_after_input": [("S[n] = a * S[n] + u * Bm[bt * dstate + n];", "S[n] = a * (S[n] + u * Bm[bt * dstate + n]);")],
+    "scan_init_ignored": [("init ? init[r * dstate + n] : 0.0", "0.0")],
+    "scan_delta_of_neighbour_channel": [("const double dl = delta[bt * dim + d];",
+                                         "const double dl = delta[bt * dim + (d + 1) % dim];")],
+}
+
 PINS = [pin_hand_example, pin_skip_only, pin_zero_input, pin_scalar_closed_forms, pin_groups,
         pin_dense_quadratic_form, pin_step_matches_forward]
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(SCAN_MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
     src = open(SRC).read()
-    for old, new, *count in MUTANTS[name]:
+    edits, pins = (MUTANTS[name], PINS) if name in MUTANTS else (SCAN_MUTANTS[name], SCAN_PINS)
+    for old, new, *count in edits:
         assert old in src, f"mutation site for {name} not found"
         src = src.replace(old, new, *count)
     path = tmp_path / "ssd_oracle_mutant.c"
@@ -46,7 +64,7 @@ def test_mutant_is_caught(name, tmp_path):
     subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-o", str(so), str(path), "-lm"])
     lib = oracle.load_variant(str(so))
     caught = []
-    for pin in PINS:
+    for pin in pins:
         try:
             pin(lib=lib)
         except AssertionError:
