@@ -42,6 +42,8 @@ def parse_args():
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-mode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--no-scan", action="store_true", help="skip the Mamba-1 selective-scan comparison leg")
+    ap.add_argument("--scan-calls", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for HBM byte counters) and exit")
     return ap.parse_args()
@@ -70,6 +72,13 @@ def kernel_work(b, L, H, P, N, G, Q, es, init):
                            + 2 * b * L * H * N * P + 2 * b * L * H * P),
     }
     return work
+
+
+# Vector-ALU ceiling of the selective scan: each (token, channel, state) update needs four fp32
+# VALU operations (delta*A, u*B, the state FMA, the readout FMA) and one exponential.  A SIMD
+# retires 16 lanes of a plain VALU op per cycle and a transcendental at a quarter of that, so an
+# update costs 8 lane-cycles: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz / 8 = 4.9e12 updates/s.
+SCAN_UPDATE_PEAK = 256 * 4 * 16 * 2.4e9 / 8
 
 
 def step_work(b, H, P, N, G, es):
@@ -279,6 +288,48 @@ def main():
                       traffic=measured_traffic("decode", "ssd_step"))
         print(f"[bench] ssd_step: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ---- the Mamba-1 selective scan at the same layer width (for the SSD-vs-scan comparison)
+    scan = None
+    if not args.no_scan:
+        from mamba_ssd_sequence_chunked_amd.inputs import SCAN_CONFIGS
+        sb, sL, sD, sN, _, _, _, sseed = SCAN_CONFIGS["scan2p7b"]
+        g = torch.Generator(device=dev)
+        g.manual_seed(sseed)
+        sx = torch.randn((sb, sL, sD), generator=g, device=dev).to(torch.bfloat16)
+        sdl = torch.nn.functional.softplus(torch.randn((sb, sL, sD), generator=g, device=dev) + float(np.log(np.expm1(0.01))))
+        sA = -torch.exp(torch.rand((sD, sN), generator=g, device=dev) * float(np.log(16.0)))
+        sBm = (torch.randn((sb, sL, sN), generator=g, device=dev) / sN ** 0.5).to(torch.bfloat16)
+        sCm = (torch.randn((sb, sL, sN), generator=g, device=dev) / sN ** 0.5).to(torch.bfloat16)
+        sDv = torch.randn(sD, generator=g, device=dev)
+        sy = torch.empty_like(sx)
+        sfin = torch.empty((sb, sD, sN), dtype=torch.float32, device=dev)
+
+        def scan_call():
+            rc = lib.ssd_selective_scan(p(sx), p(sdl), p(sA), p(sBm), p(sCm), p(sDv), None, p(sy), p(sfin), sb, sL,
+                                        sD, sN, ssd.SSD_BF16, sp)
+            if rc:
+                raise ssd.SSDError("ssd_selective_scan", rc)
+
+        scan_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.scan_calls):
+            scan_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.scan_calls
+        upd = sb * sL * sD * sN / (us / 1e6)
+        scan = dict(workload=f"scan2p7b: Mamba-1 selective scan, batch {sb}, seqlen {sL}, {sD} channels, dstate {sN}, "
+                             "bf16 x/B/C (inputs drawn on the device, timing only)",
+                    calls=args.scan_calls, us_per_call=round(us, 1), tokens_per_s=round(sb * sL / (us / 1e6), 1),
+                    bound="alu", updates_per_s=round(upd, 1), peak_updates_per_s=SCAN_UPDATE_PEAK,
+                    frac=round(upd / SCAN_UPDATE_PEAK, 4),
+                    # same batch and tokens as the l2p7b forward (whose state is 8x larger)
+                    time_over_ssd_forward=round(us / (ms_per_step * 1e3), 3) if args.workload == "l2p7b" else None)
+        print(f"[bench] selective scan: {us:.1f} us/call", file=sys.stderr, flush=True)
+        del sx, sdl, sBm, sCm, sy
+
     # ---- the fp64 CPU oracle on the host, beside it
     cpu = None
     if not args.no_cpu_baseline:
@@ -310,6 +361,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "ssd_step": decode,
+        "selective_scan": scan,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

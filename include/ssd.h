@@ -27,6 +27,10 @@
  *   ssd_step    - the recurrent mode: one token per call, O(1) in the
  *                 sequence length (crackai.dev paper card, "Why It Matters").
  *
+ * For comparison the library also runs the layer SSD replaces, the Mamba-1
+ * selective scan with a diagonal transition per channel
+ * (ssd_selective_scan, at the end of this header).
+ *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers (current HIP device) to dense,
  *     row-major arrays in the layouts given per call.  The caller owns every
@@ -178,6 +182,30 @@ int ssd_chunk_scan(const void* x, const void* B, const void* C, const float* dt_
 int ssd_step(float* state, const void* x, const float* dt, const float* A, const void* B,
              const void* C, const float* D, void* y, int64_t batch, int64_t nheads,
              int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * The Mamba-1 selective scan (mohakchugh blog, section "Mamba-1: Selective State Spaces"): each
+ * channel d of the input has its own diagonal transition, one decay per state entry, and B, C
+ * are per token, shared by all channels:
+ *
+ *     h_t[d, n] = exp(delta_t[d] A[d, n]) h_{t-1}[d, n] + (delta_t[d] x_t[d]) B_t[n]
+ *     y_t[d]    = sum_n C_t[n] h_t[d, n] + D[d] x_t[d]
+ *
+ * The input enters as delta * B * x, as in ssd_forward.  It runs as a sequential scan on the
+ * vector units (one kernel); there is no workspace.
+ *   x T (batch, seqlen, dim); delta float (batch, seqlen, dim), positive
+ *   A float (dim, dstate), negative or zero; D float (dim)
+ *   B, C T (batch, seqlen, dstate)
+ *   init_states float (batch, dim, dstate) or NULL (zeros)
+ *   y T (batch, seqlen, dim), written; final_states float (batch, dim, dstate), written
+ * Shape limits: 0 <= batch <= 65535; 0 <= seqlen < 2^31; dim a multiple of 8 in [8, 2^20];
+ * dstate in {4, 8, 16, 32, 64}.  x, delta and y must be 16-byte aligned; with seqlen 0 the
+ * token arrays (x, delta, B, C, y) may be NULL and final_states receives the initial state.  Errors as above
+ * (SSD_ERR_SHAPE for a bad size or alignment, SSD_ERR_ALIAS when an output overlaps an input
+ * or the other output). */
+int ssd_selective_scan(const void* x, const float* delta, const float* A, const void* B, const void* C,
+                       const float* D, const float* init_states, void* y, float* final_states, int64_t batch,
+                       int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* stream);
 
 #ifdef __cplusplus
 }

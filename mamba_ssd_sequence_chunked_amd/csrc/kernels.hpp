@@ -32,4 +32,9 @@ template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
                            const T* C, const float* D, T* y, const Dims& d, hipStream_t stream);
 
+template <typename T>
+hipError_t launch_selective_scan(const T* x, const float* delta, const float* A, const T* B, const T* C,
+                                 const float* D, const float* init, T* y, float* final_states, int64_t batch,
+                                 int64_t seqlen, int64_t dim, int64_t dstate, hipStream_t stream);
+
 }  // namespace ssd

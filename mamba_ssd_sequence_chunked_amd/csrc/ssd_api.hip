@@ -116,7 +116,7 @@ const char* ssd_status_string(int status)
     }
 }
 
-int ssd_abi_version(void) { return 100; }
+int ssd_abi_version(void) { return 101; }
 
 int64_t ssd_num_chunks(int64_t seqlen, int64_t chunk_size)
 {
@@ -318,6 +318,38 @@ int ssd_step(float* state, const void* x, const float* dt, const float* A, const
                                                      D, (bf16*)y, d, s));
     return hip_status(ssd::launch_ssd_step<float>(state, (const float*)x, dt, A, (const float*)B, (const float*)C,
                                                   D, (float*)y, d, s));
+}
+
+int ssd_selective_scan(const void* x, const float* delta, const float* A, const void* B, const void* C,
+                       const float* D, const float* init_states, void* y, float* final_states, int64_t batch,
+                       int64_t seqlen, int64_t dim, int64_t dstate, int dtype, void* stream)
+{
+    if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
+    if (batch < 0 || batch > 65535 || seqlen < 0 || seqlen > INT32_MAX) return SSD_ERR_SHAPE;
+    if (dim < 8 || dim % 8 != 0 || dim > (int64_t(1) << 20)) return SSD_ERR_SHAPE;
+    if (dstate != 4 && dstate != 8 && dstate != 16 && dstate != 32 && dstate != 64) return SSD_ERR_SHAPE;
+    if (batch * ((dim + 31) / 32) > INT32_MAX) return SSD_ERR_SHAPE;
+    if (batch == 0) return SSD_OK;
+    if (!A || !D || !final_states) return SSD_ERR_NULL;
+    if (seqlen > 0 && (!x || !delta || !B || !C || !y)) return SSD_ERR_NULL;   // empty tensors may be NULL
+    if (!aligned16(x) || !aligned16(delta) || !aligned16(y)) return SSD_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)(batch * seqlen * dim) * es;
+    const size_t nd = (size_t)(batch * seqlen * dim) * 4;
+    const size_t nb = (size_t)(batch * seqlen * dstate) * es;
+    const size_t nst = (size_t)(batch * dim * dstate) * 4;
+    if (any_overlap({{y, nx}, {final_states, nst}},
+                    {{x, nx}, {delta, nd}, {A, (size_t)(dim * dstate) * 4}, {B, nb}, {C, nb},
+                     {D, (size_t)dim * 4}, {init_states, init_states ? nst : 0}}))
+        return SSD_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == SSD_BF16)
+        return hip_status(ssd::launch_selective_scan<bf16>((const bf16*)x, delta, A, (const bf16*)B, (const bf16*)C,
+                                                           D, init_states, (bf16*)y, final_states, batch, seqlen,
+                                                           dim, dstate, s));
+    return hip_status(ssd::launch_selective_scan<float>((const float*)x, delta, A, (const float*)B, (const float*)C,
+                                                        D, init_states, (float*)y, final_states, batch, seqlen, dim,
+                                                        dstate, s));
 }
 
 }  // extern "C"

@@ -61,6 +61,8 @@ def load_library():
     lib.ssd_chunk_scan.argtypes = [vp] * 8 + [i64] * 7 + [i32, vp]
     lib.ssd_step.restype = i32
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [i32, vp]
+    lib.ssd_selective_scan.restype = i32
+    lib.ssd_selective_scan.argtypes = [vp] * 9 + [i64] * 4 + [i32, vp]
     _lib = lib
     return lib
 
@@ -179,6 +181,37 @@ def step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor
                       G, code, _stream(dev))
     _check("ssd_step", rc)
     return y
+
+
+def selective_scan(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                   D: torch.Tensor, init_states: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The Mamba-1 selective scan (per-channel diagonal decays); see ssd_selective_scan.
+
+    x (batch, seqlen, dim); delta (batch, seqlen, dim) fp32; A (dim, dstate) fp32;
+    B, C (batch, seqlen, dstate) in x's dtype; D (dim,) fp32; init_states (batch, dim, dstate)
+    fp32 or None.  Returns (y in x's dtype, final_states fp32)."""
+    lib = load_library()
+    if x.dim() != 3 or A.dim() != 2:
+        raise ValueError("x must be (batch, seqlen, dim) and A (dim, dstate)")
+    b, L, Dm = x.shape
+    N = A.shape[1]
+    dev = x.device
+    code = _dtype_code(x)
+    _need(x, "x", (b, L, Dm), x.dtype, dev)
+    _need(delta, "delta", (b, L, Dm), torch.float32, dev)
+    _need(A, "A", (Dm, N), torch.float32, dev)
+    _need(B, "B", (b, L, N), x.dtype, dev)
+    _need(C, "C", (b, L, N), x.dtype, dev)
+    _need(D, "D", (Dm,), torch.float32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, Dm, N), torch.float32, dev)
+    y = torch.empty_like(x)
+    final = torch.empty((b, Dm, N), dtype=torch.float32, device=dev)
+    rc = lib.ssd_selective_scan(_ptr(x), _ptr(delta), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states),
+                                _ptr(y), _ptr(final), b, L, Dm, N, code, _stream(dev))
+    _check("ssd_selective_scan", rc)
+    return y, final
 
 
 # --- the four stages of the chunked mode, one entry point each ---------------------------------

@@ -34,7 +34,7 @@ def test_library_exports_every_declared_function():
     lib = ssd.load_library()
     names = declared_functions()
     assert {"ssd_forward", "ssd_step", "ssd_forward_workspace_bytes", "ssd_status_string", "ssd_dA_cumsum",
-            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"} <= set(names)
+            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_selective_scan"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in include/ssd.h but not exported"
 
@@ -43,7 +43,7 @@ def test_status_strings():
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS):
         assert ssd.status_string(code).startswith("SSD_")
     assert "unknown" in ssd.status_string(123)
-    assert ssd.load_library().ssd_abi_version() == 100
+    assert ssd.load_library().ssd_abi_version() == 101
 
 
 def test_num_chunks_and_workspace():
@@ -120,6 +120,31 @@ def test_step_rejects():
     assert call(y=fake(2)) == ERR_ALIAS
     assert call(state=P(0x10000004)) == ERR_SHAPE
     assert call(batch=0) == OK                     # nothing to do, nothing enqueued
+
+
+def test_selective_scan_rejects():
+    lib = ssd.load_library()
+
+    def call(**kw):
+        a = dict(x=fake(1), delta=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), init=None, y=fake(7),
+                 final=fake(8), batch=2, seqlen=100, dim=64, dstate=16, dtype=1)
+        a.update(kw)
+        return lib.ssd_selective_scan(a["x"], a["delta"], a["A"], a["B"], a["C"], a["D"], a["init"], a["y"],
+                                      a["final"], a["batch"], a["seqlen"], a["dim"], a["dstate"], a["dtype"], None)
+
+    assert call(dim=60) == ERR_SHAPE                 # not a multiple of 8
+    assert call(dim=0) == ERR_SHAPE
+    assert call(dstate=12) == ERR_SHAPE
+    assert call(dstate=128) == ERR_SHAPE
+    assert call(batch=65536) == ERR_SHAPE
+    assert call(seqlen=-1) == ERR_SHAPE
+    assert call(dtype=3) == ERR_DTYPE
+    assert call(final=None) == ERR_NULL
+    assert call(delta=None) == ERR_NULL
+    assert call(y=fake(1)) == ERR_ALIAS              # y == x
+    assert call(final=P(0x10000000 + 0x1000000 * 7 + 64)) == ERR_ALIAS   # final inside y
+    assert call(x=P(0x10000008)) == ERR_SHAPE        # misaligned
+    assert call(batch=0) == OK                       # nothing to do, nothing enqueued
 
 
 def test_stage_entry_points_reject():
