@@ -35,15 +35,18 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kVec = 8;                 // channels per staging load/store (16 bytes of bf16)
 
-// sum over aligned groups of W lanes (W in {1, 2, 4, 8}) with DPP lane moves
+// sum over aligned groups of W lanes (W in {1, 2, 4, 8, 16}) with DPP lane moves; every lane of a
+// group ends with the group's sum
 template <int W>
 __device__ __forceinline__ float lane_group_sum(float v) {
     if constexpr (W >= 2)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, true));   // quad_perm 1,0,3,2
     if constexpr (W >= 4)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, true));   // quad_perm 2,3,0,1
     if constexpr (W >= 8)
-        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false));  // row_half_mirror
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, true));  // row_half_mirror
+    if constexpr (W >= 16)
+        v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, true));  // row_mirror
     return v;
 }
 
@@ -185,8 +188,8 @@ __global__ __launch_bounds__(kThreads) void selective_scan_kernel(
                 h[s] = fmaf(a, h[s], u * bs[t][n]);
                 part = fmaf(cs[t][n], h[s], part);
             }
-            part = lane_group_sum<W>(part);
-            if (sub == 0) ys[t][ch] = part;
+            // all W lanes of the channel hold the sum and store it to the same word (no branch)
+            ys[t][ch] = lane_group_sum<W>(part);
         }
         __syncthreads();
         // y of the block: readout plus the skip term, 8 channels per 16-byte store
