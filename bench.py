@@ -36,8 +36,9 @@ KERNEL_SOURCES = {"dA_cumsum": "dA_cumsum.hip", "chunk_state": "chunk_state.hip"
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    # untimed; the GPU needs some tens of milliseconds of work to reach its full clocks
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="l2p7b", choices=["l130m", "l2p7b", "long64k"])
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-mode leg")

@@ -73,11 +73,16 @@ constexpr int pick_heads() {
     else return pick_heads<T, P, NK, HB / 2>();
 }
 
-template <typename T, int P, int NK, int HB>
+// kOwnCumsum: the workgroup also does stage 1 for its heads and chunk -- it reads dt (B, L, H)
+// and A, forms the in-chunk prefix sums of dt A with the same arithmetic as dA_cumsum.hip (4
+// tokens per lane summed in order, then a DPP wavefront prefix sum) and writes dA_cs and
+// dt_chunked for the later stages -- so the chunked forward needs no separate stage-1 launch.
+template <typename T, int P, int NK, int HB, bool kOwnCumsum>
 __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
-    const T* __restrict__ x, const T* __restrict__ Bm, const float* __restrict__ dt_chunked,
-    const float* __restrict__ dA_cs, float* __restrict__ chunk_states, int seqlen, int nheads,
-    int ngroups, int N, int Q, int nc, int nhb, int hpw, int nblocks)
+    const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ dt_chunked,
+    float* __restrict__ dA_cs, const float* __restrict__ dt, const float* __restrict__ A,
+    float* __restrict__ chunk_states, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb,
+    int hpw, int nblocks)
 {
     using S = StateCfg<T, P, NK, HB>;
     constexpr int EPC = S::EPC, NT = S::NT, PT = S::PT;
@@ -119,11 +124,41 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
         if (sb < nsb) issue_stage(sb);
 
     // w_l = dt_l exp(cs[Q-1] - cs[l]) per head, 0 past the sequence and for heads past the workgroup
-    for (int i = tid; i < HB * kMaxQ; i += kThreads) {
-        const int ht = i / kMaxQ, l = i % kMaxQ;
-        const int64_t base = (((int64_t)b * nheads + h0 + min(ht, nh - 1)) * nc + c) * Q;
-        const float w = dt_chunked[base + min(l, Q - 1)] * __expf(dA_cs[base + Q - 1] - dA_cs[base + min(l, Q - 1)]);
-        wt[i] = select(l < len && ht < nh, w, 0.f);
+    if constexpr (!kOwnCumsum) {
+        for (int i = tid; i < HB * kMaxQ; i += kThreads) {
+            const int ht = i / kMaxQ, l = i % kMaxQ;
+            const int64_t base = (((int64_t)b * nheads + h0 + min(ht, nh - 1)) * nc + c) * Q;
+            const float w = dt_chunked[base + min(l, Q - 1)] * __expf(dA_cs[base + Q - 1] - dA_cs[base + min(l, Q - 1)]);
+            wt[i] = select(l < len && ht < nh, w, 0.f);
+        }
+    } else if (wave < HB) {
+        // wavefront hh = wave scans its head: lane owns tokens 4 lane .. 4 lane + 3
+        const int hs = h0 + min(wave, nh - 1);
+        const float a = A[hs];
+        float v[4], cs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int l = 4 * lane + j;
+            v[j] = l < len ? dt[(b * seqlen + t0 + l) * nheads + hs] : 0.f;
+        }
+        cs[0] = v[0] * a;
+#pragma unroll
+        for (int j = 1; j < 4; ++j) cs[j] = cs[j - 1] + v[j] * a;
+        const float incl = wave_inclusive_sum(cs[3]);
+        const float excl = incl - cs[3];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs[j] += excl;
+        const float last = __shfl(cs[3], (Q - 1) / 4, kWave);       // cs[Q - 1]
+        if (wave < nh && 4 * lane + 3 < Q) {
+            const int64_t base = (((int64_t)b * nheads + hs) * nc + c) * Q + 4 * lane;
+            store4(dA_cs + base, cs[0], cs[1], cs[2], cs[3]);
+            store4(dt_chunked + base, v[0], v[1], v[2], v[3]);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int l = 4 * lane + j;
+            wt[wave * kMaxQ + l] = select(l < len && wave < nh, v[j] * __expf(last - cs[j]), 0.f);
+        }
     }
     wait_vmem();                       // the first stages and the tables' loads
     __syncthreads();
@@ -180,9 +215,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     }
 }
 
-template <typename T, int P, int NK>
-hipError_t launch(const T* x, const T* B, const float* dtc, const float* cs, float* out, const Dims& d,
-                  hipStream_t stream)
+template <typename T, int P, int NK, bool OWN>
+hipError_t launch(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
+                  const Dims& d, hipStream_t stream)
 {
     constexpr int HB = pick_heads<T, P, NK, 8>();
     static_assert(StateCfg<T, P, NK, HB>::fits, "LDS budget");
@@ -192,21 +227,25 @@ hipError_t launch(const T* x, const T* B, const float* dtc, const float* cs, flo
     const int hpw = (hpg + nhb - 1) / nhb;
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream, x,
-                       B, dtc, cs, out, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
+    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB, OWN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                       x, B, dtc, cs, dt, A, out, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
                        (int)d.chunk, nc, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, int P>
-hipError_t launch_p(const T* x, const T* B, const float* dtc, const float* cs, float* out, const Dims& d,
-                    hipStream_t stream)
+template <typename T, bool OWN>
+hipError_t launch_any(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
+                      const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
-    if (nk <= 1) return launch<T, P, 1>(x, B, dtc, cs, out, d, stream);
-    if (nk <= 2) return launch<T, P, 2>(x, B, dtc, cs, out, d, stream);
-    if (nk <= 4) return launch<T, P, 4>(x, B, dtc, cs, out, d, stream);
-    return launch<T, P, 8>(x, B, dtc, cs, out, d, stream);
+    const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
+#define SSD_CS_CASE(PP, KK) \
+    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, OWN>(x, B, dtc, cs, dt, A, out, d, stream);
+#define SSD_CS_P(PP) SSD_CS_CASE(PP, 1) SSD_CS_CASE(PP, 2) SSD_CS_CASE(PP, 4) SSD_CS_CASE(PP, 8)
+    SSD_CS_P(16) SSD_CS_P(32) SSD_CS_P(64) SSD_CS_P(128)
+#undef SSD_CS_P
+#undef SSD_CS_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -215,18 +254,25 @@ template <typename T>
 hipError_t launch_chunk_state(const T* x, const T* B, const float* dt_chunked, const float* dA_cs,
                               float* chunk_states, const Dims& d, hipStream_t stream)
 {
-    switch (d.headdim) {
-    case 16: return launch_p<T, 16>(x, B, dt_chunked, dA_cs, chunk_states, d, stream);
-    case 32: return launch_p<T, 32>(x, B, dt_chunked, dA_cs, chunk_states, d, stream);
-    case 64: return launch_p<T, 64>(x, B, dt_chunked, dA_cs, chunk_states, d, stream);
-    case 128: return launch_p<T, 128>(x, B, dt_chunked, dA_cs, chunk_states, d, stream);
-    default: return hipErrorInvalidValue;
-    }
+    // stage 2 alone: the prefix sums come from stage 1 and are only read
+    return launch_any<T, false>(x, B, const_cast<float*>(dt_chunked), const_cast<float*>(dA_cs), nullptr, nullptr,
+                                chunk_states, d, stream);
+}
+
+template <typename T>
+hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, const float* A, float* dt_chunked,
+                                     float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream)
+{
+    return launch_any<T, true>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, d, stream);
 }
 
 template hipError_t launch_chunk_state<float>(const float*, const float*, const float*, const float*,
                                               float*, const Dims&, hipStream_t);
 template hipError_t launch_chunk_state<bf16>(const bf16*, const bf16*, const float*, const float*,
                                              float*, const Dims&, hipStream_t);
+template hipError_t launch_chunk_state_cumsum<float>(const float*, const float*, const float*, const float*,
+                                                     float*, float*, float*, const Dims&, hipStream_t);
+template hipError_t launch_chunk_state_cumsum<bf16>(const bf16*, const bf16*, const float*, const float*,
+                                                    float*, float*, float*, const Dims&, hipStream_t);
 
 }  // namespace ssd

@@ -18,6 +18,11 @@ template <typename T>
 hipError_t launch_chunk_state(const T* x, const T* B, const float* dt_chunked, const float* dA_cs,
                               float* chunk_states, const Dims& d, hipStream_t stream);
 
+// stage 2 with stage 1 folded in: also writes dA_cs and dt_chunked from dt and A
+template <typename T>
+hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, const float* A, float* dt_chunked,
+                                     float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, const float* init,
                                 T* entry_states, float* final_states, const Dims& d,

@@ -272,17 +272,17 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
             return hip_status(ssd::launch_state_passing<bf16>(nullptr, nullptr, init_states, nullptr, final_states, d, s));
         return hip_status(ssd::launch_state_passing<float>(nullptr, nullptr, init_states, nullptr, final_states, d, s));
     }
-    hipError_t e = ssd::launch_dA_cumsum(dt, A, cs, dtc, d, s);
-    if (e != hipSuccess) return SSD_ERR_HIP;
+    // stage 1 runs inside the stage-2 kernel (each workgroup scans dt A for its heads and chunk)
+    hipError_t e;
     if (dtype == SSD_BF16) {
-        e = ssd::launch_chunk_state<bf16>((const bf16*)x, (const bf16*)B, dtc, cs, states, d, s);
+        e = ssd::launch_chunk_state_cumsum<bf16>((const bf16*)x, (const bf16*)B, dt, A, dtc, cs, states, d, s);
         if (e == hipSuccess)
             e = ssd::launch_state_passing<bf16>(states, cs, init_states, (bf16*)entry, final_states, d, s);
         if (e == hipSuccess)
             e = ssd::launch_chunk_scan<bf16>((const bf16*)x, (const bf16*)B, (const bf16*)C, dtc, cs,
                                              (const bf16*)entry, D, (bf16*)y, d, s);
     } else {
-        e = ssd::launch_chunk_state<float>((const float*)x, (const float*)B, dtc, cs, states, d, s);
+        e = ssd::launch_chunk_state_cumsum<float>((const float*)x, (const float*)B, dt, A, dtc, cs, states, d, s);
         if (e == hipSuccess)
             e = ssd::launch_state_passing<float>(states, cs, init_states, (float*)entry, final_states, d, s);
         if (e == hipSuccess)
