@@ -17,6 +17,13 @@ library is measured on:
   decode   bf16, batch 256 H=80 P=64 N=128 G=1, 1024 single-token steps on
            an fp32 state initialised N(0, 0.1^2)
 
+packed variable-length batches,
+
+  varlen2p7b the l2p7b layer shape over 16384 packed tokens split into
+           sequences of seeded uniform lengths in [64, 4096] (the last one
+           cut to fit), state reset at every sequence start; per-token draws
+           as for a batch of one
+
 and, for the Mamba-1 selective scan the SSD layer is compared with,
 
   scan2p7b bf16, B=4 L=4096 channels 5120 N=16 (the same 2.7B-class layer
@@ -44,7 +51,8 @@ import numpy as np
 __all__ = [
     "CONFIGS", "SSDConfig", "SSDInputs", "StepInputs", "ScanInputs", "SCAN_CONFIGS", "bf16_bits",
     "bf16_to_f64", "make_inputs", "make_step_params", "make_step_inputs", "make_random",
-    "make_scan_random", "make_scan_inputs",
+    "make_scan_random", "make_scan_inputs", "VarlenInputs", "VARLEN_CONFIGS", "varlen_lengths",
+    "make_varlen", "make_varlen_inputs",
 ]
 
 
@@ -263,3 +271,56 @@ def make_scan_random(batch, seqlen, dim, dstate, dtype="bf16", dt_kind="ranged",
 def make_scan_inputs(name: str) -> ScanInputs:
     b, l, d, n, dtype, kind, init, seed = SCAN_CONFIGS[name]
     return make_scan_random(b, l, d, n, dtype, kind, init, seed)
+
+
+@dataclasses.dataclass
+class VarlenInputs:
+    """Packed sequences: sequence k is tokens cu_seqlens[k] .. cu_seqlens[k+1]-1."""
+    x: np.ndarray          # (T, nheads, headdim) storage dtype
+    dt: np.ndarray         # (T, nheads)
+    A: np.ndarray          # (nheads,)
+    B: np.ndarray          # (T, ngroups, dstate)
+    C: np.ndarray          # (T, ngroups, dstate)
+    D: np.ndarray          # (nheads,)
+    cu_seqlens: np.ndarray  # (nseq + 1,) int32
+    chunk_size: int
+    dtype: str
+
+    def f64(self, name: str) -> np.ndarray:
+        a = getattr(self, name)
+        if name in ("x", "B", "C") and self.dtype == "bf16":
+            return bf16_to_f64(a)
+        return a.astype(np.float64)
+
+
+def varlen_lengths(total: int, lo: int, hi: int, seed: int) -> np.ndarray:
+    """Seeded sequence lengths, uniform integers in [lo, hi], the last cut so they sum to total."""
+    rng = np.random.default_rng(seed)
+    out = []
+    left = total
+    while left > 0:
+        n = min(int(rng.integers(lo, hi + 1)), left)
+        out.append(n)
+        left -= n
+    return np.array(out, dtype=np.int64)
+
+
+def make_varlen(lengths, nheads, headdim, dstate, ngroups, chunk_size, dtype="bf16", dt_kind="ranged",
+                seed=0) -> VarlenInputs:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    T = int(lengths.sum())
+    p = make_random(1, T, nheads, headdim, dstate, ngroups, chunk_size, dtype, dt_kind, False, seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    return VarlenInputs(x=p.x[0], dt=p.dt[0], A=p.A, B=p.B[0], C=p.C[0], D=p.D, cu_seqlens=cu,
+                        chunk_size=chunk_size, dtype=dtype)
+
+
+VARLEN_CONFIGS = {
+    # name: (total tokens, length range, nheads, headdim, dstate, ngroups, chunk, dtype, dt_kind, seed)
+    "varlen2p7b": (16384, (64, 4096), 80, 64, 128, 1, 256, "bf16", "ranged", 6),
+}
+
+
+def make_varlen_inputs(name: str) -> VarlenInputs:
+    T, (lo, hi), H, P, N, G, Q, dtype, kind, seed = VARLEN_CONFIGS[name]
+    return make_varlen(varlen_lengths(T, lo, hi, seed), H, P, N, G, Q, dtype, kind, seed)

@@ -6,7 +6,8 @@ calls anything here, and nothing here imports the library.
 
 ``forward`` and ``step`` call the plain C recurrence in ``ssd_oracle.c``
 (token by token, double precision, one independent (b, h, p) row per
-OpenMP task); ``selective_scan`` calls the Mamba-1 recurrence there (one
+OpenMP task); ``forward_varlen`` runs ``forward`` on each sequence of a
+packed batch; ``selective_scan`` calls the Mamba-1 recurrence there (one
 (b, channel) row per task).  The helpers below it are written on top of those two calls
 and plain numpy indexing only:
 
@@ -138,6 +139,31 @@ def step(state, x, dt, A, B, C, D, nthreads: int = 0, lib=None):
     if rc != 0:
         raise ValueError("ssd_oracle_step rejected its arguments")
     return y, st
+
+
+def forward_varlen(x, dt, A, B, C, D, cu_seqlens, nthreads: int = 0, lib=None):
+    """Packed variable-length sequences: sequence k is tokens cu_seqlens[k] .. cu_seqlens[k+1]-1
+    of the packed arrays and starts from a zero state (the recurrence is reset at every sequence
+    start); each sequence is run through ``forward`` on its own.
+
+    x (T,H,P); dt (T,H); A, D (H,); B, C (T,G,N); cu_seqlens (nseq+1,) non-decreasing from 0 to T.
+    Returns (y (T,H,P), final (nseq,H,P,N)) in fp64; an empty sequence's final state is zero."""
+    x, dt, B, C = (_f64(a) for a in (x, dt, B, C))
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    T, H, P = x.shape
+    N = B.shape[2]
+    assert cu[0] == 0 and cu[-1] == T and np.all(np.diff(cu) >= 0), "cu_seqlens must run from 0 to T"
+    y = np.empty((T, H, P))
+    final = np.zeros((len(cu) - 1, H, P, N))
+    for k in range(len(cu) - 1):
+        a, e = int(cu[k]), int(cu[k + 1])
+        if e == a:
+            continue
+        yk, fk = forward(x[None, a:e], dt[None, a:e], A, B[None, a:e], C[None, a:e], D, None,
+                         nthreads=nthreads, lib=lib)
+        y[a:e] = yk[0]
+        final[k] = fk[0]
+    return y, final
 
 
 def selective_scan(x, delta, A, B, C, D, init=None, nthreads: int = 0, lib=None):

@@ -438,3 +438,82 @@ def pin_scan_split_resume(lib=None):
 SCAN_PINS = [pin_scan_dense_form, pin_scan_scalar_identity, pin_scan_one_hot_filters, pin_scan_zero_input,
              pin_scan_split_resume]
 ALL_PINS = ALL_PINS + SCAN_PINS
+
+
+# ----------------------------------------------------------------------------------------------
+# Packed variable-length batches (state reset at every sequence start).  Pins V1-V3.
+
+def dense_mixer_packed(x, dt, A, Bm, Cm, D, seq_id):
+    """y of a packed stream from the dense matrix-mixer form over ALL its tokens, with the
+    entries that connect two different sequences set to zero (a block-diagonal mixer): the
+    decays are explicit products of a_j over the whole stream, so a missing reset would leave
+    cross-sequence entries nonzero."""
+    T, H, P = x.shape
+    G = Bm.shape[1]
+    hpg = H // G
+    y = np.zeros((T, H, P))
+    same = seq_id[:, None] == seq_id[None, :]
+    for h in range(H):
+        g = h // hpg
+        a = np.exp(dt[:, h] * A[h])
+        dec = np.zeros((T, T))
+        for t in range(T):
+            for i in range(t + 1):
+                dec[t, i] = np.prod(a[i + 1:t + 1])
+        M = np.tril((Cm[:, g, :] @ Bm[:, g, :].T) * dec * dt[None, :, h]) * same
+        y[:, h, :] = M @ x[:, h, :] + D[h] * x[:, h, :]
+    return y
+
+
+def _packed(seed, lens, H=3, P=2, N=4, G=1):
+    rng = np.random.default_rng(seed)
+    T = int(sum(lens))
+    x = rng.standard_normal((T, H, P))
+    dt = np.logaddexp(0.0, rng.standard_normal((T, H)) - 1.0)
+    A = -np.exp(rng.uniform(0.0, np.log(16.0), H))
+    Bm = rng.standard_normal((T, G, N)) / np.sqrt(N)
+    Cm = rng.standard_normal((T, G, N)) / np.sqrt(N)
+    D = rng.standard_normal(H)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return x, dt, A, Bm, Cm, D, cu
+
+
+def pin_varlen_dense_form(lib=None):
+    """V1: the packed forward == the block-diagonal dense mixer of the whole stream."""
+    for seed, lens, G in ((31, [5, 1, 9, 7], 1), (32, [12, 3, 3, 6], 3)):
+        x, dt, A, Bm, Cm, D, cu = _packed(seed, lens, G=G)
+        seq_id = np.repeat(np.arange(len(lens)), lens)
+        y, _ = oracle.forward_varlen(x, dt, A, Bm, Cm, D, cu, lib=lib)
+        ref = dense_mixer_packed(x, dt, A, Bm, Cm, D, seq_id)
+        assert _rel(y, ref) < TOL, f"varlen dense form seed={seed}: {_rel(y, ref)}"
+
+
+def pin_varlen_equal_lengths_batch(lib=None):
+    """V2: sequences of one length packed end to end == the same sequences as a batch."""
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(33, b=3, L=11, H=4, P=3, N=5, G=2, init=False)
+    yb, fb = oracle.forward(x, dt, A, Bm, Cm, D, None, lib=lib)
+    cu = np.arange(4) * 11
+    y, f = oracle.forward_varlen(x.reshape(33, 4, 3), dt.reshape(33, 4), A, Bm.reshape(33, 2, 5),
+                                 Cm.reshape(33, 2, 5), D, cu, lib=lib)
+    assert _rel(y, yb.reshape(33, 4, 3)) < TOL
+    assert _rel(f, fb) < TOL
+
+
+def pin_varlen_final_states(lib=None):
+    """V3: a sequence's final state is the dense form's: sum_i prod_{j>i} a_j dt_i x_i B_i^T over
+    its own tokens only; an empty sequence's is zero."""
+    lens = [4, 0, 6, 1]
+    x, dt, A, Bm, Cm, D, cu = _packed(34, lens, H=2, P=2, N=3)
+    _, f = oracle.forward_varlen(x, dt, A, Bm, Cm, D, cu, lib=lib)
+    for k in range(len(lens)):
+        a, e = cu[k], cu[k + 1]
+        for h in range(2):
+            ref = np.zeros((2, 3))
+            for i in range(a, e):
+                w = np.prod(np.exp(dt[i + 1:e, h] * A[h])) * dt[i, h]
+                ref += w * np.outer(x[i, h], Bm[i, 0])
+            assert np.max(np.abs(f[k, h] - ref)) < TOL * max(1.0, np.max(np.abs(ref))), (k, h)
+
+
+VARLEN_PINS = [pin_varlen_dense_form, pin_varlen_equal_lengths_batch, pin_varlen_final_states]
+ALL_PINS = ALL_PINS + VARLEN_PINS

@@ -70,3 +70,38 @@ def test_mutant_is_caught(name, tmp_path):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+# mistakes planted in the packed variable-length driver (Python), each caught by the varlen pins
+def _varlen_no_reset(x, dt, A, B, C, D, cu_seqlens, nthreads=0, lib=None):
+    """the whole packed stream run as one sequence (state carried across sequence starts)"""
+    import numpy as np
+    y, f = oracle.forward(np.asarray(x)[None], np.asarray(dt)[None], A, np.asarray(B)[None], np.asarray(C)[None], D,
+                          None, lib=lib)
+    cu = np.asarray(cu_seqlens)
+    fin = np.zeros((len(cu) - 1,) + f.shape[1:])
+    return y[0], fin
+
+
+def _varlen_shifted_boundary(x, dt, A, B, C, D, cu_seqlens, nthreads=0, lib=None):
+    """every sequence start moved one token late"""
+    import numpy as np
+    cu = np.asarray(cu_seqlens).copy()
+    cu[1:-1] = np.minimum(cu[1:-1] + 1, cu[-1])
+    return _ORIG_VARLEN(x, dt, A, B, C, D, cu, nthreads=nthreads, lib=lib)
+
+
+_ORIG_VARLEN = oracle.forward_varlen
+
+
+@pytest.mark.parametrize("mutant", [_varlen_no_reset, _varlen_shifted_boundary], ids=["no_reset", "shifted_boundary"])
+def test_varlen_mutant_is_caught(mutant, monkeypatch):
+    from oracle_pins import VARLEN_PINS
+    monkeypatch.setattr(oracle, "forward_varlen", mutant)
+    caught = []
+    for pin in VARLEN_PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught {mutant.__name__}"
