@@ -44,6 +44,7 @@ def parse_args():
     ap.add_argument("--no-decode", action="store_true", help="skip the recurrent-mode leg")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-scan", action="store_true", help="skip the Mamba-1 selective-scan comparison leg")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length leg")
     ap.add_argument("--scan-calls", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for HBM byte counters) and exit")
@@ -289,6 +290,43 @@ def main():
                       traffic=measured_traffic("decode", "ssd_step"))
         print(f"[bench] ssd_step: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ---- packed variable-length batch: the same layer shape and token count, mixed sequence lengths
+    varlen = None
+    if not args.no_varlen and args.workload == "l2p7b":
+        from mamba_ssd_sequence_chunked_amd.inputs import make_varlen_inputs
+        vi = make_varlen_inputs("varlen2p7b")
+        vT = vi.x.shape[0]
+        vx, vdt, vB, vC = t(vi.x), t(vi.dt), t(vi.B), t(vi.C)
+        vcu = torch.from_numpy(vi.cu_seqlens.astype(np.int32)).to(dev)
+        nseq = len(vi.cu_seqlens) - 1
+        vy = torch.empty_like(vx)
+        vfin = torch.empty((nseq, H, P, N), dtype=torch.float32, device=dev)
+        vws_bytes = lib.ssd_forward_varlen_workspace_bytes(vT, H, P, N, Q, code)
+        vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev)
+
+        def varlen_call():
+            rc = lib.ssd_forward_varlen(p(vx), p(vdt), p(A), p(vB), p(vC), p(D), p(vcu), nseq, p(vy), p(vfin), vT, H,
+                                        P, N, G, Q, code, p(vws), vws_bytes, sp)
+            if rc:
+                raise ssd.SSDError("ssd_forward_varlen", rc)
+
+        for _ in range(20):
+            varlen_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            varlen_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        lens = np.diff(vi.cu_seqlens)
+        varlen = dict(workload=f"varlen2p7b: {vT} packed tokens in {nseq} sequences (lengths {int(lens.min())}-"
+                               f"{int(lens.max())}), 80 heads x 64, dstate 128, chunk 256, bf16",
+                      us_per_call=round(us, 1), tokens_per_s=round(vT / (us / 1e6), 1))
+        print(f"[bench] varlen forward: {us:.1f} us/call", file=sys.stderr, flush=True)
+        del vx, vdt, vB, vC, vy, vws
+
     # ---- the Mamba-1 selective scan at the same layer width (for the SSD-vs-scan comparison)
     scan = None
     if not args.no_scan:
@@ -362,6 +400,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "ssd_step": decode,
+        "varlen": varlen,
         "selective_scan": scan,
         "cpu_baseline": cpu,
     }

@@ -121,7 +121,33 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
 
-/* Stage 1 (segment decays).  For every chunk c and position l inside it:
+/* Packed variable-length batch: nseq sequences stored back to back on one token axis of
+ * total_tokens tokens, sequence k being tokens cu_seqlens[k] .. cu_seqlens[k+1]-1 (the padding-free
+ * variable-length batches of the ql.gl page, section "Mamba-2 Changes More Than the Algorithm").
+ * Every sequence starts from a zero state: the recurrence is reset at each sequence start, so y
+ * equals running ssd_forward on every sequence alone.  Chunks of chunk_size tokens are laid over the
+ * packed axis (a chunk may hold parts of several sequences).
+ *   x T (total_tokens, nheads, headdim); dt float (total_tokens, nheads); A, D float (nheads)
+ *   B, C T (total_tokens, ngroups, dstate)
+ *   cu_seqlens int32 (nseq + 1), DEVICE memory, non-decreasing from 0 to total_tokens (empty
+ *     sequences allowed).  Its content is not checked on the host; other content yields
+ *     unspecified values but no access outside the buffers.
+ *   y T (total_tokens, nheads, headdim), written
+ *   final_states float (nseq, nheads, headdim, dstate), written: each sequence's state after its
+ *     last token (zeros for an empty sequence)
+ *   workspace of at least ssd_forward_varlen_workspace_bytes() bytes:
+ *     dA_cs, dt_chunked float (nheads, nc, chunk_size); chunk states float (nc, nheads, headdim,
+ *     dstate); entry states T (same shape); int32 per-token sequence starts (total_tokens) and
+ *     int32 x 4 per-chunk boundary records (nc)
+ * Limits as for ssd_forward with batch 1; 0 <= nseq <= 2^24 (nseq 0 only with no tokens). */
+size_t ssd_forward_varlen_workspace_bytes(int64_t total_tokens, int64_t nheads, int64_t headdim, int64_t dstate,
+                                          int64_t chunk_size, int dtype);
+int ssd_forward_varlen(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                       const int32_t* cu_seqlens, int64_t nseq, void* y, float* final_states, int64_t total_tokens,
+                       int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Stage 1 (segment decays)./* Stage 1 (segment decays).  For every chunk c and position l inside it:
  *   dA_cs[b,h,c,l]      = sum_{j = cQ .. cQ+l} dt[b,j,h] * A[h]
  *   dt_chunked[b,h,c,l] = dt[b, cQ+l, h]
  * so that exp(dA_cs[l] - dA_cs[s]) is the decay product prod_{j=s+1..l} a_j

@@ -66,7 +66,7 @@ constexpr int kMaxQ = 256;
 constexpr int kWaves = 4;                      // one row-block pair per wavefront
 constexpr int kThreads = 64 * kWaves;
 
-template <typename T, int P, int NK, int HB, int STG, int SW>
+template <typename T, int P, int NK, int HB, int STG, int SW, bool V = false>
 struct ScanCfg {
     static constexpr int kHeads = HB;
     static constexpr int kStages = STG;                            // depth of the source-token ring
@@ -84,7 +84,8 @@ struct ScanCfg {
     static constexpr int ring_bytes = STG * stage_bytes;
     static constexpr int main_bytes = ring_bytes + HB * sh_bytes;
     static constexpr int region = main_bytes;
-    static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ;           // cs, dt, per-token decay factor
+    static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ + (V ? 4 * kMaxQ : 0);   // cs, dt, per-token decay factor
+                                                                                // (+ sequence starts)
     static constexpr int total = tab_bytes + region;
     static constexpr bool pair_fits = total <= 80 * 1024;           // two workgroups per CU
     static constexpr bool fits = total <= 160 * 1024;
@@ -103,29 +104,35 @@ struct ScanCfg {
 // and a single head takes a CU alone when it must.
 template <class C> struct TypeBox { using type = C; };
 
-template <typename T, int P, int NK, int HB>
+template <typename T, int P, int NK, int HB, bool V>
 constexpr auto pick_shape() {
-    using C = ScanCfg<T, P, NK, HB, 2, 32>;
+    using C = ScanCfg<T, P, NK, HB, 2, 32, V>;
     if constexpr (C::pair_fits || (HB == 1 && C::fits)) return TypeBox<C>{};
-    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2>();
+    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2, V>();
     else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
 }
 
-template <typename T, int P, int NK>
+template <typename T, int P, int NK, bool V = false>
 using ScanShape = typename decltype(pick_shape<T, P, NK,
-    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P)>())::type;
+    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), V>())::type;
 
-template <typename T, int P, int NK, class S>
+// kVarlen: a packed variable-length batch (batch 1; tstart from varlen_meta.hip).  A pair (l, s)
+// of one chunk is kept only when s >= tstart[l] (same sequence); since sequences are contiguous,
+// for a stage ending at token e wholly before row l this factors into [tstart[l] <= e] per row
+// times [s >= tstart[e]] per token, which fold into the row decay and the token table; the state
+// entering the chunk reaches only the rows of the sequence holding the chunk's first token.
+template <typename T, int P, int NK, class S, bool kVarlen>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
-    const T* __restrict__ entry, const float* __restrict__ Dv, T* __restrict__ y, int seqlen,
-    int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
+    const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, T* __restrict__ y,
+    int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
     __shared__ float cst[HB * kMaxQ];
     __shared__ float dtt[HB * kMaxQ];
     __shared__ float vst[HB * kMaxQ];          // exp(cs[e(s)] - cs[s]) dt[s], e(s) = last token of s's stage
+    __shared__ int lst[kVarlen ? kMaxQ : 1];   // first token of each token's sequence, chunk-relative
     __shared__ __attribute__((aligned(1024))) unsigned char region[S::region];
     unsigned char* const ring = region;
     unsigned char* const stile = region + S::ring_bytes;
@@ -191,6 +198,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         cst[i] = select(ok, cv, 0.f);
         dtt[i] = select(ok, dv, 0.f);
     }
+    if constexpr (kVarlen) {
+        for (int l = tid; l < kMaxQ; l += kThreads) lst[l] = tstart[t0 + min(l, len - 1)] - (int)t0;
+    }
     // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots)
     Vec8<T> cf[2][S::NP / 32];
 #pragma unroll
@@ -206,7 +216,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     for (int i = tid; i < HB * kMaxQ; i += kThreads) {
         const int hh = i / kMaxQ, sidx = i % kMaxQ;
         const int e = min(kSB * (sidx / kSB) + kSB - 1, kMaxQ - 1);
-        vst[i] = __expf(cst[hh * kMaxQ + e] - cst[i]) * dtt[i];
+        const float v = __expf(cst[hh * kMaxQ + e] - cst[i]) * dtt[i];
+        if constexpr (kVarlen) vst[i] = select(sidx >= lst[e], v, 0.f);
+        else vst[i] = v;
     }
     wait_vmem();                   // S_in tiles, the first stages, the tables' and C's loads
     __syncthreads();
@@ -248,9 +260,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     for (int j = 0; j < 2; ++j) {
         if (!has[j]) continue;
         const int l = min(16 * rbk[j] + r16, kMaxQ - 1);
+        // (packed batches: only rows whose sequence holds the chunk's first token see the entering state)
+        const bool carried = !kVarlen || lst[l] <= 0;
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
-            const float e = __expf(cst[hh * kMaxQ + l]);
+            const float e = select(carried, __expf(cst[hh * kMaxQ + l]), 0.f);
 #pragma unroll
             for (int pt = 0; pt < P / 16; ++pt)
 #pragma unroll
@@ -288,9 +302,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             }
             if (s0 + kSB <= lb) {
                 // the stage lies wholly before the block: G = C.B * exp(cs[l] - cs[e]) * vst[s]
+                const bool rin = !kVarlen || lst[min(lrow, kMaxQ - 1)] <= s0 + kSB - 1;
 #pragma unroll
                 for (int hh = 0; hh < HB; ++hh) {
-                    const float u = __expf(cst[hh * kMaxQ + lrow] - cst[hh * kMaxQ + s0 + kSB - 1]);
+                    const float u = select(rin, __expf(cst[hh * kMaxQ + lrow] - cst[hh * kMaxQ + s0 + kSB - 1]), 0.f);
                     const float* vr = vst + hh * kMaxQ + s0 + 4 * grp;
                     const float4 va = *reinterpret_cast<const float4*>(vr);
                     const float4 vb = *reinterpret_cast<const float4*>(vr + 16);
@@ -313,7 +328,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 for (int hh = 0; hh < HB; ++hh) {
                     const float* csr = cst + hh * kMaxQ;
                     const float* dtr = dtt + hh * kMaxQ;
-                    const float cl = csr[lrow];
+                        const float cl = csr[lrow];
+                    const int rst = kVarlen ? lst[min(lrow, kMaxQ - 1)] : 0;   // first token of the row's sequence
                     Vec8<T> gf;                                   // G[lrow][s], s = s0 + 16 st2 + 4 grp + i
 #pragma unroll
                     for (int st2 = 0; st2 < 2; ++st2) {
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float v = gt[st2][i] * (__expf(cl - cv[i]) * dv[i]);
-                            gf.set(4 * st2 + i, select(sb4 + i <= lrow, v, 0.f));
+                            gf.set(4 * st2 + i, select(sb4 + i <= lrow && (!kVarlen || sb4 + i >= rst), v, 0.f));
                         }
                     }
                     const unsigned char* xt = stg + hh * S::xh_bytes;
@@ -373,11 +389,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 }
 
-template <typename T, int P, int NK>
+template <typename T, int P, int NK, bool V>
 hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
-                  const float* D, T* y, const Dims& d, hipStream_t stream)
+                  const float* D, const int* tstart, T* y, const Dims& d, hipStream_t stream)
 {
-    using S = ScanShape<T, P, NK>;
+    using S = ScanShape<T, P, NK, V>;
     static_assert(S::fits, "LDS budget");
     constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
@@ -388,21 +404,25 @@ hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const fl
     const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, S>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       x, B, C, dtc, cs, entry, D, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
+    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+                       x, B, C, dtc, cs, entry, D, tstart, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, int P>
-hipError_t launch_p(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
-                    const float* D, T* y, const Dims& d, hipStream_t stream)
+template <typename T, bool V>
+hipError_t launch_any(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
+                      const float* D, const int* tstart, T* y, const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
-    if (nk <= 1) return launch<T, P, 1>(x, B, C, dtc, cs, entry, D, y, d, stream);
-    if (nk <= 2) return launch<T, P, 2>(x, B, C, dtc, cs, entry, D, y, d, stream);
-    if (nk <= 4) return launch<T, P, 4>(x, B, C, dtc, cs, entry, D, y, d, stream);
-    return launch<T, P, 8>(x, B, C, dtc, cs, entry, D, y, d, stream);
+    const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
+#define SSD_SCAN_CASE(PP, KK) \
+    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+#define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
+    SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
+#undef SSD_SCAN_P
+#undef SSD_SCAN_CASE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -412,13 +432,15 @@ hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt
                              const float* dA_cs, const T* entry_states, const float* D, T* y,
                              const Dims& d, hipStream_t stream)
 {
-    switch (d.headdim) {
-    case 16: return launch_p<T, 16>(x, B, C, dt_chunked, dA_cs, entry_states, D, y, d, stream);
-    case 32: return launch_p<T, 32>(x, B, C, dt_chunked, dA_cs, entry_states, D, y, d, stream);
-    case 64: return launch_p<T, 64>(x, B, C, dt_chunked, dA_cs, entry_states, D, y, d, stream);
-    case 128: return launch_p<T, 128>(x, B, C, dt_chunked, dA_cs, entry_states, D, y, d, stream);
-    default: return hipErrorInvalidValue;
-    }
+    return launch_any<T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+}
+
+template <typename T>
+hipError_t launch_chunk_scan_varlen(const T* x, const T* B, const T* C, const float* dt_chunked,
+                                    const float* dA_cs, const T* entry_states, const float* D, const int* tstart,
+                                    T* y, const Dims& d, hipStream_t stream)
+{
+    return launch_any<T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
 }
 
 template hipError_t launch_chunk_scan<float>(const float*, const float*, const float*, const float*,
@@ -427,5 +449,11 @@ template hipError_t launch_chunk_scan<float>(const float*, const float*, const f
 template hipError_t launch_chunk_scan<bf16>(const bf16*, const bf16*, const bf16*, const float*,
                                             const float*, const bf16*, const float*, bf16*,
                                             const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_varlen<float>(const float*, const float*, const float*, const float*,
+                                                    const float*, const float*, const float*, const int*, float*,
+                                                    const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_varlen<bf16>(const bf16*, const bf16*, const bf16*, const float*,
+                                                   const float*, const bf16*, const float*, const int*, bf16*,
+                                                   const Dims&, hipStream_t);
 
 }  // namespace ssd

@@ -77,29 +77,72 @@ constexpr int pick_heads() {
 // and A, forms the in-chunk prefix sums of dt A with the same arithmetic as dA_cumsum.hip (4
 // tokens per lane summed in order, then a DPP wavefront prefix sum) and writes dA_cs and
 // dt_chunked for the later stages -- so the chunked forward needs no separate stage-1 launch.
-template <typename T, int P, int NK, int HB, bool kOwnCumsum>
+// kVarlen (requires kOwnCumsum): a packed variable-length batch (batch 1, sequences given by cu,
+// tstart from varlen_meta.hip).  The first nblocks workgroups are the chunks': their state counts
+// only the tokens of the sequence holding the chunk's last token (w = 0 before its start).  The
+// nseq * ngroups * nhb workgroups after them compute, per sequence, its own part of its final
+// state: the same contraction over its tokens in the chunk where it ends, decayed to its last
+// token (pe) instead of the chunk's, written to final_states (nseq, H, P, N); stage 3 then adds
+// the decayed entering state when the sequence began in an earlier chunk.  An empty sequence
+// gets zeros.
+struct VarlenArgs {
+    const int* cu;               // (nseq + 1) sequence boundaries
+    const int* tstart;           // (T) first token of each token's sequence
+    float* final_states;         // (nseq, H, P, N)
+    int nseq;
+};
+
+template <typename T, int P, int NK, int HB, bool kOwnCumsum, bool kVarlen>
 __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ dt_chunked,
     float* __restrict__ dA_cs, const float* __restrict__ dt, const float* __restrict__ A,
-    float* __restrict__ chunk_states, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb,
-    int hpw, int nblocks)
+    float* __restrict__ chunk_states, VarlenArgs va, int seqlen, int nheads, int ngroups, int N, int Q,
+    int nc, int nhb, int hpw, int nblocks)
 {
+    static_assert(!kVarlen || kOwnCumsum, "the sequence workgroups form their own prefix sums");
     using S = StateCfg<T, P, NK, HB>;
     constexpr int EPC = S::EPC, NT = S::NT, PT = S::PT;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * S::stage_bytes];
     __shared__ __attribute__((aligned(16))) float wt[HB * kMaxQ];
 
-    int id = xcd_logical_block(blockIdx.x, nblocks);
+    const bool seqwg = kVarlen && (int)blockIdx.x >= nblocks;      // a sequence's final-state workgroup
+    int id = seqwg ? (int)blockIdx.x - nblocks : xcd_logical_block(blockIdx.x, nblocks);
     const int hb = id % nhb; id /= nhb;
     const int g = id % ngroups; id /= ngroups;
-    const int c = id % nc;
-    const int64_t b = id / nc;
+    int c;
+    int64_t b;
+    int lo = 0, pe = 0, kseq = 0;                                   // token range [lo, pe] of the chunk that counts
+    if (seqwg) {
+        kseq = id;
+        b = 0;
+        const int s0 = min(max(va.cu[kseq], 0), seqlen);
+        const int s1 = min(max(va.cu[kseq + 1], s0), seqlen);
+        if (s1 == s0) {
+            // an empty sequence: zero final state for this workgroup's heads
+            const int hpg0 = nheads / ngroups;
+            const int h00 = g * hpg0 + hb * hpw;
+            const int nh0 = min(hpw, hpg0 - hb * hpw);
+            float* f = va.final_states + ((int64_t)kseq * nheads + h00) * P * N;
+            for (int i = threadIdx.x; i < nh0 * P * N; i += kThreads) f[i] = 0.f;
+            return;
+        }
+        c = (s1 - 1) / Q;
+        pe = s1 - 1 - c * Q;
+        lo = max(s0 - c * Q, 0);
+    } else {
+        c = id % nc;
+        b = id / nc;
+    }
     const int hpg = nheads / ngroups;
     const int h0 = g * hpg + hb * hpw;
     const int nh = min(hpw, hpg - hb * hpw);                       // heads of this workgroup (<= HB)
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, (int64_t)seqlen - t0);
-    const int nsb = (len + kSB - 1) / kSB;
+    if (!seqwg) {
+        pe = len - 1;
+        if constexpr (kVarlen) lo = max(va.tstart[t0 + len - 1] - (int)t0, 0);
+    }
+    const int nsb = (pe + kSB) / kSB;                               // stages up to token pe
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
     const int r16 = lane & 15, grp = lane >> 4;
@@ -148,8 +191,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
         const float excl = incl - cs[3];
 #pragma unroll
         for (int j = 0; j < 4; ++j) cs[j] += excl;
-        const float last = __shfl(cs[3], (Q - 1) / 4, kWave);       // cs[Q - 1]
-        if (wave < nh && 4 * lane + 3 < Q) {
+        // cs[pe]: the decay reference (pe = Q - 1 for a whole chunk; cs is flat past the sequence)
+        const int pq = kVarlen ? pe : Q - 1;
+        const float cq = (pq & 3) == 0 ? cs[0] : (pq & 3) == 1 ? cs[1] : (pq & 3) == 2 ? cs[2] : cs[3];
+        const float last = __shfl(cq, pq / 4, kWave);
+        if (!seqwg && wave < nh && 4 * lane + 3 < Q) {
             const int64_t base = (((int64_t)b * nheads + hs) * nc + c) * Q + 4 * lane;
             store4(dA_cs + base, cs[0], cs[1], cs[2], cs[3]);
             store4(dt_chunked + base, v[0], v[1], v[2], v[3]);
@@ -157,7 +203,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int l = 4 * lane + j;
-            wt[wave * kMaxQ + l] = select(l < len && wave < nh, v[j] * __expf(last - cs[j]), 0.f);
+            wt[wave * kMaxQ + l] = select(l >= lo && l <= pe && wave < nh, v[j] * __expf(last - cs[j]), 0.f);
         }
     }
     wait_vmem();                       // the first stages and the tables' loads
@@ -202,7 +248,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     }
 
     if (hh < nh && p0 < P) {
-        float* out = chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + hh) * P) * N;
+        float* out = seqwg ? va.final_states + (((int64_t)kseq * nheads + h0 + hh) * P) * N
+                           : chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + hh) * P) * N;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = n0 + 16 * nt + 4 * grp;
@@ -215,9 +262,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     }
 }
 
-template <typename T, int P, int NK, bool OWN>
+template <typename T, int P, int NK, bool OWN, bool VARLEN>
 hipError_t launch(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
-                  const Dims& d, hipStream_t stream)
+                  const VarlenArgs& va, const Dims& d, hipStream_t stream)
 {
     constexpr int HB = pick_heads<T, P, NK, 8>();
     static_assert(StateCfg<T, P, NK, HB>::fits, "LDS budget");
@@ -226,21 +273,22 @@ hipError_t launch(const T* x, const T* B, float* dtc, float* cs, const float* dt
     const int nhb = (hpg + HB - 1) / HB;
     const int hpw = (hpg + nhb - 1) / nhb;
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
-    if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB, OWN>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       x, B, dtc, cs, dt, A, out, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
-                       (int)d.chunk, nc, nhb, hpw, (int)nblocks);
+    const int64_t nseqwg = VARLEN ? (int64_t)va.nseq * d.ngroups * nhb : 0;
+    if (nblocks + nseqwg == 0) return hipSuccess;
+    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB, OWN, VARLEN>), dim3((unsigned)(nblocks + nseqwg)),
+                       dim3(kThreads), 0, stream, x, B, dtc, cs, dt, A, out, va, (int)d.seqlen, (int)d.nheads,
+                       (int)d.ngroups, (int)d.dstate, (int)d.chunk, nc, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, bool OWN>
+template <typename T, bool OWN, bool VARLEN>
 hipError_t launch_any(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
-                      const Dims& d, hipStream_t stream)
+                      const VarlenArgs& va, const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
 #define SSD_CS_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, OWN>(x, B, dtc, cs, dt, A, out, d, stream);
+    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, OWN, VARLEN>(x, B, dtc, cs, dt, A, out, va, d, stream);
 #define SSD_CS_P(PP) SSD_CS_CASE(PP, 1) SSD_CS_CASE(PP, 2) SSD_CS_CASE(PP, 4) SSD_CS_CASE(PP, 8)
     SSD_CS_P(16) SSD_CS_P(32) SSD_CS_P(64) SSD_CS_P(128)
 #undef SSD_CS_P
@@ -255,15 +303,24 @@ hipError_t launch_chunk_state(const T* x, const T* B, const float* dt_chunked, c
                               float* chunk_states, const Dims& d, hipStream_t stream)
 {
     // stage 2 alone: the prefix sums come from stage 1 and are only read
-    return launch_any<T, false>(x, B, const_cast<float*>(dt_chunked), const_cast<float*>(dA_cs), nullptr, nullptr,
-                                chunk_states, d, stream);
+    return launch_any<T, false, false>(x, B, const_cast<float*>(dt_chunked), const_cast<float*>(dA_cs), nullptr,
+                                       nullptr, chunk_states, VarlenArgs{}, d, stream);
 }
 
 template <typename T>
 hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, const float* A, float* dt_chunked,
                                      float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, true>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, d, stream);
+    return launch_any<T, true, false>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, VarlenArgs{}, d, stream);
+}
+
+template <typename T>
+hipError_t launch_chunk_state_varlen(const T* x, const T* B, const float* dt, const float* A, const int* cu,
+                                     int64_t nseq, const int* tstart, float* dt_chunked, float* dA_cs,
+                                     float* chunk_states, float* final_states, const Dims& d, hipStream_t stream)
+{
+    const VarlenArgs va{cu, tstart, final_states, (int)nseq};
+    return launch_any<T, true, true>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, va, d, stream);
 }
 
 template hipError_t launch_chunk_state<float>(const float*, const float*, const float*, const float*,
@@ -274,5 +331,11 @@ template hipError_t launch_chunk_state_cumsum<float>(const float*, const float*,
                                                      float*, float*, float*, const Dims&, hipStream_t);
 template hipError_t launch_chunk_state_cumsum<bf16>(const bf16*, const bf16*, const float*, const float*,
                                                     float*, float*, float*, const Dims&, hipStream_t);
+template hipError_t launch_chunk_state_varlen<float>(const float*, const float*, const float*, const float*,
+                                                    const int*, int64_t, const int*, float*, float*, float*,
+                                                    float*, const Dims&, hipStream_t);
+template hipError_t launch_chunk_state_varlen<bf16>(const bf16*, const bf16*, const float*, const float*,
+                                                   const int*, int64_t, const int*, float*, float*, float*,
+                                                   float*, const Dims&, hipStream_t);
 
 }  // namespace ssd

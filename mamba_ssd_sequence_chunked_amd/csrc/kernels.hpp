@@ -23,6 +23,24 @@ template <typename T>
 hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, const float* A, float* dt_chunked,
                                      float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream);
 
+// packed variable-length batches (d.batch == 1, d.seqlen = total tokens)
+hipError_t launch_varlen_meta(const int* cu_seqlens, int64_t nseq, int64_t total, int64_t chunk, int* tstart,
+                              int* cmeta, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_chunk_state_varlen(const T* x, const T* B, const float* dt, const float* A, const int* cu,
+                                     int64_t nseq, const int* tstart, float* dt_chunked, float* dA_cs,
+                                     float* chunk_states, float* final_states, const Dims& d, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_state_passing_varlen(const float* chunk_states, const float* dA_cs, const int* cmeta,
+                                       T* entry_states, float* final_states, const Dims& d, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_chunk_scan_varlen(const T* x, const T* B, const T* C, const float* dt_chunked,
+                                    const float* dA_cs, const T* entry_states, const float* D, const int* tstart,
+                                    T* y, const Dims& d, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, const float* init,
                                 T* entry_states, float* final_states, const Dims& d,

@@ -95,6 +95,27 @@ Workspace layout(const Dims& d, int dtype)
     return w;
 }
 
+struct VarlenWorkspace {
+    size_t cs, dtc, states, entry, tstart, cmeta, total;
+};
+
+VarlenWorkspace layout_varlen(const Dims& d, int dtype)
+{
+    VarlenWorkspace w;
+    const int64_t nc = d.nchunks();
+    const int64_t ncs = d.nheads * nc * d.chunk * 4;
+    const int64_t nst = nc * d.nheads * d.headdim * d.dstate;
+    w.cs = 0;
+    w.dtc = align_up(ncs);
+    w.states = w.dtc + align_up(ncs);
+    w.entry = w.states + align_up(nst * 4);
+    w.tstart = w.entry + align_up(nst * (int64_t)elem_size(dtype));
+    w.cmeta = w.tstart + align_up(d.seqlen * 4);
+    w.total = w.cmeta + align_up(nc * 16);
+    if (w.total < (size_t)kAlign) w.total = kAlign;
+    return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -116,7 +137,7 @@ const char* ssd_status_string(int status)
     }
 }
 
-int ssd_abi_version(void) { return 101; }
+int ssd_abi_version(void) { return 102; }
 
 int64_t ssd_num_chunks(int64_t seqlen, int64_t chunk_size)
 {
@@ -288,6 +309,75 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
         if (e == hipSuccess)
             e = ssd::launch_chunk_scan<float>((const float*)x, (const float*)B, (const float*)C, dtc, cs,
                                               (const float*)entry, D, (float*)y, d, s);
+    }
+    return hip_status(e);
+}
+
+size_t ssd_forward_varlen_workspace_bytes(int64_t total_tokens, int64_t nheads, int64_t headdim, int64_t dstate,
+                                          int64_t chunk_size, int dtype)
+{
+    if (!valid_dtype(dtype)) return 0;
+    Dims d{1, total_tokens, nheads, headdim, dstate, 1, chunk_size};
+    if (check_seq(d) != SSD_OK) return 0;
+    return layout_varlen(d, dtype).total;
+}
+
+int ssd_forward_varlen(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                       const int32_t* cu_seqlens, int64_t nseq, void* y, float* final_states, int64_t total_tokens,
+                       int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype,
+                       void* workspace, size_t workspace_bytes, void* stream)
+{
+    Dims d{1, total_tokens, nheads, headdim, dstate, ngroups, chunk_size};
+    if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
+    int rc = check_seq(d);
+    if (rc != SSD_OK) return rc;
+    if (nseq < 0 || nseq > (int64_t(1) << 24) || (nseq == 0 && total_tokens > 0)) return SSD_ERR_SHAPE;
+    if (nseq == 0) return SSD_OK;
+    if (!cu_seqlens || !A || !final_states) return SSD_ERR_NULL;
+    if (total_tokens > 0 && (!x || !dt || !B || !C || !D || !y)) return SSD_ERR_NULL;
+    const VarlenWorkspace w = layout_varlen(d, dtype);
+    if (workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL;
+    if (!aligned16(workspace) || !aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) ||
+        !aligned16(final_states))
+        return SSD_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)(total_tokens * nheads * headdim) * es;
+    const size_t nb = (size_t)(total_tokens * ngroups * dstate) * es;
+    const size_t nfin = (size_t)(nseq * nheads * headdim * dstate) * 4;
+    const size_t ndt = (size_t)(total_tokens * nheads) * 4;
+    if (any_overlap({{y, nx}, {final_states, nfin}, {workspace, w.total}},
+                    {{x, nx}, {dt, ndt}, {A, (size_t)nheads * 4}, {B, nb}, {C, nb}, {D, (size_t)nheads * 4},
+                     {cu_seqlens, (size_t)(nseq + 1) * 4}}))
+        return SSD_ERR_ALIAS;
+
+    hipStream_t s = (hipStream_t)stream;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* cs = reinterpret_cast<float*>(ws + w.cs);
+    float* dtc = reinterpret_cast<float*>(ws + w.dtc);
+    float* states = reinterpret_cast<float*>(ws + w.states);
+    void* entry = ws + w.entry;
+    int* tstart = reinterpret_cast<int*>(ws + w.tstart);
+    int* cmeta = reinterpret_cast<int*>(ws + w.cmeta);
+    hipError_t e = ssd::launch_varlen_meta(cu_seqlens, nseq, total_tokens, chunk_size, tstart, cmeta, s);
+    if (dtype == SSD_BF16) {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state_varlen<bf16>((const bf16*)x, (const bf16*)B, dt, A, cu_seqlens, nseq, tstart,
+                                                     dtc, cs, states, final_states, d, s);
+        if (e == hipSuccess)
+            e = ssd::launch_state_passing_varlen<bf16>(states, cs, cmeta, (bf16*)entry, final_states, d, s);
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_scan_varlen<bf16>((const bf16*)x, (const bf16*)B, (const bf16*)C, dtc, cs,
+                                                    (const bf16*)entry, D, tstart, (bf16*)y, d, s);
+    } else {
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_state_varlen<float>((const float*)x, (const float*)B, dt, A, cu_seqlens, nseq,
+                                                      tstart, dtc, cs, states, final_states, d, s);
+        if (e == hipSuccess)
+            e = ssd::launch_state_passing_varlen<float>(states, cs, cmeta, (float*)entry, final_states, d, s);
+        if (e == hipSuccess)
+            e = ssd::launch_chunk_scan_varlen<float>((const float*)x, (const float*)B, (const float*)C, dtc, cs,
+                                                     (const float*)entry, D, tstart, (float*)y, d, s);
     }
     return hip_status(e);
 }

@@ -27,11 +27,18 @@ namespace {
 
 constexpr int kElemsPerBlock = 1024;
 
-template <typename T>
+// Packed variable-length batches (batch 1; cmeta from varlen_meta.hip, per chunk {cont, whole,
+// kend, pe}): the state entering chunk c is the running state only when the chunk's first token
+// continues a sequence (else zero, a reset); the running state after the chunk is the chunk's
+// own state (masked to its last sequence) plus the decayed entering state only when no sequence
+// starts inside it; and the sequence that continues into the chunk and ends there at position pe
+// gets exp(cs[pe]) times the entering state added to its final state, which stage 2 has set to
+// the sequence's own part.  final_states is (nseq, H, P, N) and no initial state is taken.
+template <typename T, bool kVarlen>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float* __restrict__ chunk_states, const float* __restrict__ dA_cs,
     const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_states,
-    int nheads, int PN, int Q, int nc)
+    const int4* __restrict__ cmeta, int nheads, int PN, int Q, int nc)
 {
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
@@ -45,6 +52,29 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
     const float* src = chunk_states + (b * nc * nheads + h) * (int64_t)PN + e;
     T* dst = entry + (b * nc * nheads + h) * (int64_t)PN + e;
 
+    if constexpr (kVarlen) {
+        const float* csc = dA_cs + bh * (int64_t)nc * Q;
+#pragma unroll 4
+        for (int c = 0; c < nc; ++c) {
+            const float4 sc = *reinterpret_cast<const float4*>(src + c * stride);
+            const int4 m = cmeta[c];
+            if (!m.x) s = make_float4(0.f, 0.f, 0.f, 0.f);            // a sequence starts at the chunk
+            store4(dst + c * stride, s.x, s.y, s.z, s.w);
+            if (m.z >= 0) {
+                // the continued sequence ends in this chunk at position m.w
+                float4* f = reinterpret_cast<float4*>(final_states + ((int64_t)m.z * nheads + h) * PN + e);
+                const float de = __expf(csc[(int64_t)c * Q + min(max(m.w, 0), Q - 1)]);
+                const float4 fv = *f;
+                *f = make_float4(fmaf(de, s.x, fv.x), fmaf(de, s.y, fv.y), fmaf(de, s.z, fv.z), fmaf(de, s.w, fv.w));
+            }
+            const float dec = m.y ? __expf(cs[(int64_t)c * Q]) : 0.f;   // no start inside: carry on
+            s.x = fmaf(dec, s.x, sc.x);
+            s.y = fmaf(dec, s.y, sc.y);
+            s.z = fmaf(dec, s.z, sc.z);
+            s.w = fmaf(dec, s.w, sc.w);
+        }
+        return;
+    }
 #pragma unroll 4
     for (int c = 0; c < nc; ++c) {
         const float4 sc = *reinterpret_cast<const float4*>(src + c * stride);
@@ -69,8 +99,21 @@ hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, c
     const int PN = (int)(d.headdim * d.dstate);
     dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads,
               (unsigned)d.batch);
-    hipLaunchKernelGGL((state_passing_kernel<T>), grid, dim3(256), 0, stream, chunk_states, dA_cs, init,
-                       entry_states, final_states, (int)d.nheads, PN, (int)d.chunk, (int)d.nchunks());
+    hipLaunchKernelGGL((state_passing_kernel<T, false>), grid, dim3(256), 0, stream, chunk_states, dA_cs, init,
+                       entry_states, final_states, nullptr, (int)d.nheads, PN, (int)d.chunk, (int)d.nchunks());
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_state_passing_varlen(const float* chunk_states, const float* dA_cs, const int* cmeta,
+                                       T* entry_states, float* final_states, const Dims& d, hipStream_t stream)
+{
+    if (d.seqlen == 0) return hipSuccess;
+    const int PN = (int)(d.headdim * d.dstate);
+    dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads, 1u);
+    hipLaunchKernelGGL((state_passing_kernel<T, true>), grid, dim3(256), 0, stream, chunk_states, dA_cs, nullptr,
+                       entry_states, final_states, reinterpret_cast<const int4*>(cmeta), (int)d.nheads, PN,
+                       (int)d.chunk, (int)d.nchunks());
     return hipGetLastError();
 }
 
@@ -78,5 +121,9 @@ template hipError_t launch_state_passing<float>(const float*, const float*, cons
                                                 float*, const Dims&, hipStream_t);
 template hipError_t launch_state_passing<bf16>(const float*, const float*, const float*, bf16*,
                                                float*, const Dims&, hipStream_t);
+template hipError_t launch_state_passing_varlen<float>(const float*, const float*, const int*, float*, float*,
+                                                       const Dims&, hipStream_t);
+template hipError_t launch_state_passing_varlen<bf16>(const float*, const float*, const int*, bf16*, float*,
+                                                      const Dims&, hipStream_t);
 
 }  // namespace ssd

@@ -61,6 +61,10 @@ def load_library():
     lib.ssd_chunk_scan.argtypes = [vp] * 8 + [i64] * 7 + [i32, vp]
     lib.ssd_step.restype = i32
     lib.ssd_step.argtypes = [vp] * 8 + [i64] * 5 + [i32, vp]
+    lib.ssd_forward_varlen_workspace_bytes.restype = sz
+    lib.ssd_forward_varlen_workspace_bytes.argtypes = [i64] * 5 + [i32]
+    lib.ssd_forward_varlen.restype = i32
+    lib.ssd_forward_varlen.argtypes = [vp] * 7 + [i64] + [vp] * 2 + [i64] * 6 + [i32, vp, sz, vp]
     lib.ssd_selective_scan.restype = i32
     lib.ssd_selective_scan.argtypes = [vp] * 9 + [i64] * 4 + [i32, vp]
     _lib = lib
@@ -181,6 +185,43 @@ def step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor
                       G, code, _stream(dev))
     _check("ssd_step", rc)
     return y
+
+
+def forward_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                   D: torch.Tensor, cu_seqlens: torch.Tensor, chunk_size: int) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Packed variable-length batch; see ssd_forward_varlen.
+
+    x (T, nheads, headdim); dt (T, nheads) fp32; A, D (nheads,) fp32; B, C (T, ngroups, dstate) in
+    x's dtype; cu_seqlens int32 (nseq + 1,) on the same device.  Every sequence starts from a zero
+    state.  Returns (y (T, nheads, headdim) in x's dtype, final_states (nseq, nheads, headdim, dstate))."""
+    lib = load_library()
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be (T, nheads, headdim) and B, C (T, ngroups, dstate)")
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dev = x.device
+    code = _dtype_code(x)
+    _need(x, "x", (T, H, P), x.dtype, dev)
+    _need(dt, "dt", (T, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (T, G, N), x.dtype, dev)
+    _need(C, "C", (T, G, N), x.dtype, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D tensor of nseq + 1 offsets")
+    _need(cu_seqlens, "cu_seqlens", (cu_seqlens.numel(),), torch.int32, dev)
+    nseq = cu_seqlens.numel() - 1
+    ws_bytes = lib.ssd_forward_varlen_workspace_bytes(T, H, P, N, chunk_size, code)
+    if ws_bytes == 0:
+        raise SSDError("ssd_forward_varlen_workspace_bytes", -2)
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    final = torch.empty((nseq, H, P, N), dtype=torch.float32, device=dev)
+    rc = lib.ssd_forward_varlen(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(cu_seqlens), nseq,
+                                _ptr(y), _ptr(final), T, H, P, N, G, chunk_size, code, _ptr(workspace),
+                                workspace.numel(), _stream(dev))
+    _check("ssd_forward_varlen", rc)
+    return y, final
 
 
 def selective_scan(x: torch.Tensor, delta: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -34,7 +34,8 @@ def test_library_exports_every_declared_function():
     lib = ssd.load_library()
     names = declared_functions()
     assert {"ssd_forward", "ssd_step", "ssd_forward_workspace_bytes", "ssd_status_string", "ssd_dA_cumsum",
-            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_selective_scan"} <= set(names)
+            "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_selective_scan", "ssd_forward_varlen",
+            "ssd_forward_varlen_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in include/ssd.h but not exported"
 
@@ -43,7 +44,7 @@ def test_status_strings():
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS):
         assert ssd.status_string(code).startswith("SSD_")
     assert "unknown" in ssd.status_string(123)
-    assert ssd.load_library().ssd_abi_version() == 101
+    assert ssd.load_library().ssd_abi_version() == 102
 
 
 def test_num_chunks_and_workspace():
@@ -120,6 +121,35 @@ def test_step_rejects():
     assert call(y=fake(2)) == ERR_ALIAS
     assert call(state=P(0x10000004)) == ERR_SHAPE
     assert call(batch=0) == OK                     # nothing to do, nothing enqueued
+
+
+def test_forward_varlen_rejects():
+    lib = ssd.load_library()
+
+    def call(**kw):
+        a = dict(x=fake(1), dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), cu=fake(10), nseq=3, y=fake(7),
+                 final=fake(8), T=300, H=4, P=16, N=16, G=1, Q=64, dtype=0, ws=fake(9), ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.ssd_forward_varlen(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["cu"], a["nseq"], a["y"],
+                                      a["final"], a["T"], a["H"], a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["ws"],
+                                      a["ws_bytes"], None)
+
+    assert call(P=48) == ERR_SHAPE
+    assert call(Q=24) == ERR_SHAPE
+    assert call(nseq=-1) == ERR_SHAPE
+    assert call(nseq=0) == ERR_SHAPE                 # tokens but no sequences
+    assert call(nseq=0, T=0) == OK                   # nothing at all
+    assert call(cu=None) == ERR_NULL
+    assert call(final=None) == ERR_NULL
+    assert call(dtype=5) == ERR_DTYPE
+    assert call(ws_bytes=64) == ERR_WS
+    assert call(y=fake(1)) == ERR_ALIAS
+    assert call(final=P(0x10000000 + 0x1000000 * 10)) == ERR_ALIAS   # final over cu_seqlens
+    ws = lib.ssd_forward_varlen_workspace_bytes(300, 4, 16, 16, 64, 0)
+    nc = 5
+    up = lambda v: (v + 255) // 256 * 256    # noqa: E731
+    assert ws == 2 * up(4 * nc * 64 * 4) + up(nc * 4 * 16 * 16 * 4) * 2 + up(300 * 4) + up(nc * 16)
+    assert lib.ssd_forward_varlen_workspace_bytes(300, 4, 48, 16, 64, 0) == 0
 
 
 def test_selective_scan_rejects():
