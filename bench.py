@@ -30,7 +30,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, published
 KERNELS = ("dA_cumsum", "chunk_state", "state_passing", "chunk_scan")
 KERNEL_SOURCES = {"dA_cumsum": "dA_cumsum.hip", "chunk_state": "chunk_state.hip",
-                  "state_passing": "state_passing.hip", "chunk_scan": "chunk_scan.hip", "ssd_step": "ssd_step.hip"}
+                  "chunk_state_cumsum": "chunk_state.hip", "chunk_state_varlen": "chunk_state.hip",
+                  "state_passing": "state_passing.hip", "state_passing_varlen": "state_passing.hip",
+                  "chunk_scan": "chunk_scan.hip", "chunk_scan_varlen": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
+                  "selective_scan": "selective_scan.hip", "varlen_meta": "varlen_meta.hip"}
 
 
 def parse_args():
@@ -399,6 +402,8 @@ def main():
                    "global_batch": b, "seq_len": L, "parallelism": "single GPU"},
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_note": "the stage entry points timed one by one; inside ssd_forward stage 1 runs in the prologue "
+                        "of the stage-2 kernel, so the forward launches three kernels",
         "ssd_step": decode,
         "varlen": varlen,
         "selective_scan": scan,
