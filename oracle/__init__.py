@@ -6,7 +6,9 @@ calls anything here, and nothing here imports the library.
 
 ``forward`` and ``step`` call the plain C recurrence in ``ssd_oracle.c``
 (token by token, double precision, one independent (b, h, p) row per
-OpenMP task); ``forward_varlen`` runs ``forward`` on each sequence of a
+OpenMP task); ``backward`` is the reverse-mode derivative of that
+recurrence (the adjoint state run backwards over the stored states);
+``forward_varlen`` runs ``forward`` on each sequence of a
 packed batch; ``selective_scan`` calls the Mamba-1 recurrence there (one
 (b, channel) row per task).  The helpers below it are written on top of those two calls
 and plain numpy indexing only:
@@ -61,6 +63,8 @@ def _bind(lib):
                                                                 ctypes.c_int]
     lib.ssd_oracle_step.restype = ctypes.c_int
     lib.ssd_oracle_step.argtypes = [_dp] * 8 + [_i64] * 5 + [ctypes.c_int]
+    lib.ssd_oracle_backward.restype = ctypes.c_int
+    lib.ssd_oracle_backward.argtypes = [_dp] * 16 + [_i64] * 6 + [ctypes.c_int]
     lib.ssd_oracle_selective_scan.restype = ctypes.c_int
     lib.ssd_oracle_selective_scan.argtypes = [_dp] * 9 + [_i64] * 4 + [ctypes.c_int]
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
@@ -139,6 +143,27 @@ def step(state, x, dt, A, B, C, D, nthreads: int = 0, lib=None):
     if rc != 0:
         raise ValueError("ssd_oracle_step rejected its arguments")
     return y, st
+
+
+def backward(x, dt, A, B, C, D, init, dy, dfinal=None, nthreads: int = 0, lib=None):
+    """Gradients of the forward for dL/dy = dy and dL/dfinal = dfinal (None = 0).
+
+    Shapes as in ``forward`` (dy like x, dfinal like init).  Returns a dict with dx, ddt, dA, dB,
+    dC, dD and dinit (dinit is returned even when init is None: the gradient w.r.t. a zero
+    initial state)."""
+    x, dt, A, B, C, D, init, dy, dfinal = (_f64(a) for a in (x, dt, A, B, C, D, init, dy, dfinal))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    assert dy.shape == x.shape and (dfinal is None or dfinal.shape == (b, H, P, N))
+    out = dict(dx=np.empty((b, L, H, P)), ddt=np.empty((b, L, H)), dA=np.empty(H), dB=np.empty((b, L, G, N)),
+               dC=np.empty((b, L, G, N)), dD=np.empty(H), dinit=np.empty((b, H, P, N)))
+    rc = (lib or _load()).ssd_oracle_backward(
+        _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(dy), _ptr(dfinal),
+        _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
+        _ptr(out["dinit"]), b, L, H, P, N, G, int(nthreads))
+    if rc != 0:
+        raise ValueError("ssd_oracle_backward rejected its arguments")
+    return out
 
 
 def forward_varlen(x, dt, A, B, C, D, cu_seqlens, nthreads: int = 0, lib=None):

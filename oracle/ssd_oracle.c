@@ -141,6 +141,127 @@ int ssd_oracle_step(double* state, const double* x, const double* dt, const doub
     return 0;
 }
 
+/* Gradients of the forward (the training pass the pages' throughput claims are about:
+ * "Transformers are SSMs" paper card, "How It Works" and "Key Takeaways").  For a loss L with
+ * dL/dy = dy and dL/d(final state) = dfinal (NULL = 0), the reverse-mode derivative of the
+ * recurrence above, written out: with g_t = dL/dh_t,
+ *
+ *   g_{L-1} = dfinal + dy_{L-1} C_{L-1}^T,   g_{t-1} = a_t g_t + dy_{t-1} C_{t-1}^T
+ *   du_t  = g_t B_t                          (u_t = dt_t x_t, the input vector)
+ *   dx_t  = dt_t du_t + D dy_t
+ *   dB_t += g_t^T u_t   (summed over the heads of the group)
+ *   dC_t += h_t^T dy_t  (summed over the heads of the group)
+ *   da_t  = <g_t, h_{t-1}>,  ddt_t = x_t . du_t + A a_t da_t,  dA += dt_t a_t da_t
+ *   dD   += x_t . dy_t,      dinit = a_0 g_0
+ *
+ * Every state h_t of one (b, h) is kept (L x P x N doubles), so this is for test sizes.
+ * Per-head parts of dB and dC are summed over the group at the end. */
+int ssd_oracle_backward(const double* x, const double* dt, const double* A, const double* Bm, const double* Cm,
+                        const double* D, const double* init, const double* dy, const double* dfinal, double* dx,
+                        double* ddt, double* dA, double* dB, double* dC, double* dD, double* dinit, int64_t batch,
+                        int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                        int nthreads)
+{
+    if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
+        nheads % ngroups != 0)
+        return -1;
+    const int64_t hpg = nheads / ngroups, P = headdim, N = dstate, L = seqlen;
+    const int64_t PN = P * N;
+    /* per-head parts of dB, dC: (B, L, H, N) */
+    double* dBh = (double*)calloc((size_t)(batch * L * nheads * N) + 1, sizeof(double));
+    double* dCh = (double*)calloc((size_t)(batch * L * nheads * N) + 1, sizeof(double));
+    double* dAbh = (double*)calloc((size_t)(batch * nheads) + 1, sizeof(double));
+    double* dDbh = (double*)calloc((size_t)(batch * nheads) + 1, sizeof(double));
+    if (!dBh || !dCh || !dAbh || !dDbh) { free(dBh); free(dCh); free(dAbh); free(dDbh); return -2; }
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bh = 0; bh < batch * nheads; ++bh) {
+        const int64_t b = bh / nheads, h = bh % nheads, g = h / hpg;
+        double* hs = (double*)malloc(sizeof(double) * (size_t)((L + 1) * PN));   /* hs[t + 1] = h_t, hs[0] = h_{-1} */
+        double* gs = (double*)malloc(sizeof(double) * (size_t)PN);
+        double* du = (double*)malloc(sizeof(double) * (size_t)P);
+        for (int64_t i = 0; i < PN; ++i) hs[i] = init ? init[bh * PN + i] : 0.0;
+        for (int64_t t = 0; t < L; ++t) {
+            const int64_t bt = b * L + t;
+            const double a = exp(dt[bt * nheads + h] * A[h]);
+            for (int64_t p = 0; p < P; ++p) {
+                const double u = dt[bt * nheads + h] * x[(bt * nheads + h) * P + p];
+                for (int64_t n = 0; n < N; ++n)
+                    hs[(t + 1) * PN + p * N + n] = a * hs[t * PN + p * N + n] + u * Bm[(bt * ngroups + g) * N + n];
+            }
+        }
+        for (int64_t i = 0; i < PN; ++i) gs[i] = dfinal ? dfinal[bh * PN + i] : 0.0;
+        double dA_acc = 0.0, dD_acc = 0.0;
+        for (int64_t t = L - 1; t >= 0; --t) {
+            const int64_t bt = b * L + t;
+            const double dtv = dt[bt * nheads + h];
+            const double a = exp(dtv * A[h]);
+            const double* xt = x + (bt * nheads + h) * P;
+            const double* dyt = dy + (bt * nheads + h) * P;
+            const double* Bt = Bm + (bt * ngroups + g) * N;
+            const double* Ct = Cm + (bt * ngroups + g) * N;
+            for (int64_t p = 0; p < P; ++p)
+                for (int64_t n = 0; n < N; ++n) gs[p * N + n] += dyt[p] * Ct[n];
+            double xdu = 0.0, da = 0.0, xdy = 0.0;
+            for (int64_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int64_t n = 0; n < N; ++n) acc += gs[p * N + n] * Bt[n];
+                du[p] = acc;
+                xdu += xt[p] * acc;
+                xdy += xt[p] * dyt[p];
+                dx[(bt * nheads + h) * P + p] = dtv * acc + D[h] * dyt[p];
+            }
+            for (int64_t n = 0; n < N; ++n) {
+                double sb = 0.0, sc = 0.0;
+                for (int64_t p = 0; p < P; ++p) {
+                    sb += gs[p * N + n] * dtv * xt[p];
+                    sc += hs[(t + 1) * PN + p * N + n] * dyt[p];
+                }
+                dBh[(bt * nheads + h) * N + n] = sb;
+                dCh[(bt * nheads + h) * N + n] = sc;
+            }
+            for (int64_t i = 0; i < PN; ++i) da += gs[i] * hs[t * PN + i];
+            ddt[bt * nheads + h] = xdu + A[h] * a * da;
+            dA_acc += dtv * a * da;
+            dD_acc += xdy;
+            for (int64_t i = 0; i < PN; ++i) gs[i] *= a;
+        }
+        if (dinit)
+            for (int64_t i = 0; i < PN; ++i) dinit[bh * PN + i] = gs[i];
+        dAbh[bh] = dA_acc;
+        dDbh[bh] = dD_acc;
+        free(hs);
+        free(gs);
+        free(du);
+    }
+    for (int64_t h = 0; h < nheads; ++h) {
+        double sa = 0.0, sd = 0.0;
+        for (int64_t b = 0; b < batch; ++b) { sa += dAbh[b * nheads + h]; sd += dDbh[b * nheads + h]; }
+        dA[h] = sa;
+        dD[h] = sd;
+    }
+    for (int64_t bt = 0; bt < batch * L; ++bt)
+        for (int64_t g = 0; g < ngroups; ++g)
+            for (int64_t n = 0; n < N; ++n) {
+                double sb = 0.0, sc = 0.0;
+                for (int64_t k = 0; k < hpg; ++k) {
+                    sb += dBh[(bt * nheads + g * hpg + k) * N + n];
+                    sc += dCh[(bt * nheads + g * hpg + k) * N + n];
+                }
+                dB[(bt * ngroups + g) * N + n] = sb;
+                dC[(bt * ngroups + g) * N + n] = sc;
+            }
+    free(dBh);
+    free(dCh);
+    free(dAbh);
+    free(dDbh);
+    return 0;
+}
+
 /* The Mamba-1 selective scan, the layer Mamba-2 replaces (mohakchugh blog,
  * section "Mamba-1: Selective State Spaces"): every channel d of the input
  * has its own diagonal N x N transition, so each of its N state entries

@@ -517,3 +517,61 @@ def pin_varlen_final_states(lib=None):
 
 VARLEN_PINS = [pin_varlen_dense_form, pin_varlen_equal_lengths_batch, pin_varlen_final_states]
 ALL_PINS = ALL_PINS + VARLEN_PINS
+
+
+# ----------------------------------------------------------------------------------------------
+# Gradients (the backward pass).  Pins W1-W2.
+
+def _loss(x, dt, A, Bm, Cm, D, h0, dy, dfin, lib=None):
+    y, fin = oracle.forward(x, dt, A, Bm, Cm, D, h0, lib=None)
+    return float(np.sum(y * dy) + np.sum(fin * dfin))
+
+
+def pin_backward_finite_differences(lib=None):
+    """W1: every gradient equals the central finite difference of L = <y, dy> + <final, dfinal>
+    computed with the forward recurrence (step 1e-6 in fp64), on a problem with groups and an
+    initial state; all coordinates of every input are probed."""
+    rng = np.random.default_rng(41)
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(41, b=2, L=7, H=4, P=2, N=3, G=2, init=True)
+    dy = rng.standard_normal(x.shape)
+    dfin = rng.standard_normal(h0.shape)
+    gr = oracle.backward(x, dt, A, Bm, Cm, D, h0, dy, dfin, lib=lib)
+    args = dict(x=x, dt=dt, A=A, B=Bm, C=Cm, D=D, init=h0)
+    names = dict(x="dx", dt="ddt", A="dA", B="dB", C="dC", D="dD", init="dinit")
+    eps = 1e-6
+    for k, a in args.items():
+        fd = np.zeros_like(a)
+        for i in np.ndindex(a.shape):
+            old = a[i]
+            a[i] = old + eps
+            lp = _loss(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"], args["init"], dy, dfin)
+            a[i] = old - eps
+            lm = _loss(args["x"], args["dt"], args["A"], args["B"], args["C"], args["D"], args["init"], dy, dfin)
+            a[i] = old
+            fd[i] = (lp - lm) / (2 * eps)
+        assert _rel(gr[names[k]], fd) < 1e-6, f"d{k}: {_rel(gr[names[k]], fd)}"
+
+
+def pin_backward_structure(lib=None):
+    """W2: closed forms: dD_h = sum of x . dy over tokens; with C = 0 and no final-state gradient
+    only the skip path remains (dx = D dy, dB = dC's partner terms vanish: dB = 0, ddt = 0, dA = 0);
+    the gradients are linear in (dy, dfinal)."""
+    rng = np.random.default_rng(42)
+    x, dt, A, Bm, Cm, D, h0 = rand_problem(42, b=1, L=9, H=2, P=3, N=4, G=1, init=True)
+    dy = rng.standard_normal(x.shape)
+    dfin = rng.standard_normal(h0.shape)
+    gr = oracle.backward(x, dt, A, Bm, Cm, D, h0, dy, dfin, lib=lib)
+    assert _rel(gr["dD"], np.einsum("blhp,blhp->h", x, dy)) < TOL
+    z = oracle.backward(x, dt, A, Bm, np.zeros_like(Cm), D, h0, dy, None, lib=lib)
+    assert _rel(z["dx"], D[None, None, :, None] * dy) < TOL
+    assert np.max(np.abs(z["dB"])) == 0.0 and np.max(np.abs(z["ddt"])) == 0.0 and np.max(np.abs(z["dA"])) == 0.0
+    g1 = oracle.backward(x, dt, A, Bm, Cm, D, h0, dy, None, lib=lib)
+    g2 = oracle.backward(x, dt, A, Bm, Cm, D, h0, np.zeros_like(dy), dfin, lib=lib)
+    for k in gr:
+        if k == "dD":
+            continue
+        assert _rel(gr[k], g1[k] + g2[k]) < TOL, f"linearity {k}"
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_structure]
+ALL_PINS = ALL_PINS + BACKWARD_PINS

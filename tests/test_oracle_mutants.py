@@ -8,7 +8,7 @@ import subprocess
 import pytest
 
 import oracle
-from oracle_pins import (SCAN_PINS, pin_dense_quadratic_form, pin_groups, pin_hand_example, pin_skip_only,
+from oracle_pins import (BACKWARD_PINS, SCAN_PINS, pin_dense_quadratic_form, pin_groups, pin_hand_example, pin_skip_only,
                          pin_step_matches_forward, pin_zero_input, pin_scalar_closed_forms)
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "ssd_oracle.c")
@@ -47,14 +47,33 @@ SCAN_MUTANTS = {
                                          "const double dl = delta[bt * dim + (d + 1) % dim];")],
 }
 
+# mistakes planted in the backward, caught by the gradient pins
+BACKWARD_MUTANTS = {
+    "bwd_decay_before_dy": [("for (int64_t n = 0; n < N; ++n) gs[p * N + n] += dyt[p] * Ct[n];",
+                             "for (int64_t n = 0; n < N; ++n) gs[p * N + n] = a * gs[p * N + n] + dyt[p] * Ct[n];")],
+    "bwd_ddt_missing_decay_term": [("ddt[bt * nheads + h] = xdu + A[h] * a * da;", "ddt[bt * nheads + h] = xdu;")],
+    "bwd_dB_missing_dt": [("sb += gs[p * N + n] * dtv * xt[p];", "sb += gs[p * N + n] * xt[p];")],
+    "bwd_dC_previous_state": [("sc += hs[(t + 1) * PN + p * N + n] * dyt[p];", "sc += hs[t * PN + p * N + n] * dyt[p];")],
+    "bwd_dx_missing_skip": [("dx[(bt * nheads + h) * P + p] = dtv * acc + D[h] * dyt[p];",
+                             "dx[(bt * nheads + h) * P + p] = dtv * acc;")],
+    "bwd_dA_missing_dt": [("dA_acc += dtv * a * da;", "dA_acc += a * da;")],
+    "bwd_dinit_not_decayed": [("for (int64_t i = 0; i < PN; ++i) gs[i] *= a;",
+                               "if (t > 0) for (int64_t i = 0; i < PN; ++i) gs[i] *= a;")],
+}
+
 PINS = [pin_hand_example, pin_skip_only, pin_zero_input, pin_scalar_closed_forms, pin_groups,
         pin_dense_quadratic_form, pin_step_matches_forward]
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(SCAN_MUTANTS))
+@pytest.mark.parametrize("name", sorted(MUTANTS) + sorted(SCAN_MUTANTS) + sorted(BACKWARD_MUTANTS))
 def test_mutant_is_caught(name, tmp_path):
     src = open(SRC).read()
-    edits, pins = (MUTANTS[name], PINS) if name in MUTANTS else (SCAN_MUTANTS[name], SCAN_PINS)
+    if name in MUTANTS:
+        edits, pins = MUTANTS[name], PINS
+    elif name in SCAN_MUTANTS:
+        edits, pins = SCAN_MUTANTS[name], SCAN_PINS
+    else:
+        edits, pins = BACKWARD_MUTANTS[name], BACKWARD_PINS
     for old, new, *count in edits:
         assert old in src, f"mutation site for {name} not found"
         src = src.replace(old, new, *count)
