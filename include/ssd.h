@@ -121,6 +121,27 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
 
+/* Gradients of ssd_forward (the training pass) for dL/dy = dy and dL/d(final_states) = dfinal
+ * (NULL = 0), by the adjoint of the recurrence: the adjoint state runs backwards in time as an SSD
+ * of its own (dy as input, C in the role of B), computed with the same stage kernels on
+ * time-reversed and role-swapped arrays; the log-decay gradient is the suffix sum over tokens of
+ * dy.(y - D x) - (dt x).(dL/d(dt x)).  Arguments as for ssd_forward, plus
+ *   dy T (batch, seqlen, nheads, headdim); dfinal float (batch, nheads, headdim, dstate) or NULL
+ *   dx T like x; ddt float like dt; dA, dD float (nheads); dB, dC T like B, C;
+ *   dinit float (batch, nheads, headdim, dstate): the gradient of the initial state (written
+ *     also when init_states is NULL)
+ *   workspace of at least ssd_backward_workspace_bytes() bytes
+ * dstate must be one of 16, 32, 64, 128, 256 and nheads * dstate <= 2^20.  With bf16 inputs the
+ * pass widens them to fp32 and computes in fp32 (the decay gradients cancel too much for bf16
+ * operands); dx, dB, dC are rounded to bf16 once. */
+size_t ssd_backward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                                    int64_t ngroups, int64_t chunk_size, int dtype);
+int ssd_backward(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                 const float* init_states, const void* dy, const float* dfinal, void* dx, float* ddt, float* dA,
+                 void* dB, void* dC, float* dD, float* dinit, int64_t batch, int64_t seqlen, int64_t nheads,
+                 int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
 /* Packed variable-length batch: nseq sequences stored back to back on one token axis of
  * total_tokens tokens, sequence k being tokens cu_seqlens[k] .. cu_seqlens[k+1]-1 (the padding-free
  * variable-length batches of the ql.gl page, section "Mamba-2 Changes More Than the Algorithm").

@@ -1,0 +1,549 @@
+// bwd.hip - gradients of the chunked forward (the training pass).
+//
+// For a loss L with dL/dy = dy and dL/d(final state) = dfinal, the adjoint state
+// g_t = dL/dh_t obeys g_{t-1} = a_t g_t + dy_{t-1} C_{t-1}^T: the same kind of linear
+// recurrence as the forward, run backwards in time with dy as its input and C in the role of B.
+// The pass therefore reuses the forward's stage kernels, each fed the arrays that put the wanted
+// quantity in the place of y:
+//
+//   forward recompute    chunk states, entry states S_in (rounded to T), the final state, and
+//                        yhat = y - D x in fp32 (chunk_scan with D = 0)
+//   adjoint chunk states Ghat_c = sum_{s in c} exp(cs[s]) dy_s C_s^T   (chunk_state with w = exp(cs))
+//   adjoint passing      Gout[c] (adjoint at chunk c's last token from later tokens), backwards
+//                        over chunks from dfinal; what is left at the front is dinit = a_0 g_0
+//   du = g B             chunk_scan on the time-reversed sequence: x <- dy, B <- C, C <- B,
+//                        entry <- Gout, no dt scaling, decays cs'[l'] = cs[last] - cs[l]
+//   dB (per head)        time-reversed chunk_scan with x <- C (copied per head), B <- dy, C <- u = dt x,
+//                        entry <- Gout^T; contraction over the head dimension
+//   dC (per head)        chunk_scan with x <- B (copied per head), B <- x (dt scaled), C <- dy,
+//                        entry <- S_in^T
+//   per token            dx = dt du + D dy; with q_t = dy_t . yhat_t - u_t . du_t the gradient of
+//                        the log-decay dt_t A is the suffix sum of q from t plus <dfinal, h_final>
+//                        (the telescoping of <g_t, h_t> over t), so ddt = A dl + x . du,
+//                        dA = sum dt dl, dD = sum x . dy
+//   dB, dC               per-head parts summed over the heads of each group
+//
+// The reversal pads the sequence in front to whole chunks (zero tokens, unit decay), so the
+// reversed chunks line up with the forward's.  Outputs of the chunk_scan passes stay fp32.
+//
+// The gradient of the log-decays is a suffix sum of differences of two nearly equal products per
+// token, and dA sums it over all tokens: rounding the matrix-core operands to bf16 (as the forward
+// does) leaves ddt and dA with errors of several percent up to several hundred percent, against
+// ~1e-5 in fp32.  Inputs in bf16 are therefore widened to fp32 (exactly) and the whole pass runs
+// on the fp32 matrix-core path; dx, dB and dC are rounded to bf16 once at the end.
+#include <algorithm>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kT = 256;
+
+__device__ __forceinline__ int64_t grid_stride() { return (int64_t)gridDim.x * kT; }
+__device__ __forceinline__ int64_t gtid() { return (int64_t)blockIdx.x * kT + threadIdx.x; }
+
+// original token of reversed position tau (padded length nc Q), or -1 for a padding position
+__device__ __forceinline__ int64_t unrev(int64_t tau, int Q, int nc, int64_t L)
+{
+    const int64_t cr = tau / Q, lr = tau % Q;
+    const int64_t t = (nc - 1 - cr) * (int64_t)Q + (Q - 1 - lr);
+    return t < L ? t : -1;
+}
+
+// weight and decay tables of the adjoint chunk states and of the reversed passes
+__global__ __launch_bounds__(kT) void bwd_tables_kernel(const float* __restrict__ cs, float* __restrict__ W,
+                                                        float* __restrict__ Z, float* __restrict__ dtp,
+                                                        float* __restrict__ csp, int64_t nrows, int L, int Q, int nc)
+{
+    for (int64_t i = gtid(); i < nrows * Q; i += grid_stride()) {
+        const int64_t row = i / Q;                  // (b, h, c)
+        const int l = (int)(i % Q);
+        const int c = (int)(row % nc);
+        const int len = min(Q, L - c * Q);
+        W[i] = l < len ? __expf(cs[i]) : 0.f;
+        Z[i] = 0.f;
+        // reversed chunk c' = nc - 1 - c of the same (b, h), position l' = Q - 1 - l
+        const int64_t rrow = row - c + (nc - 1 - c);
+        const int lr = Q - 1 - l;
+        const bool ok = l < len;
+        dtp[rrow * Q + lr] = ok ? 1.f : 0.f;
+        csp[rrow * Q + lr] = ok ? cs[row * Q + len - 1] - cs[i] : 0.f;
+    }
+}
+
+// reversed (front-padded) copies of dy (B, Lp, H, P), B and C (B, Lp, G, N), u = dt x (B, Lp, H, P),
+// C copied per head and reversed, B copied per head, both split into column halves when N > 128:
+// (nsplit, B, Lp|L, H, Nh); eight elements per thread
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, const float* __restrict__ dt,
+                                                      const T* __restrict__ Bm, const T* __restrict__ Cm,
+                                                      const T* __restrict__ dy, T* __restrict__ dy_rev,
+                                                      T* __restrict__ B_rev, T* __restrict__ C_rev,
+                                                      T* __restrict__ u_rev, T* __restrict__ Crep_rev,
+                                                      T* __restrict__ Brep, int batch, int64_t L, int nc, int Q,
+                                                      int H, int P, int N, int G, int nsplit)
+{
+    const int64_t Lp = (int64_t)nc * Q;
+    const int hpg = H / G, Nh = N / nsplit;
+    // 1. per (b, tau, h): dy_rev and u_rev, P / 8 vectors each
+    const int64_t n1 = (int64_t)batch * Lp * H * (P / 8);
+    for (int64_t i = gtid(); i < n1; i += grid_stride()) {
+        const int v = (int)(i % (P / 8));
+        const int64_t r = i / (P / 8);             // (b, tau, h)
+        const int h = (int)(r % H);
+        const int64_t bt = r / H;
+        const int64_t b = bt / Lp, tau = bt % Lp;
+        const int64_t t = unrev(tau, Q, nc, L);
+        Vec8<T> a, u;
+        if (t >= 0) {
+            const int64_t o = ((b * L + t) * H + h) * P + 8 * v;
+            load8(a, dy + o);
+            load8(u, x + o);
+            const float d = dt[(b * L + t) * H + h];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) u.set(k, d * u.get(k));
+        } else {
+            a.zero();
+            u.zero();
+        }
+        store8(dy_rev + r * P + 8 * v, a);
+        store8(u_rev + r * P + 8 * v, u);
+    }
+    // 2. per (b, tau, g): B_rev, C_rev
+    const int64_t n2 = (int64_t)batch * Lp * G * (N / 8);
+    for (int64_t i = gtid(); i < n2; i += grid_stride()) {
+        const int v = (int)(i % (N / 8));
+        const int64_t r = i / (N / 8);             // (b, tau, g)
+        const int g = (int)(r % G);
+        const int64_t bt = r / G;
+        const int64_t b = bt / Lp, tau = bt % Lp;
+        const int64_t t = unrev(tau, Q, nc, L);
+        Vec8<T> vb, vc;
+        if (t >= 0) {
+            const int64_t o = ((b * L + t) * G + g) * N + 8 * v;
+            load8(vb, Bm + o);
+            load8(vc, Cm + o);
+        } else {
+            vb.zero();
+            vc.zero();
+        }
+        store8(B_rev + r * N + 8 * v, vb);
+        store8(C_rev + r * N + 8 * v, vc);
+    }
+    // 3. per (split, b, tau, h): C copied per head, reversed; per (split, b, t, h): B copied per head
+    const int64_t n3 = (int64_t)nsplit * batch * Lp * H * (Nh / 8);
+    for (int64_t i = gtid(); i < n3; i += grid_stride()) {
+        const int v = (int)(i % (Nh / 8));
+        int64_t r = i / (Nh / 8);                  // (k, b, tau, h)
+        const int h = (int)(r % H);
+        r /= H;
+        const int64_t tau = r % Lp;
+        r /= Lp;
+        const int64_t b = r % batch;
+        const int k = (int)(r / batch);
+        const int g = h / hpg;
+        const int64_t t = unrev(tau, Q, nc, L);
+        Vec8<T> vc;
+        if (t >= 0) load8(vc, Cm + ((b * L + t) * G + g) * N + k * Nh + 8 * v);
+        else vc.zero();
+        store8(Crep_rev + (((k * batch + b) * Lp + tau) * H + h) * Nh + 8 * v, vc);
+        if (tau < L) {
+            Vec8<T> vb;
+            load8(vb, Bm + ((b * L + tau) * G + g) * N + k * Nh + 8 * v);
+            store8(Brep + (((k * batch + b) * L + tau) * H + h) * Nh + 8 * v, vb);
+        }
+    }
+}
+
+// S_in^T per chunk and head, split into column halves: (nsplit, B, nc, H, Nh, P) from (B, nc, H, P, N)
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                           int64_t nblk, int P, int N, int nsplit)
+{
+    const int Nh = N / nsplit;
+    const int64_t n = (int64_t)nsplit * nblk * Nh * P;
+    for (int64_t i = gtid(); i < n; i += grid_stride()) {
+        const int p = (int)(i % P);
+        int64_t r = i / P;
+        const int j = (int)(r % Nh);
+        r /= Nh;
+        const int64_t blk = r % nblk;              // (b, c, h)
+        const int k = (int)(r / nblk);
+        dst[i] = src[(blk * P + p) * N + k * Nh + j];
+    }
+}
+
+// backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
+// order as T (P x N) and transposed (split into column halves, N x P); dinit at the end
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
+                                                         const float* __restrict__ dfinal, T* __restrict__ Gout_rev,
+                                                         T* __restrict__ GoutT_rev, float* __restrict__ dinit,
+                                                         int batch, int H, int P, int N, int Q, int nc, int nsplit)
+{
+    const int PN = P * N, Nh = N / nsplit;
+    const int h = blockIdx.y;
+    const int64_t b = blockIdx.z;
+    const int e = blockIdx.x * (4 * kT) + 4 * threadIdx.x;
+    if (e >= PN) return;
+    const int64_t bh = b * H + h;
+    const int p = e / N, n0 = e % N;
+    float4 s = dfinal ? *reinterpret_cast<const float4*>(dfinal + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c = nc - 1; c >= 0; --c) {
+        const int cr = nc - 1 - c;
+        store4(Gout_rev + ((b * nc + cr) * H + h) * (int64_t)PN + e, s.x, s.y, s.z, s.w);
+        const float sv[4] = {s.x, s.y, s.z, s.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = n0 + q, k = n / Nh, j = n % Nh;
+            GoutT_rev[((((int64_t)k * batch + b) * nc + cr) * H + h) * (int64_t)Nh * P + (int64_t)j * P + p] =
+                from_f32<T>(sv[q]);
+        }
+        const float4 gh = *reinterpret_cast<const float4*>(Ghat + ((b * nc + c) * H + h) * (int64_t)PN + e);
+        const float dec = __expf(cs[(bh * nc + c) * Q + Q - 1]);
+        s.x = fmaf(dec, s.x, gh.x);
+        s.y = fmaf(dec, s.y, gh.y);
+        s.z = fmaf(dec, s.z, gh.z);
+        s.w = fmaf(dec, s.w, gh.w);
+    }
+    *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
+}
+
+// per (b, h): dx, ddt, and the per-(b, h) parts of dA and dD.  Threads take tokens from the end
+// (thread i of a block of 256 has token blk*256 + 255 - i), so a prefix sum over threads is the
+// suffix sum over tokens that the log-decay gradient needs.
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_tokens_kernel(const T* __restrict__ x, const float* __restrict__ dt,
+                                                        const float* __restrict__ A, const float* __restrict__ Dv,
+                                                        const T* __restrict__ dy, const float* __restrict__ yhat,
+                                                        const float* __restrict__ du_rev,
+                                                        const float* __restrict__ dfinal,
+                                                        const float* __restrict__ hfinal, T* __restrict__ dx,
+                                                        float* __restrict__ ddt, float* __restrict__ dAp,
+                                                        float* __restrict__ dDp, int64_t L, int H, int P, int N, int Q,
+                                                        int nc)
+{
+    __shared__ float red[kT / kWave];
+    const int h = blockIdx.x % H;
+    const int64_t b = blockIdx.x / H;
+    const int64_t bh = b * H + h;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    auto block_sum = [&](float v) {
+        v = group_sum<kWave>(v);
+        __syncthreads();
+        if (lane == 0) red[wave] = v;
+        __syncthreads();
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < kT / kWave; ++w) s += red[w];
+        return s;
+    };
+    // <dfinal, h_final>: the gradient every log-decay receives through the final state
+    float fh = 0.f;
+    if (dfinal) {
+        const int64_t PN = (int64_t)P * N;
+        for (int64_t i = tid; i < PN; i += kT) fh += dfinal[bh * PN + i] * hfinal[bh * PN + i];
+    }
+    float carry = block_sum(fh);
+    const float a = A[h], dh = Dv[h];
+    float dA_acc = 0.f, dD_acc = 0.f;
+    const int64_t Lp = (int64_t)nc * Q;
+    const int nblk = (int)((L + kT - 1) / kT);
+    for (int blk = nblk - 1; blk >= 0; --blk) {
+        const int64_t t = (int64_t)blk * kT + (kT - 1 - tid);
+        float q = 0.f, xdu = 0.f, dtv = 0.f;
+        if (t < L) {
+            const int64_t row = (b * L + t) * H + h;
+            const int64_t tau = (int64_t)(nc - 1 - t / Q) * Q + (Q - 1 - t % Q);
+            const int64_t rrow = (b * Lp + tau) * H + h;
+            dtv = dt[row];
+            float dyy = 0.f, xdy = 0.f;
+            for (int p0 = 0; p0 < P; p0 += 8) {
+                Vec8<T> xv, dv, o;
+                load8(xv, x + row * P + p0);
+                load8(dv, dy + row * P + p0);
+                const float4 y0 = *reinterpret_cast<const float4*>(yhat + row * P + p0);
+                const float4 y1 = *reinterpret_cast<const float4*>(yhat + row * P + p0 + 4);
+                const float4 u0 = *reinterpret_cast<const float4*>(du_rev + rrow * P + p0);
+                const float4 u1 = *reinterpret_cast<const float4*>(du_rev + rrow * P + p0 + 4);
+                const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+                const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float xf = xv.get(k), df = dv.get(k);
+                    dyy += df * yv[k];
+                    xdu += xf * uv[k];
+                    xdy += xf * df;
+                    o.set(k, fmaf(dtv, uv[k], dh * df));
+                }
+                store8(dx + row * P + p0, o);
+            }
+            q = dyy - dtv * xdu;
+            dD_acc += xdy;
+        }
+        // suffix sum over tokens = prefix sum over threads, plus everything after this block
+        float incl = wave_inclusive_sum(q);
+        __syncthreads();
+        if (lane == kWave - 1) red[wave] = incl;
+        __syncthreads();
+        float before = 0.f, total = 0.f;
+#pragma unroll
+        for (int w = 0; w < kT / kWave; ++w) {
+            before += w < wave ? red[w] : 0.f;
+            total += red[w];
+        }
+        const float dl = carry + before + incl;
+        if (t < L) {
+            ddt[(b * L + t) * H + h] = fmaf(a, dl, xdu);
+            dA_acc += dtv * dl;
+        }
+        carry += total;
+    }
+    const float sa = block_sum(dA_acc);
+    const float sd = block_sum(dD_acc);
+    if (tid == 0) {
+        dAp[bh] = sa;
+        dDp[bh] = sd;
+    }
+}
+
+// dB and dC: the per-head parts summed over each group's heads (dB's parts are in reversed time)
+template <typename T>
+__global__ __launch_bounds__(kT) void bwd_group_sum_kernel(const float* __restrict__ dBh_rev,
+                                                           const float* __restrict__ dCh, T* __restrict__ dB,
+                                                           T* __restrict__ dC, int batch, int64_t L, int H, int N,
+                                                           int G, int Q, int nc, int nsplit)
+{
+    const int hpg = H / G, Nh = N / nsplit;
+    const int64_t Lp = (int64_t)nc * Q;
+    const int64_t n = (int64_t)batch * L * G * (N / 4);
+    for (int64_t i = gtid(); i < n; i += grid_stride()) {
+        const int n0 = (int)(i % (N / 4)) * 4;
+        int64_t r = i / (N / 4);
+        const int g = (int)(r % G);
+        const int64_t bt = r / G;
+        const int64_t b = bt / L, t = bt % L;
+        const int64_t tau = (int64_t)(nc - 1 - t / Q) * Q + (Q - 1 - t % Q);
+        const int k = n0 / Nh, j = n0 % Nh;
+        float4 sb = make_float4(0.f, 0.f, 0.f, 0.f), sc = sb;
+        for (int hh = 0; hh < hpg; ++hh) {
+            const int h = g * hpg + hh;
+            const float4 vb = *reinterpret_cast<const float4*>(dBh_rev + ((((int64_t)k * batch + b) * Lp + tau) * H + h) * Nh + j);
+            const float4 vc = *reinterpret_cast<const float4*>(dCh + ((((int64_t)k * batch + b) * L + t) * H + h) * Nh + j);
+            sb.x += vb.x; sb.y += vb.y; sb.z += vb.z; sb.w += vb.w;
+            sc.x += vc.x; sc.y += vc.y; sc.z += vc.z; sc.w += vc.w;
+        }
+        const int64_t o = ((b * L + t) * G + g) * N + n0;
+        store4(dB + o, sb.x, sb.y, sb.z, sb.w);
+        store4(dC + o, sc.x, sc.y, sc.z, sc.w);
+    }
+}
+
+__global__ __launch_bounds__(kT) void bwd_heads_kernel(const float* __restrict__ dAp, const float* __restrict__ dDp,
+                                                       float* __restrict__ dA, float* __restrict__ dD, int batch, int H)
+{
+    for (int h = blockIdx.x * kT + threadIdx.x; h < H; h += gridDim.x * kT) {
+        float sa = 0.f, sd = 0.f;
+        for (int b = 0; b < batch; ++b) {
+            sa += dAp[(int64_t)b * H + h];
+            sd += dDp[(int64_t)b * H + h];
+        }
+        dA[h] = sa;
+        dD[h] = sd;
+    }
+}
+
+__global__ __launch_bounds__(kT) void fill_zero_kernel(float* __restrict__ p, int64_t n)
+{
+    for (int64_t i = gtid(); i < n; i += grid_stride()) p[i] = 0.f;
+}
+
+unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + kT - 1) / kT, 8192)); }
+
+}  // namespace
+
+BwdLayout bwd_layout(const Dims& d, int elem)
+{
+    BwdLayout w;
+    const int64_t nc = d.nchunks(), Lp = nc * d.chunk;
+    const int64_t B = d.batch, H = d.nheads, P = d.headdim, N = d.dstate, G = d.ngroups;
+    const int64_t tab = B * H * nc * d.chunk * 4;
+    const int64_t st = B * nc * H * P * N;
+    size_t o = 0;
+    auto take = [&](int64_t bytes) { const size_t at = o; o += (size_t)((bytes + 255) / 256 * 256); return at; };
+    w.cs = take(tab);
+    w.dtc = take(tab);
+    w.W = take(tab);
+    w.Z = take(tab);
+    w.dtp = take(tab);
+    w.csp = take(tab);
+    w.states = take(st * 4);
+    w.entry = take(st * elem);
+    w.SinT = take(st * elem);
+    w.Gout_rev = take(st * elem);
+    w.GoutT_rev = take(st * elem);
+    w.hfinal = take(B * H * P * N * 4);
+    w.yhat = take(B * d.seqlen * H * P * 4);
+    w.dy_rev = take(B * Lp * H * P * elem);
+    w.u_rev = take(B * Lp * H * P * elem);
+    w.B_rev = take(B * Lp * G * N * elem);
+    w.C_rev = take(B * Lp * G * N * elem);
+    w.Crep_rev = take(B * Lp * H * N * elem);
+    w.Brep = take(B * d.seqlen * H * N * elem);
+    w.du_rev = take(B * Lp * H * P * 4);
+    w.dBh_rev = take(B * Lp * H * N * 4);
+    w.dCh = take(B * d.seqlen * H * N * 4);
+    w.zeros = take(std::max<int64_t>(H, 1) * 4);
+    w.dAp = take(B * H * 4);
+    w.dDp = take(B * H * 4);
+    w.total = std::max<size_t>(o, 256);
+    return w;
+}
+
+template <typename T>
+hipError_t launch_backward(const T* x, const float* dt, const float* A, const T* Bm, const T* Cm, const float* D,
+                           const float* init, const T* dy, const float* dfinal, T* dx, float* ddt, float* dA, T* dB,
+                           T* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t s)
+{
+    const BwdLayout w = bwd_layout(d, (int)sizeof(T));
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+    auto TT = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+    const int nc = (int)d.nchunks(), Q = (int)d.chunk;
+    const int B = (int)d.batch, H = (int)d.nheads, P = (int)d.headdim, N = (int)d.dstate, G = (int)d.ngroups;
+    const int nsplit = N > 128 ? 2 : 1;
+    const int Nh = N / nsplit;
+    const int64_t L = d.seqlen, Lp = (int64_t)nc * Q;
+    hipError_t e;
+#define SSD_TRY(expr) do { e = (expr); if (e != hipSuccess) return e; } while (0)
+    float* zeros = F(w.zeros);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(kT), 0, s, zeros, (int64_t)H);
+    SSD_TRY(hipGetLastError());
+    // forward recompute: chunk states, entry states (T), the final state, yhat = y - D x (fp32)
+    SSD_TRY(launch_chunk_state_cumsum<T>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
+    SSD_TRY(launch_state_passing<T>(F(w.states), F(w.cs), init, TT(w.entry), F(w.hfinal), d, s));
+    SSD_TRY(launch_chunk_scan_f32out<T>(x, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), zeros, F(w.yhat), d, s));
+    // tables, adjoint chunk states (into the chunk-state buffer, free again), adjoint passing
+    const int64_t nrows = (int64_t)B * H * nc;
+    hipLaunchKernelGGL(bwd_tables_kernel, dim3(grid_for(nrows * Q)), dim3(kT), 0, s, F(w.cs), F(w.W), F(w.Z), F(w.dtp),
+                       F(w.csp), nrows, (int)L, Q, nc);
+    SSD_TRY(hipGetLastError());
+    SSD_TRY(launch_chunk_state<T>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
+    hipLaunchKernelGGL((bwd_passing_kernel<T>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
+                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, TT(w.Gout_rev), TT(w.GoutT_rev),
+                       dinit, B, H, P, N, Q, nc, nsplit);
+    SSD_TRY(hipGetLastError());
+    // reversed and per-head copies, S_in^T
+    const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)nsplit * B * Lp * H * (Nh / 8));
+    hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, TT(w.dy_rev),
+                       TT(w.B_rev), TT(w.C_rev), TT(w.u_rev), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q, H, P, N, G,
+                       nsplit);
+    SSD_TRY(hipGetLastError());
+    hipLaunchKernelGGL((bwd_transpose_kernel<T>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
+                       TT(w.entry), TT(w.SinT), nrows, P, N, nsplit);
+    SSD_TRY(hipGetLastError());
+    // du: the adjoint readout, on the reversed sequence
+    const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
+    SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.dy_rev), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev),
+                                        zeros, F(w.du_rev), dr, s));
+    // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half
+    const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
+    const Dims dcd{d.batch, L, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
+    for (int k = 0; k < nsplit; ++k) {
+        SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.Crep_rev) + (int64_t)k * B * Lp * H * Nh, TT(w.dy_rev),
+                                            TT(w.u_rev), F(w.dtp), F(w.csp),
+                                            TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P, zeros,
+                                            F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
+        SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.Brep) + (int64_t)k * B * L * H * Nh, x, dy, F(w.dtc), F(w.cs),
+                                            TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
+                                            F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
+    }
+    // per token, then the group and batch sums
+    hipLaunchKernelGGL((bwd_tokens_kernel<T>), dim3((unsigned)(B * H)), dim3(kT), 0, s, x, dt, A, D, dy, F(w.yhat),
+                       F(w.du_rev), dfinal, F(w.hfinal), dx, ddt, F(w.dAp), F(w.dDp), L, H, P, N, Q, nc);
+    SSD_TRY(hipGetLastError());
+    hipLaunchKernelGGL((bwd_group_sum_kernel<T>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
+                       F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
+    SSD_TRY(hipGetLastError());
+    hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, F(w.dAp), F(w.dDp), dA, dD, B, H);
+    SSD_TRY(hipGetLastError());
+#undef SSD_TRY
+    return hipSuccess;
+}
+
+namespace {
+
+__global__ __launch_bounds__(kT) void widen_kernel(const bf16* __restrict__ src, float* __restrict__ dst, int64_t n8)
+{
+    for (int64_t i = gtid(); i < n8; i += grid_stride()) {
+        Vec8<bf16> v;
+        load8(v, src + 8 * i);
+        Vec8<float> f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f.set(k, v.get(k));
+        store8(dst + 8 * i, f);
+    }
+}
+
+__global__ __launch_bounds__(kT) void narrow_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int64_t n8)
+{
+    for (int64_t i = gtid(); i < n8; i += grid_stride()) {
+        Vec8<float> f;
+        load8(f, src + 8 * i);
+        Vec8<bf16> v;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v.set(k, f.get(k));
+        store8(dst + 8 * i, v);
+    }
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs)
+{
+    const size_t base = bwd_layout(d, 4).total;
+    if (!bf16_inputs) return base;
+    const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
+    auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
+    return base + 3 * up(nx * 4) + 4 * up(nb * 4);       // x, dy, dx and B, C, dB, dC in fp32
+}
+
+hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* Bm, const bf16* Cm,
+                                const float* D, const float* init, const bf16* dy, const float* dfinal, bf16* dx,
+                                float* ddt, float* dA, bf16* dB, bf16* dC, float* dD, float* dinit, const Dims& d,
+                                void* workspace, hipStream_t s)
+{
+    const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
+    auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
+    unsigned char* p = static_cast<unsigned char*>(workspace) + bwd_layout(d, 4).total;
+    float* x32 = reinterpret_cast<float*>(p);  p += up(nx * 4);
+    float* dy32 = reinterpret_cast<float*>(p); p += up(nx * 4);
+    float* dx32 = reinterpret_cast<float*>(p); p += up(nx * 4);
+    float* B32 = reinterpret_cast<float*>(p);  p += up(nb * 4);
+    float* C32 = reinterpret_cast<float*>(p);  p += up(nb * 4);
+    float* dB32 = reinterpret_cast<float*>(p); p += up(nb * 4);
+    float* dC32 = reinterpret_cast<float*>(p);
+    // element counts are multiples of 8 (headdim and dstate are multiples of 16)
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, x, x32, nx / 8);
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dy, dy32, nx / 8);
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Bm, B32, nb / 8);
+    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Cm, C32, nb / 8);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_backward<float>(x32, dt, A, B32, C32, D, init, dy32, dfinal, dx32, ddt, dA, dB32, dC32, dD, dinit, d,
+                               workspace, s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dx32, dx, nx / 8);
+    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dB32, dB, nb / 8);
+    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dC32, dC, nb / 8);
+    return hipGetLastError();
+}
+
+template hipError_t launch_backward<float>(const float*, const float*, const float*, const float*, const float*,
+                                           const float*, const float*, const float*, const float*, float*, float*,
+                                           float*, float*, float*, float*, float*, const Dims&, void*, hipStream_t);
+
+}  // namespace ssd

@@ -121,11 +121,12 @@ using ScanShape = typename decltype(pick_shape<T, P, NK,
 // for a stage ending at token e wholly before row l this factors into [tstart[l] <= e] per row
 // times [s >= tstart[e]] per token, which fold into the row decay and the token table; the state
 // entering the chunk reaches only the rows of the sequence holding the chunk's first token.
-template <typename T, int P, int NK, class S, bool kVarlen>
+// TY: the type y is stored in (T, or float when the caller needs the sum unrounded).
+template <typename T, typename TY, int P, int NK, class S, bool kVarlen>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
-    const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, T* __restrict__ y,
+    const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, TY* __restrict__ y,
     int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
@@ -369,9 +370,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 
     {
-        T* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
+        TY* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc(yb, 0, len * nheads * P * (int)sizeof(T), kBufferDword3);
+            __builtin_amdgcn_make_buffer_rsrc(yb, 0, len * nheads * P * (int)sizeof(TY), kBufferDword3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = 16 * rbk[j] + r16;
@@ -381,17 +382,17 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 const bool ok = rok && hh < nh;
 #pragma unroll
                 for (int pt = 0; pt < P / 16; ++pt) {
-                    const int off = ok ? ((row * nheads + hh) * P + 16 * pt + 4 * grp) * (int)sizeof(T) : kDropped;
-                    buffer_store4(rs, off, 0, acc[j][hh][pt], T{});
+                    const int off = ok ? ((row * nheads + hh) * P + 16 * pt + 4 * grp) * (int)sizeof(TY) : kDropped;
+                    buffer_store4(rs, off, 0, acc[j][hh][pt], TY{});
                 }
             }
         }
     }
 }
 
-template <typename T, int P, int NK, bool V>
+template <typename T, typename TY, int P, int NK, bool V>
 hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
-                  const float* D, const int* tstart, T* y, const Dims& d, hipStream_t stream)
+                  const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
 {
     using S = ScanShape<T, P, NK, V>;
     static_assert(S::fits, "LDS budget");
@@ -404,20 +405,20 @@ hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const fl
     const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((chunk_scan_kernel<T, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        x, B, C, dtc, cs, entry, D, tstart, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, bool V>
+template <typename T, typename TY, bool V>
 hipError_t launch_any(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
-                      const float* D, const int* tstart, T* y, const Dims& d, hipStream_t stream)
+                      const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
 #define SSD_SCAN_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+    if (d.headdim == PP && nki == KK) return launch<T, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -432,7 +433,15 @@ hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt
                              const float* dA_cs, const T* entry_states, const float* D, T* y,
                              const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+    return launch_any<T, T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+}
+
+template <typename T>
+hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const float* dt_chunked,
+                                    const float* dA_cs, const T* entry_states, const float* D, float* y,
+                                    const Dims& d, hipStream_t stream)
+{
+    return launch_any<T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
 }
 
 template <typename T>
@@ -440,7 +449,7 @@ hipError_t launch_chunk_scan_varlen(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, const int* tstart,
                                     T* y, const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
+    return launch_any<T, T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
 }
 
 template hipError_t launch_chunk_scan<float>(const float*, const float*, const float*, const float*,
@@ -449,6 +458,12 @@ template hipError_t launch_chunk_scan<float>(const float*, const float*, const f
 template hipError_t launch_chunk_scan<bf16>(const bf16*, const bf16*, const bf16*, const float*,
                                             const float*, const bf16*, const float*, bf16*,
                                             const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_f32out<float>(const float*, const float*, const float*, const float*,
+                                                    const float*, const float*, const float*, float*,
+                                                    const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_f32out<bf16>(const bf16*, const bf16*, const bf16*, const float*,
+                                                   const float*, const bf16*, const float*, float*,
+                                                   const Dims&, hipStream_t);
 template hipError_t launch_chunk_scan_varlen<float>(const float*, const float*, const float*, const float*,
                                                     const float*, const float*, const float*, const int*, float*,
                                                     const Dims&, hipStream_t);

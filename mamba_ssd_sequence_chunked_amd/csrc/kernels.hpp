@@ -51,6 +51,12 @@ hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt
                              const float* dA_cs, const T* entry_states, const float* D, T* y,
                              const Dims& d, hipStream_t stream);
 
+// stage 4 with y stored in fp32 (no rounding to T)
+template <typename T>
+hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const float* dt_chunked,
+                                    const float* dA_cs, const T* entry_states, const float* D, float* y,
+                                    const Dims& d, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
                            const T* C, const float* D, T* y, const Dims& d, hipStream_t stream);
@@ -59,5 +65,24 @@ template <typename T>
 hipError_t launch_selective_scan(const T* x, const float* delta, const float* A, const T* B, const T* C,
                                  const float* D, const float* init, T* y, float* final_states, int64_t batch,
                                  int64_t seqlen, int64_t dim, int64_t dstate, hipStream_t stream);
+
+// the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
+struct BwdLayout {
+    size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, u_rev, B_rev,
+        C_rev, Crep_rev, Brep, du_rev, dBh_rev, dCh, zeros, dAp, dDp, total;
+};
+BwdLayout bwd_layout(const Dims& d, int elem_bytes);
+size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
+
+// bf16 inputs: widened to fp32, the fp32 pass, dx / dB / dC rounded back (see bwd.hip)
+hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* B, const bf16* C,
+                                const float* D, const float* init, const bf16* dy, const float* dfinal, bf16* dx,
+                                float* ddt, float* dA, bf16* dB, bf16* dC, float* dD, float* dinit, const Dims& d,
+                                void* workspace, hipStream_t stream);
+
+template <typename T>
+hipError_t launch_backward(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
+                           const float* init, const T* dy, const float* dfinal, T* dx, float* ddt, float* dA, T* dB,
+                           T* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t stream);
 
 }  // namespace ssd

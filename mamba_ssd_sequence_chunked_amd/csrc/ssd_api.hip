@@ -137,7 +137,7 @@ const char* ssd_status_string(int status)
     }
 }
 
-int ssd_abi_version(void) { return 102; }
+int ssd_abi_version(void) { return 103; }
 
 int64_t ssd_num_chunks(int64_t seqlen, int64_t chunk_size)
 {
@@ -380,6 +380,66 @@ int ssd_forward_varlen(const void* x, const float* dt, const float* A, const voi
                                                      (const float*)entry, D, tstart, (float*)y, d, s);
     }
     return hip_status(e);
+}
+
+namespace {
+int check_backward(const Dims& d, int dtype)
+{
+    if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
+    int rc = check_seq(d);
+    if (rc != SSD_OK) return rc;
+    // the per-head dB / dC passes put dstate in the head dimension's place
+    if (d.dstate != 16 && d.dstate != 32 && d.dstate != 64 && d.dstate != 128 && d.dstate != 256) return SSD_ERR_SHAPE;
+    if (d.nheads * d.dstate > (int64_t(1) << 20)) return SSD_ERR_SHAPE;
+    return SSD_OK;
+}
+}  // namespace
+
+size_t ssd_backward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                                    int64_t ngroups, int64_t chunk_size, int dtype)
+{
+    Dims d{batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size};
+    if (check_backward(d, dtype) != SSD_OK) return 0;
+    return ssd::bwd_workspace_bytes(d, dtype == SSD_BF16);
+}
+
+int ssd_backward(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                 const float* init_states, const void* dy, const float* dfinal, void* dx, float* ddt, float* dA,
+                 void* dB, void* dC, float* dD, float* dinit, int64_t batch, int64_t seqlen, int64_t nheads,
+                 int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream)
+{
+    Dims d{batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size};
+    int rc = check_backward(d, dtype);
+    if (rc != SSD_OK) return rc;
+    if (!A || !D || !dA || !dD || !dinit) return SSD_ERR_NULL;
+    if (batch == 0) return SSD_OK;
+    if (seqlen > 0 && (!x || !dt || !B || !C || !dy || !dx || !ddt || !dB || !dC)) return SSD_ERR_NULL;
+    const size_t need = ssd::bwd_workspace_bytes(d, dtype == SSD_BF16);
+    if (workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    if (!workspace) return SSD_ERR_NULL;
+    if (!aligned16(workspace) || !aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(dy) ||
+        !aligned16(dx) || !aligned16(dB) || !aligned16(dC) || !aligned16(init_states) || !aligned16(dfinal) ||
+        !aligned16(dinit))
+        return SSD_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)(batch * seqlen * nheads * headdim) * es;
+    const size_t nb = (size_t)(batch * seqlen * ngroups * dstate) * es;
+    const size_t nst = (size_t)(batch * nheads * headdim * dstate) * 4;
+    const size_t ndt = (size_t)(batch * seqlen * nheads) * 4;
+    const size_t nh = (size_t)nheads * 4;
+    if (any_overlap({{dx, nx}, {ddt, ndt}, {dA, nh}, {dB, nb}, {dC, nb}, {dD, nh}, {dinit, nst}, {workspace, need}},
+                    {{x, nx}, {dt, ndt}, {A, nh}, {B, nb}, {C, nb}, {D, nh}, {init_states, init_states ? nst : 0},
+                     {dy, nx}, {dfinal, dfinal ? nst : 0}}))
+        return SSD_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == SSD_BF16)
+        return hip_status(ssd::launch_backward_bf16((const bf16*)x, dt, A, (const bf16*)B, (const bf16*)C, D,
+                                                    init_states, (const bf16*)dy, dfinal, (bf16*)dx, ddt, dA,
+                                                    (bf16*)dB, (bf16*)dC, dD, dinit, d, workspace, s));
+    return hip_status(ssd::launch_backward<float>((const float*)x, dt, A, (const float*)B, (const float*)C, D,
+                                                  init_states, (const float*)dy, dfinal, (float*)dx, ddt, dA,
+                                                  (float*)dB, (float*)dC, dD, dinit, d, workspace, s));
 }
 
 int ssd_step(float* state, const void* x, const float* dt, const float* A, const void* B,

@@ -65,6 +65,10 @@ def load_library():
     lib.ssd_forward_varlen_workspace_bytes.argtypes = [i64] * 5 + [i32]
     lib.ssd_forward_varlen.restype = i32
     lib.ssd_forward_varlen.argtypes = [vp] * 7 + [i64] + [vp] * 2 + [i64] * 6 + [i32, vp, sz, vp]
+    lib.ssd_backward_workspace_bytes.restype = sz
+    lib.ssd_backward_workspace_bytes.argtypes = [i64] * 7 + [i32]
+    lib.ssd_backward.restype = i32
+    lib.ssd_backward.argtypes = [vp] * 16 + [i64] * 7 + [i32, vp, sz, vp]
     lib.ssd_selective_scan.restype = i32
     lib.ssd_selective_scan.argtypes = [vp] * 9 + [i64] * 4 + [i32, vp]
     _lib = lib
@@ -185,6 +189,41 @@ def step(state: torch.Tensor, x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor
                       G, code, _stream(dev))
     _check("ssd_step", rc)
     return y
+
+
+def backward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+             D: torch.Tensor, dy: torch.Tensor, chunk_size: int, init_states: Optional[torch.Tensor] = None,
+             dfinal: Optional[torch.Tensor] = None) -> dict:
+    """Gradients of ``forward`` for dL/dy = dy and dL/d(final_states) = dfinal (None = 0); see
+    ssd_backward.  Returns a dict with dx, ddt, dA, dB, dC, dD, dinit (dx, dB, dC in x's dtype)."""
+    lib = load_library()
+    b, L, H, P, N, G = _forward_dims(x, B)
+    dev = x.device
+    code = _dtype_code(x)
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    _need(dy, "dy", (b, L, H, P), x.dtype, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    if dfinal is not None:
+        _need(dfinal, "dfinal", (b, H, P, N), torch.float32, dev)
+    ws_bytes = lib.ssd_backward_workspace_bytes(b, L, H, P, N, G, chunk_size, code)
+    if ws_bytes == 0:
+        raise SSDError("ssd_backward_workspace_bytes", -2)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty_like(dt), dA=torch.empty_like(A), dB=torch.empty_like(B),
+               dC=torch.empty_like(C), dD=torch.empty_like(D),
+               dinit=torch.empty((b, H, P, N), dtype=torch.float32, device=dev))
+    rc = lib.ssd_backward(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states), _ptr(dy),
+                          _ptr(dfinal), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]),
+                          _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), b, L, H, P, N, G, chunk_size, code,
+                          _ptr(ws), ws.numel(), _stream(dev))
+    _check("ssd_backward", rc)
+    return out
 
 
 def forward_varlen(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

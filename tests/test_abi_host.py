@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"ssd_forward", "ssd_step", "ssd_forward_workspace_bytes", "ssd_status_string", "ssd_dA_cumsum",
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_selective_scan", "ssd_forward_varlen",
-            "ssd_forward_varlen_workspace_bytes"} <= set(names)
+            "ssd_forward_varlen_workspace_bytes", "ssd_backward", "ssd_backward_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in include/ssd.h but not exported"
 
@@ -44,7 +44,7 @@ def test_status_strings():
     for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS):
         assert ssd.status_string(code).startswith("SSD_")
     assert "unknown" in ssd.status_string(123)
-    assert ssd.load_library().ssd_abi_version() == 102
+    assert ssd.load_library().ssd_abi_version() == 103
 
 
 def test_num_chunks_and_workspace():
@@ -150,6 +150,31 @@ def test_forward_varlen_rejects():
     up = lambda v: (v + 255) // 256 * 256    # noqa: E731
     assert ws == 2 * up(4 * nc * 64 * 4) + up(nc * 4 * 16 * 16 * 4) * 2 + up(300 * 4) + up(nc * 16)
     assert lib.ssd_forward_varlen_workspace_bytes(300, 4, 48, 16, 64, 0) == 0
+
+
+def test_backward_rejects():
+    lib = ssd.load_library()
+    assert lib.ssd_backward_workspace_bytes(2, 100, 4, 16, 48, 1, 64, 0) == 0      # dstate 48: not a head size
+    assert lib.ssd_backward_workspace_bytes(2, 100, 4, 16, 32, 1, 64, 0) > 0
+    assert lib.ssd_backward_workspace_bytes(2, 100, 4, 16, 32, 1, 64, 1) > lib.ssd_backward_workspace_bytes(
+        2, 100, 4, 16, 32, 1, 64, 0)                                                # bf16: fp32 copies too
+
+    def call(**kw):
+        a = dict(x=fake(1), dt=fake(2), A=fake(3), B=fake(4), C=fake(5), D=fake(6), init=None, dy=fake(7),
+                 dfinal=None, dx=fake(8), ddt=fake(9), dA=fake(10), dB=fake(11), dC=fake(12), dD=fake(13),
+                 dinit=fake(14), b=2, L=100, H=4, P=16, N=32, G=1, Q=64, dtype=0, ws=fake(15), ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.ssd_backward(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"], a["dy"], a["dfinal"],
+                                a["dx"], a["ddt"], a["dA"], a["dB"], a["dC"], a["dD"], a["dinit"], a["b"], a["L"], a["H"],
+                                a["P"], a["N"], a["G"], a["Q"], a["dtype"], a["ws"], a["ws_bytes"], None)
+
+    assert call(N=48) == ERR_SHAPE
+    assert call(dtype=4) == ERR_DTYPE
+    assert call(dinit=None) == ERR_NULL
+    assert call(dy=None) == ERR_NULL
+    assert call(ws_bytes=1000) == ERR_WS
+    assert call(dx=fake(1)) == ERR_ALIAS
+    assert call(batch=0) if False else call(b=0) == OK
 
 
 def test_selective_scan_rejects():

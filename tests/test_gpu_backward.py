@@ -1,0 +1,93 @@
+"""Parity of the backward pass (ssd_backward) against the fp64 oracle's gradients."""
+import numpy as np
+import pytest
+
+import oracle
+from mamba_ssd_sequence_chunked_amd.inputs import make_inputs, make_random
+from util import TOL, head_slice, slice_rel_err, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+# (batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype, init, dfinal): ragged last chunks,
+# groups, every head size, dstate up to 256 (computed in two halves), with and without the
+# initial state and the final-state gradient
+CASES = [
+    (1, 64, 2, 16, 16, 1, 16, "f32", False, False),
+    (2, 100, 4, 16, 32, 2, 32, "f32", True, True),
+    (2, 300, 4, 32, 64, 1, 64, "f32", True, True),
+    (1, 256, 4, 64, 128, 1, 256, "bf16", False, True),
+    (1, 200, 4, 64, 256, 2, 128, "bf16", True, False),
+    (2, 77, 6, 128, 16, 3, 64, "f32", False, True),
+    (1, 1000, 4, 64, 128, 1, 256, "bf16", True, True),
+]
+
+
+def _grads(inp, dy, dfin):
+    import torch
+    import mamba_ssd_sequence_chunked_amd as ssd
+    d = {k: to_device(getattr(inp, k)) for k in ("x", "dt", "A", "B", "C", "D", "init")}
+    g = ssd.backward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], to_device(dy), inp.chunk_size, d["init"],
+                     None if dfin is None else to_device(dfin))
+    torch.cuda.synchronize()
+    return {k: to_f64(v) for k, v in g.items()}
+
+
+def _rel_all(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+@pytest.mark.parametrize("c", CASES, ids=["b{}_L{}_H{}_P{}_N{}_G{}_Q{}_{}_i{}_f{}".format(*c) for c in CASES])
+def test_backward_matches_oracle(c):
+    b, L, H, P, N, G, Q, dt, init, dfin = c
+    inp = make_random(b, L, H, P, N, G, Q, dt, "shifted", init, seed=800 + CASES.index(c))
+    rng = np.random.default_rng(850 + CASES.index(c))
+    dy64 = rng.standard_normal((b, L, H, P))
+    from mamba_ssd_sequence_chunked_amd.inputs import bf16_bits, bf16_to_f64
+    dy = bf16_bits(dy64) if dt == "bf16" else dy64.astype(np.float32)
+    dyf = bf16_to_f64(dy) if dt == "bf16" else dy.astype(np.float64)
+    dfinal = (0.3 * rng.standard_normal((b, H, P, N))).astype(np.float32) if dfin else None
+    g = _grads(inp, dy, dfinal)
+    r = oracle.backward(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D, inp.f64("init"), dyf, dfinal)
+    tol = TOL[dt]
+    assert slice_rel_err(g["dx"], r["dx"], 2) <= tol, "dx"
+    assert slice_rel_err(g["ddt"][..., None], r["ddt"][..., None], 2) <= tol, "ddt"
+    assert slice_rel_err(g["dB"], r["dB"], 2) <= tol, "dB"
+    assert slice_rel_err(g["dC"], r["dC"], 2) <= tol, "dC"
+    assert slice_rel_err(g["dinit"], r["dinit"], 1) <= tol, "dinit"
+    assert _rel_all(g["dA"], r["dA"]) <= tol, "dA"
+    assert _rel_all(g["dD"], r["dD"]) <= tol, "dD"
+
+
+def test_backward_empty_sequence():
+    """No tokens: the initial state's gradient is the final state's, the rest is zero-sized or zero."""
+    import torch
+    import mamba_ssd_sequence_chunked_amd as ssd
+    z = torch.empty((1, 0, 2, 16), device="cuda")
+    zb = torch.empty((1, 0, 1, 16), device="cuda")
+    dfin = torch.randn((1, 2, 16, 16), device="cuda")
+    g = ssd.backward(z, torch.empty((1, 0, 2), device="cuda"), torch.full((2,), -1.0, device="cuda"), zb, zb,
+                     torch.ones(2, device="cuda"), z, 64, None, dfin)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dinit"], dfin)
+    assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0)
+
+
+def test_backward_full_size_sampled():
+    """The 2.7B-layer shape (4 x 4096 tokens, 80 heads, N = 128, bf16) in the benchmark's launch
+    configuration; a head's dx, ddt and dinit depend on that head's inputs and the group's B, C
+    only, so sampled (batch, head) pairs are checked against the oracle run on them alone."""
+    inp = make_inputs("l2p7b")
+    b, L, H, P, N, G = inp.dims
+    rng = np.random.default_rng(870)
+    from mamba_ssd_sequence_chunked_amd.inputs import bf16_bits, bf16_to_f64
+    dy = bf16_bits(rng.standard_normal((b, L, H, P)))
+    g = _grads(inp, dy, None)
+    for bb, h in ((0, 0), (3, 57)):
+        xs, dts, As, Bs, Cs, Ds, h0 = head_slice(inp, bb, h)
+        dys = bf16_to_f64(np.ascontiguousarray(dy[bb:bb + 1, :, h:h + 1]))
+        r = oracle.backward(xs, dts, As, Bs, Cs, Ds, h0, dys, None)
+        print(f"l2p7b backward b={bb} h={h}", flush=True)
+        assert slice_rel_err(g["dx"][bb:bb + 1, :, h:h + 1], r["dx"], 2) <= TOL["bf16"]
+        assert slice_rel_err(g["ddt"][bb:bb + 1, :, h:h + 1, None], r["ddt"][..., None], 2) <= TOL["bf16"]
+        assert slice_rel_err(g["dinit"][bb:bb + 1, h:h + 1], r["dinit"], 1) <= TOL["bf16"]
+    assert np.all(np.isfinite(g["dB"])) and np.all(np.isfinite(g["dC"])) and np.all(np.isfinite(g["dA"]))
