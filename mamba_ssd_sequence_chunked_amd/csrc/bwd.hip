@@ -74,21 +74,22 @@ __global__ __launch_bounds__(kT) void bwd_tables_kernel(const float* __restrict_
     }
 }
 
-// reversed (front-padded) copies of dy (B, Lp, H, P), B and C (B, Lp, G, N), u = dt x (B, Lp, H, P),
-// C copied per head and reversed, B copied per head, both split into column halves when N > 128:
+// reversed (front-padded) copies: in fp32 dy (B, Lp, H, P) and B, C (B, Lp, G, N) for the adjoint
+// readout; in TD (the operand type of the dB / dC passes) dy and u = dt x (B, Lp, H, P), C copied
+// per head and reversed, B copied per head, both split into column halves when N > 128:
 // (nsplit, B, Lp|L, H, Nh); eight elements per thread
-template <typename T>
-__global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, const float* __restrict__ dt,
-                                                      const T* __restrict__ Bm, const T* __restrict__ Cm,
-                                                      const T* __restrict__ dy, T* __restrict__ dy_rev,
-                                                      T* __restrict__ B_rev, T* __restrict__ C_rev,
-                                                      T* __restrict__ u_rev, T* __restrict__ Crep_rev,
-                                                      T* __restrict__ Brep, int batch, int64_t L, int nc, int Q,
-                                                      int H, int P, int N, int G, int nsplit)
+template <typename TD>
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ x, const float* __restrict__ dt,
+                                                      const float* __restrict__ Bm, const float* __restrict__ Cm,
+                                                      const float* __restrict__ dy, float* __restrict__ dy_rev,
+                                                      float* __restrict__ B_rev, float* __restrict__ C_rev,
+                                                      TD* __restrict__ dy_revD, TD* __restrict__ u_revD,
+                                                      TD* __restrict__ Crep_rev, TD* __restrict__ Brep, int batch,
+                                                      int64_t L, int nc, int Q, int H, int P, int N, int G, int nsplit)
 {
     const int64_t Lp = (int64_t)nc * Q;
     const int hpg = H / G, Nh = N / nsplit;
-    // 1. per (b, tau, h): dy_rev and u_rev, P / 8 vectors each
+    // 1. per (b, tau, h): dy_rev (fp32 and TD) and u_rev (TD), P / 8 vectors each
     const int64_t n1 = (int64_t)batch * Lp * H * (P / 8);
     for (int64_t i = gtid(); i < n1; i += grid_stride()) {
         const int v = (int)(i % (P / 8));
@@ -97,22 +98,28 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, c
         const int64_t bt = r / H;
         const int64_t b = bt / Lp, tau = bt % Lp;
         const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<T> a, u;
+        Vec8<float> a, xv;
+        Vec8<TD> ad, ud;
         if (t >= 0) {
             const int64_t o = ((b * L + t) * H + h) * P + 8 * v;
             load8(a, dy + o);
-            load8(u, x + o);
+            load8(xv, x + o);
             const float d = dt[(b * L + t) * H + h];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) u.set(k, d * u.get(k));
+            for (int k = 0; k < 8; ++k) {
+                ad.set(k, a.get(k));
+                ud.set(k, d * xv.get(k));
+            }
         } else {
             a.zero();
-            u.zero();
+            ad.zero();
+            ud.zero();
         }
         store8(dy_rev + r * P + 8 * v, a);
-        store8(u_rev + r * P + 8 * v, u);
+        store8(dy_revD + r * P + 8 * v, ad);
+        store8(u_revD + r * P + 8 * v, ud);
     }
-    // 2. per (b, tau, g): B_rev, C_rev
+    // 2. per (b, tau, g): B_rev, C_rev (fp32)
     const int64_t n2 = (int64_t)batch * Lp * G * (N / 8);
     for (int64_t i = gtid(); i < n2; i += grid_stride()) {
         const int v = (int)(i % (N / 8));
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, c
         const int64_t bt = r / G;
         const int64_t b = bt / Lp, tau = bt % Lp;
         const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<T> vb, vc;
+        Vec8<float> vb, vc;
         if (t >= 0) {
             const int64_t o = ((b * L + t) * G + g) * N + 8 * v;
             load8(vb, Bm + o);
@@ -133,7 +140,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, c
         store8(B_rev + r * N + 8 * v, vb);
         store8(C_rev + r * N + 8 * v, vc);
     }
-    // 3. per (split, b, tau, h): C copied per head, reversed; per (split, b, t, h): B copied per head
+    // 3. per (split, b, tau, h): C copied per head, reversed; per (split, b, t, h): B copied per head (TD)
     const int64_t n3 = (int64_t)nsplit * batch * Lp * H * (Nh / 8);
     for (int64_t i = gtid(); i < n3; i += grid_stride()) {
         const int v = (int)(i % (Nh / 8));
@@ -146,21 +153,27 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const T* __restrict__ x, c
         const int k = (int)(r / batch);
         const int g = h / hpg;
         const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<T> vc;
+        Vec8<float> vc;
+        Vec8<TD> vcd;
         if (t >= 0) load8(vc, Cm + ((b * L + t) * G + g) * N + k * Nh + 8 * v);
         else vc.zero();
-        store8(Crep_rev + (((k * batch + b) * Lp + tau) * H + h) * Nh + 8 * v, vc);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) vcd.set(q, vc.get(q));
+        store8(Crep_rev + (((k * batch + b) * Lp + tau) * H + h) * Nh + 8 * v, vcd);
         if (tau < L) {
-            Vec8<T> vb;
+            Vec8<float> vb;
+            Vec8<TD> vbd;
             load8(vb, Bm + ((b * L + tau) * G + g) * N + k * Nh + 8 * v);
-            store8(Brep + (((k * batch + b) * L + tau) * H + h) * Nh + 8 * v, vb);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vbd.set(q, vb.get(q));
+            store8(Brep + (((k * batch + b) * L + tau) * H + h) * Nh + 8 * v, vbd);
         }
     }
 }
 
 // S_in^T per chunk and head, split into column halves: (nsplit, B, nc, H, Nh, P) from (B, nc, H, P, N)
-template <typename T>
-__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const T* __restrict__ src, T* __restrict__ dst,
+template <typename TD>
+__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const float* __restrict__ src, TD* __restrict__ dst,
                                                            int64_t nblk, int P, int N, int nsplit)
 {
     const int Nh = N / nsplit;
@@ -172,16 +185,16 @@ __global__ __launch_bounds__(kT) void bwd_transpose_kernel(const T* __restrict__
         r /= Nh;
         const int64_t blk = r % nblk;              // (b, c, h)
         const int k = (int)(r / nblk);
-        dst[i] = src[(blk * P + p) * N + k * Nh + j];
+        dst[i] = from_f32<TD>(src[(blk * P + p) * N + k * Nh + j]);
     }
 }
 
 // backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
 // order as T (P x N) and transposed (split into column halves, N x P); dinit at the end
-template <typename T>
+template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
-                                                         const float* __restrict__ dfinal, T* __restrict__ Gout_rev,
-                                                         T* __restrict__ GoutT_rev, float* __restrict__ dinit,
+                                                         const float* __restrict__ dfinal, float* __restrict__ Gout_rev,
+                                                         TD* __restrict__ GoutT_rev, float* __restrict__ dinit,
                                                          int batch, int H, int P, int N, int Q, int nc, int nsplit)
 {
     const int PN = P * N, Nh = N / nsplit;
@@ -200,7 +213,7 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
         for (int q = 0; q < 4; ++q) {
             const int n = n0 + q, k = n / Nh, j = n % Nh;
             GoutT_rev[((((int64_t)k * batch + b) * nc + cr) * H + h) * (int64_t)Nh * P + (int64_t)j * P + p] =
-                from_f32<T>(sv[q]);
+                from_f32<TD>(sv[q]);
         }
         const float4 gh = *reinterpret_cast<const float4*>(Ghat + ((b * nc + c) * H + h) * (int64_t)PN + e);
         const float dec = __expf(cs[(bh * nc + c) * Q + Q - 1]);
@@ -212,20 +225,60 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
     *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
 }
 
-// per (b, h): dx, ddt, and the per-(b, h) parts of dA and dD.  Threads take tokens from the end
-// (thread i of a block of 256 has token blk*256 + 255 - i), so a prefix sum over threads is the
-// suffix sum over tokens that the log-decay gradient needs.
-template <typename T>
-__global__ __launch_bounds__(kT) void bwd_tokens_kernel(const T* __restrict__ x, const float* __restrict__ dt,
-                                                        const float* __restrict__ A, const float* __restrict__ Dv,
-                                                        const T* __restrict__ dy, const float* __restrict__ yhat,
-                                                        const float* __restrict__ du_rev,
-                                                        const float* __restrict__ dfinal,
-                                                        const float* __restrict__ hfinal, T* __restrict__ dx,
-                                                        float* __restrict__ ddt, float* __restrict__ dAp,
-                                                        float* __restrict__ dDp, int64_t L, int H, int P, int N, int Q,
-                                                        int nc)
+// per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
+// gradients need: q = dy . yhat - dt x . du and x . du (into qx as (q, x.du)) and x . dy.
+// 16 lanes share a row (P / 16 values each), so a wavefront reads four whole rows per load.
+__global__ __launch_bounds__(kT) void bwd_rows_kernel(const float* __restrict__ x, const float* __restrict__ dt,
+                                                      const float* __restrict__ Dv, const float* __restrict__ dy,
+                                                      const float* __restrict__ yhat, const float* __restrict__ du_rev,
+                                                      float* __restrict__ dx, float2* __restrict__ qx,
+                                                      float* __restrict__ xdy_out, int64_t L, int H, int P, int Q, int nc)
 {
+    const int64_t Lp = (int64_t)nc * Q;
+    const int64_t b = blockIdx.y;                                // one grid row per batch row
+    const int sub = threadIdx.x & 15;
+    const int64_t step = (int64_t)gridDim.x * (kT / 16);
+    for (int64_t row = (int64_t)blockIdx.x * (kT / 16) + threadIdx.x / 16; row < L * H; row += step) {
+        const int h = (int)(row % H);
+        const int64_t t = row / H;
+        const int64_t r = (b * L + t) * H + h;
+        const int64_t tau = (int64_t)(nc - 1 - t / Q) * Q + (Q - 1 - t % Q);
+        const int64_t rr = (b * Lp + tau) * H + h;
+        const float dtv = dt[r], dh = Dv[h];
+        float dyy = 0.f, xdu = 0.f, xdy = 0.f;
+        for (int p = 4 * sub; p < P; p += 64) {
+            const float4 xv = *reinterpret_cast<const float4*>(x + r * P + p);
+            const float4 dv = *reinterpret_cast<const float4*>(dy + r * P + p);
+            const float4 yv = *reinterpret_cast<const float4*>(yhat + r * P + p);
+            const float4 uv = *reinterpret_cast<const float4*>(du_rev + rr * P + p);
+            dyy += dv.x * yv.x + dv.y * yv.y + dv.z * yv.z + dv.w * yv.w;
+            xdu += xv.x * uv.x + xv.y * uv.y + xv.z * uv.z + xv.w * uv.w;
+            xdy += xv.x * dv.x + xv.y * dv.y + xv.z * dv.z + xv.w * dv.w;
+            *reinterpret_cast<float4*>(dx + r * P + p) =
+                make_float4(fmaf(dtv, uv.x, dh * dv.x), fmaf(dtv, uv.y, dh * dv.y), fmaf(dtv, uv.z, dh * dv.z),
+                            fmaf(dtv, uv.w, dh * dv.w));
+        }
+        dyy = group_sum<16>(dyy);
+        xdu = group_sum<16>(xdu);
+        xdy = group_sum<16>(xdy);
+        if (sub == 0) {
+            qx[r] = make_float2(dyy - dtv * xdu, xdu);
+            xdy_out[r] = xdy;
+        }
+    }
+}
+
+// per (b, h): the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
+// and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.  Thread i takes the 16 tokens
+// ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.
+__global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dt, const float* __restrict__ A,
+                                                      const float2* __restrict__ qx, const float* __restrict__ xdy,
+                                                      const float* __restrict__ dfinal,
+                                                      const float* __restrict__ hfinal, float* __restrict__ ddt,
+                                                      float* __restrict__ dAp, float* __restrict__ dDp, int64_t L,
+                                                      int H, int P, int N)
+{
+    constexpr int kPer = 16;
     __shared__ float red[kT / kWave];
     const int h = blockIdx.x % H;
     const int64_t b = blockIdx.x / H;
@@ -241,51 +294,33 @@ __global__ __launch_bounds__(kT) void bwd_tokens_kernel(const T* __restrict__ x,
         for (int w = 0; w < kT / kWave; ++w) s += red[w];
         return s;
     };
-    // <dfinal, h_final>: the gradient every log-decay receives through the final state
     float fh = 0.f;
     if (dfinal) {
         const int64_t PN = (int64_t)P * N;
         for (int64_t i = tid; i < PN; i += kT) fh += dfinal[bh * PN + i] * hfinal[bh * PN + i];
     }
     float carry = block_sum(fh);
-    const float a = A[h], dh = Dv[h];
+    const float a = A[h];
     float dA_acc = 0.f, dD_acc = 0.f;
-    const int64_t Lp = (int64_t)nc * Q;
-    const int nblk = (int)((L + kT - 1) / kT);
-    for (int blk = nblk - 1; blk >= 0; --blk) {
-        const int64_t t = (int64_t)blk * kT + (kT - 1 - tid);
-        float q = 0.f, xdu = 0.f, dtv = 0.f;
-        if (t < L) {
-            const int64_t row = (b * L + t) * H + h;
-            const int64_t tau = (int64_t)(nc - 1 - t / Q) * Q + (Q - 1 - t % Q);
-            const int64_t rrow = (b * Lp + tau) * H + h;
-            dtv = dt[row];
-            float dyy = 0.f, xdy = 0.f;
-            for (int p0 = 0; p0 < P; p0 += 8) {
-                Vec8<T> xv, dv, o;
-                load8(xv, x + row * P + p0);
-                load8(dv, dy + row * P + p0);
-                const float4 y0 = *reinterpret_cast<const float4*>(yhat + row * P + p0);
-                const float4 y1 = *reinterpret_cast<const float4*>(yhat + row * P + p0 + 4);
-                const float4 u0 = *reinterpret_cast<const float4*>(du_rev + rrow * P + p0);
-                const float4 u1 = *reinterpret_cast<const float4*>(du_rev + rrow * P + p0 + 4);
-                const float yv[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
-                const float uv[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+    const int64_t span = (int64_t)kT * kPer;
+    for (int64_t hi = L; hi > 0; hi -= span) {
+        // this thread's tokens: [hi - kPer (tid + 1), hi - kPer tid), latest first
+        const int64_t t1 = hi - (int64_t)kPer * tid;
+        float qs[kPer], xs[kPer];
+        float own = 0.f;
 #pragma unroll
-                for (int k = 0; k < 8; ++k) {
-                    const float xf = xv.get(k), df = dv.get(k);
-                    dyy += df * yv[k];
-                    xdu += xf * uv[k];
-                    xdy += xf * df;
-                    o.set(k, fmaf(dtv, uv[k], dh * df));
-                }
-                store8(dx + row * P + p0, o);
+        for (int k = 0; k < kPer; ++k) {
+            const int64_t t = t1 - 1 - k;
+            float2 v = make_float2(0.f, 0.f);
+            if (t >= 0 && t < L) {
+                v = qx[(b * L + t) * H + h];
+                dD_acc += xdy[(b * L + t) * H + h];
             }
-            q = dyy - dtv * xdu;
-            dD_acc += xdy;
+            qs[k] = v.x;
+            xs[k] = v.y;
+            own += v.x;
         }
-        // suffix sum over tokens = prefix sum over threads, plus everything after this block
-        float incl = wave_inclusive_sum(q);
+        const float incl = wave_inclusive_sum(own);
         __syncthreads();
         if (lane == kWave - 1) red[wave] = incl;
         __syncthreads();
@@ -295,10 +330,16 @@ __global__ __launch_bounds__(kT) void bwd_tokens_kernel(const T* __restrict__ x,
             before += w < wave ? red[w] : 0.f;
             total += red[w];
         }
-        const float dl = carry + before + incl;
-        if (t < L) {
-            ddt[(b * L + t) * H + h] = fmaf(a, dl, xdu);
-            dA_acc += dtv * dl;
+        float run = carry + before + incl - own;           // everything after this thread's tokens
+#pragma unroll
+        for (int k = 0; k < kPer; ++k) {
+            const int64_t t = t1 - 1 - k;
+            run += qs[k];
+            if (t >= 0 && t < L) {
+                const int64_t r = (b * L + t) * H + h;
+                ddt[r] = fmaf(a, run, xs[k]);
+                dA_acc += dt[r] * run;
+            }
         }
         carry += total;
     }
@@ -365,7 +406,7 @@ unsigned grid_for(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<in
 
 }  // namespace
 
-BwdLayout bwd_layout(const Dims& d, int elem)
+BwdLayout bwd_layout(const Dims& d, int elemD)
 {
     BwdLayout w;
     const int64_t nc = d.nchunks(), Lp = nc * d.chunk;
@@ -381,37 +422,45 @@ BwdLayout bwd_layout(const Dims& d, int elem)
     w.dtp = take(tab);
     w.csp = take(tab);
     w.states = take(st * 4);
-    w.entry = take(st * elem);
-    w.SinT = take(st * elem);
-    w.Gout_rev = take(st * elem);
-    w.GoutT_rev = take(st * elem);
+    w.entry = take(st * 4);
+    w.SinT = take(st * elemD);
+    w.Gout_rev = take(st * 4);
+    w.GoutT_rev = take(st * elemD);
     w.hfinal = take(B * H * P * N * 4);
     w.yhat = take(B * d.seqlen * H * P * 4);
-    w.dy_rev = take(B * Lp * H * P * elem);
-    w.u_rev = take(B * Lp * H * P * elem);
-    w.B_rev = take(B * Lp * G * N * elem);
-    w.C_rev = take(B * Lp * G * N * elem);
-    w.Crep_rev = take(B * Lp * H * N * elem);
-    w.Brep = take(B * d.seqlen * H * N * elem);
+    w.dy_rev = take(B * Lp * H * P * 4);
+    w.B_rev = take(B * Lp * G * N * 4);
+    w.C_rev = take(B * Lp * G * N * 4);
+    w.dy_revD = take(B * Lp * H * P * elemD);
+    w.u_revD = take(B * Lp * H * P * elemD);
+    w.Crep_rev = take(B * Lp * H * N * elemD);
+    w.Brep = take(B * d.seqlen * H * N * elemD);
     w.du_rev = take(B * Lp * H * P * 4);
     w.dBh_rev = take(B * Lp * H * N * 4);
     w.dCh = take(B * d.seqlen * H * N * 4);
     w.zeros = take(std::max<int64_t>(H, 1) * 4);
+    w.qx = take(B * d.seqlen * H * 8);
+    w.xdy = take(B * d.seqlen * H * 4);
     w.dAp = take(B * H * 4);
     w.dDp = take(B * H * 4);
     w.total = std::max<size_t>(o, 256);
     return w;
 }
 
-template <typename T>
-hipError_t launch_backward(const T* x, const float* dt, const float* A, const T* Bm, const T* Cm, const float* D,
-                           const float* init, const T* dy, const float* dfinal, T* dx, float* ddt, float* dA, T* dB,
-                           T* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t s)
+namespace {
+
+// The pass on fp32 arrays (x, B, C, dy and the outputs dx, dB, dC), with the dB / dC passes'
+// operands in TD: x_d, dy_d are x, dy in TD (the caller's own arrays when TD is their type).
+template <typename TD>
+hipError_t run_backward(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                        const float* D, const float* init, const float* dy, const float* dfinal, const TD* x_d,
+                        const TD* dy_d, float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
+                        float* dinit, const Dims& d, void* workspace, hipStream_t s)
 {
-    const BwdLayout w = bwd_layout(d, (int)sizeof(T));
+    const BwdLayout w = bwd_layout(d, (int)sizeof(TD));
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-    auto TT = [&](size_t off) { return reinterpret_cast<T*>(ws + off); };
+    auto TT = [&](size_t off) { return reinterpret_cast<TD*>(ws + off); };
     const int nc = (int)d.nchunks(), Q = (int)d.chunk;
     const int B = (int)d.batch, H = (int)d.nheads, P = (int)d.headdim, N = (int)d.dstate, G = (int)d.ngroups;
     const int nsplit = N > 128 ? 2 : 1;
@@ -422,50 +471,57 @@ hipError_t launch_backward(const T* x, const float* dt, const float* A, const T*
     float* zeros = F(w.zeros);
     hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(kT), 0, s, zeros, (int64_t)H);
     SSD_TRY(hipGetLastError());
-    // forward recompute: chunk states, entry states (T), the final state, yhat = y - D x (fp32)
-    SSD_TRY(launch_chunk_state_cumsum<T>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
-    SSD_TRY(launch_state_passing<T>(F(w.states), F(w.cs), init, TT(w.entry), F(w.hfinal), d, s));
-    SSD_TRY(launch_chunk_scan_f32out<T>(x, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), zeros, F(w.yhat), d, s));
+    // forward recompute in fp32: chunk states, entry states, the final state, yhat = y - D x
+    SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
+    SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
+    SSD_TRY(launch_chunk_scan_f32out<float>(x, Bm, Cm, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
     // tables, adjoint chunk states (into the chunk-state buffer, free again), adjoint passing
     const int64_t nrows = (int64_t)B * H * nc;
     hipLaunchKernelGGL(bwd_tables_kernel, dim3(grid_for(nrows * Q)), dim3(kT), 0, s, F(w.cs), F(w.W), F(w.Z), F(w.dtp),
                        F(w.csp), nrows, (int)L, Q, nc);
     SSD_TRY(hipGetLastError());
-    SSD_TRY(launch_chunk_state<T>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
-    hipLaunchKernelGGL((bwd_passing_kernel<T>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
-                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, TT(w.Gout_rev), TT(w.GoutT_rev),
+    SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
+    hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
+                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, F(w.Gout_rev), TT(w.GoutT_rev),
                        dinit, B, H, P, N, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)nsplit * B * Lp * H * (Nh / 8));
-    hipLaunchKernelGGL((bwd_prep_kernel<T>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, TT(w.dy_rev),
-                       TT(w.B_rev), TT(w.C_rev), TT(w.u_rev), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q, H, P, N, G,
-                       nsplit);
+    hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, F(w.dy_rev),
+                       F(w.B_rev), F(w.C_rev), TT(w.dy_revD), TT(w.u_revD), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q,
+                       H, P, N, G, nsplit);
     SSD_TRY(hipGetLastError());
-    hipLaunchKernelGGL((bwd_transpose_kernel<T>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
-                       TT(w.entry), TT(w.SinT), nrows, P, N, nsplit);
+    hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
+                       F(w.entry), TT(w.SinT), nrows, P, N, nsplit);
     SSD_TRY(hipGetLastError());
-    // du: the adjoint readout, on the reversed sequence
+    // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
-    SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.dy_rev), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev),
-                                        zeros, F(w.du_rev), dr, s));
+    SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp), F(w.Gout_rev),
+                                            zeros, F(w.du_rev), dr, s));
     // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half
     const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     const Dims dcd{d.batch, L, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     for (int k = 0; k < nsplit; ++k) {
-        SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.Crep_rev) + (int64_t)k * B * Lp * H * Nh, TT(w.dy_rev),
-                                            TT(w.u_rev), F(w.dtp), F(w.csp),
-                                            TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P, zeros,
-                                            F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
-        SSD_TRY(launch_chunk_scan_f32out<T>(TT(w.Brep) + (int64_t)k * B * L * H * Nh, x, dy, F(w.dtc), F(w.cs),
-                                            TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
-                                            F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
+        SSD_TRY(launch_chunk_scan_f32out<TD>(TT(w.Crep_rev) + (int64_t)k * B * Lp * H * Nh, TT(w.dy_revD),
+                                             TT(w.u_revD), F(w.dtp), F(w.csp),
+                                             TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P, zeros,
+                                             F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
+        SSD_TRY(launch_chunk_scan_f32out<TD>(TT(w.Brep) + (int64_t)k * B * L * H * Nh, x_d, dy_d, F(w.dtc), F(w.cs),
+                                             TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
+                                             F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
     }
-    // per token, then the group and batch sums
-    hipLaunchKernelGGL((bwd_tokens_kernel<T>), dim3((unsigned)(B * H)), dim3(kT), 0, s, x, dt, A, D, dy, F(w.yhat),
-                       F(w.du_rev), dfinal, F(w.hfinal), dx, ddt, F(w.dAp), F(w.dDp), L, H, P, N, Q, nc);
-    SSD_TRY(hipGetLastError());
-    hipLaunchKernelGGL((bwd_group_sum_kernel<T>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
+    // per token (all rows in parallel), then the suffix sums per (b, h), then the group and batch sums
+    {
+        float2* qx = reinterpret_cast<float2*>(F(w.qx));
+        float* xdy = F(w.xdy);
+        hipLaunchKernelGGL(bwd_rows_kernel, dim3(grid_for(L * H * 16), (unsigned)B), dim3(kT), 0, s, x, dt, D, dy,
+                           F(w.yhat), F(w.du_rev), dx, qx, xdy, L, H, P, Q, nc);
+        SSD_TRY(hipGetLastError());
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, qx, xdy, dfinal,
+                           F(w.hfinal), ddt, F(w.dAp), F(w.dDp), L, H, P, N);
+        SSD_TRY(hipGetLastError());
+    }
+    hipLaunchKernelGGL((bwd_group_sum_kernel<float>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
                        F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, F(w.dAp), F(w.dDp), dA, dD, B, H);
@@ -473,8 +529,6 @@ hipError_t launch_backward(const T* x, const float* dt, const float* A, const T*
 #undef SSD_TRY
     return hipSuccess;
 }
-
-namespace {
 
 __global__ __launch_bounds__(kT) void widen_kernel(const bf16* __restrict__ src, float* __restrict__ dst, int64_t n8)
 {
@@ -500,15 +554,25 @@ __global__ __launch_bounds__(kT) void narrow_kernel(const float* __restrict__ sr
     }
 }
 
+size_t up256(int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); }
+
 }  // namespace
 
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs)
 {
-    const size_t base = bwd_layout(d, 4).total;
+    const size_t base = bwd_layout(d, bf16_inputs ? 2 : 4).total;
     if (!bf16_inputs) return base;
     const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
-    auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
-    return base + 3 * up(nx * 4) + 4 * up(nb * 4);       // x, dy, dx and B, C, dB, dC in fp32
+    return base + 3 * up256(nx * 4) + 4 * up256(nb * 4);      // x, dy, dx and B, C, dB, dC in fp32
+}
+
+hipError_t launch_backward_f32(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
+                               const float* D, const float* init, const float* dy, const float* dfinal, float* dx,
+                               float* ddt, float* dA, float* dB, float* dC, float* dD, float* dinit, const Dims& d,
+                               void* workspace, hipStream_t s)
+{
+    return run_backward<float>(x, dt, A, Bm, Cm, D, init, dy, dfinal, x, dy, dx, ddt, dA, dB, dC, dD, dinit, d,
+                               workspace, s);
 }
 
 hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* Bm, const bf16* Cm,
@@ -517,14 +581,13 @@ hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, 
                                 void* workspace, hipStream_t s)
 {
     const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
-    auto up = [](int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); };
-    unsigned char* p = static_cast<unsigned char*>(workspace) + bwd_layout(d, 4).total;
-    float* x32 = reinterpret_cast<float*>(p);  p += up(nx * 4);
-    float* dy32 = reinterpret_cast<float*>(p); p += up(nx * 4);
-    float* dx32 = reinterpret_cast<float*>(p); p += up(nx * 4);
-    float* B32 = reinterpret_cast<float*>(p);  p += up(nb * 4);
-    float* C32 = reinterpret_cast<float*>(p);  p += up(nb * 4);
-    float* dB32 = reinterpret_cast<float*>(p); p += up(nb * 4);
+    unsigned char* p = static_cast<unsigned char*>(workspace) + bwd_layout(d, 2).total;
+    float* x32 = reinterpret_cast<float*>(p);  p += up256(nx * 4);
+    float* dy32 = reinterpret_cast<float*>(p); p += up256(nx * 4);
+    float* dx32 = reinterpret_cast<float*>(p); p += up256(nx * 4);
+    float* B32 = reinterpret_cast<float*>(p);  p += up256(nb * 4);
+    float* C32 = reinterpret_cast<float*>(p);  p += up256(nb * 4);
+    float* dB32 = reinterpret_cast<float*>(p); p += up256(nb * 4);
     float* dC32 = reinterpret_cast<float*>(p);
     // element counts are multiples of 8 (headdim and dstate are multiples of 16)
     hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, x, x32, nx / 8);
@@ -533,17 +596,13 @@ hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, 
     hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Cm, C32, nb / 8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_backward<float>(x32, dt, A, B32, C32, D, init, dy32, dfinal, dx32, ddt, dA, dB32, dC32, dD, dinit, d,
-                               workspace, s);
+    e = run_backward<bf16>(x32, dt, A, B32, C32, D, init, dy32, dfinal, x, dy, dx32, ddt, dA, dB32, dC32, dD, dinit, d,
+                           workspace, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dx32, dx, nx / 8);
     hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dB32, dB, nb / 8);
     hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dC32, dC, nb / 8);
     return hipGetLastError();
 }
-
-template hipError_t launch_backward<float>(const float*, const float*, const float*, const float*, const float*,
-                                           const float*, const float*, const float*, const float*, float*, float*,
-                                           float*, float*, float*, float*, float*, const Dims&, void*, hipStream_t);
 
 }  // namespace ssd

@@ -69,20 +69,21 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
     size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, u_rev, B_rev,
-        C_rev, Crep_rev, Brep, du_rev, dBh_rev, dCh, zeros, dAp, dDp, total;
+        C_rev, dy_revD, u_revD, Crep_rev, Brep, du_rev, dBh_rev, dCh, zeros, qx, xdy, dAp, dDp, total;
 };
 BwdLayout bwd_layout(const Dims& d, int elem_bytes);
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
 
-// bf16 inputs: widened to fp32, the fp32 pass, dx / dB / dC rounded back (see bwd.hip)
+// bf16 inputs: widened to fp32 for the precision-critical parts, the dB / dC passes on the bf16
+// operands, dx / dB / dC rounded back once (see bwd.hip)
 hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* B, const bf16* C,
                                 const float* D, const float* init, const bf16* dy, const float* dfinal, bf16* dx,
                                 float* ddt, float* dA, bf16* dB, bf16* dC, float* dD, float* dinit, const Dims& d,
                                 void* workspace, hipStream_t stream);
 
-template <typename T>
-hipError_t launch_backward(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
-                           const float* init, const T* dy, const float* dfinal, T* dx, float* ddt, float* dA, T* dB,
-                           T* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t stream);
+hipError_t launch_backward_f32(const float* x, const float* dt, const float* A, const float* B, const float* C,
+                               const float* D, const float* init, const float* dy, const float* dfinal, float* dx,
+                               float* ddt, float* dA, float* dB, float* dC, float* dD, float* dinit, const Dims& d,
+                               void* workspace, hipStream_t stream);
 
 }  // namespace ssd

@@ -437,9 +437,9 @@ int ssd_backward(const void* x, const float* dt, const float* A, const void* B, 
         return hip_status(ssd::launch_backward_bf16((const bf16*)x, dt, A, (const bf16*)B, (const bf16*)C, D,
                                                     init_states, (const bf16*)dy, dfinal, (bf16*)dx, ddt, dA,
                                                     (bf16*)dB, (bf16*)dC, dD, dinit, d, workspace, s));
-    return hip_status(ssd::launch_backward<float>((const float*)x, dt, A, (const float*)B, (const float*)C, D,
-                                                  init_states, (const float*)dy, dfinal, (float*)dx, ddt, dA,
-                                                  (float*)dB, (float*)dC, dD, dinit, d, workspace, s));
+    return hip_status(ssd::launch_backward_f32((const float*)x, dt, A, (const float*)B, (const float*)C, D,
+                                               init_states, (const float*)dy, dfinal, (float*)dx, ddt, dA,
+                                               (float*)dB, (float*)dC, dD, dinit, d, workspace, s));
 }
 
 int ssd_step(float* state, const void* x, const float* dt, const float* A, const void* B,

@@ -174,7 +174,7 @@ def test_backward_rejects():
     assert call(dy=None) == ERR_NULL
     assert call(ws_bytes=1000) == ERR_WS
     assert call(dx=fake(1)) == ERR_ALIAS
-    assert call(batch=0) if False else call(b=0) == OK
+    assert call(b=0) == OK                           # nothing to do, nothing enqueued
 
 
 def test_selective_scan_rejects():
