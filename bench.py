@@ -48,6 +48,8 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-scan", action="store_true", help="skip the Mamba-1 selective-scan comparison leg")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
+    ap.add_argument("--backward-calls", type=int, default=20)
     ap.add_argument("--scan-calls", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (scale for HBM byte counters) and exit")
@@ -330,6 +332,42 @@ def main():
         print(f"[bench] varlen forward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del vx, vdt, vB, vC, vy, vws
 
+    # ---- the backward pass on the same workload (gradients of every input; dL/dy drawn on the device)
+    bwd = None
+    if not args.no_backward:
+        g = torch.Generator(device=dev)
+        g.manual_seed(7)
+        dyb = torch.randn(x.shape, generator=g, device=dev).to(x.dtype)
+        bws_bytes = lib.ssd_backward_workspace_bytes(b, L, H, P, N, G, Q, code)
+        bws = torch.empty(bws_bytes, dtype=torch.uint8, device=dev)
+        gx, gB, gC = torch.empty_like(x), torch.empty_like(B), torch.empty_like(C)
+        gdt = torch.empty_like(dt)
+        gA, gD = torch.empty_like(A), torch.empty_like(D)
+        ginit = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+
+        def bwd_call():
+            rc = lib.ssd_backward(p(x), p(dt), p(A), p(B), p(C), p(D), p(init), p(dyb), None, p(gx), p(gdt), p(gA),
+                                  p(gB), p(gC), p(gD), p(ginit), b, L, H, P, N, G, Q, code, p(bws), bws_bytes, sp)
+            if rc:
+                raise ssd.SSDError("ssd_backward", rc)
+
+        for _ in range(3):
+            bwd_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.backward_calls):
+            bwd_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / args.backward_calls
+        bwd = dict(workload=f"{args.workload} backward: dx, ddt, dA, dB, dC, dD, dinit for a random dL/dy",
+                   calls=args.backward_calls, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
+                   time_over_forward=round(us / (ms_per_step * 1e3), 2),
+                   note="bf16 inputs are widened to fp32 for the decay-gradient path (see the library header)")
+        print(f"[bench] backward: {us:.1f} us/call", file=sys.stderr, flush=True)
+        del dyb, bws, gx, gB, gC
+
     # ---- the Mamba-1 selective scan at the same layer width (for the SSD-vs-scan comparison)
     scan = None
     if not args.no_scan:
@@ -405,6 +443,7 @@ def main():
         "kernels_note": "the stage entry points timed one by one; inside ssd_forward stage 1 runs in the prologue "
                         "of the stage-2 kernel, so the forward launches three kernels",
         "ssd_step": decode,
+        "backward": bwd,
         "varlen": varlen,
         "selective_scan": scan,
         "cpu_baseline": cpu,

@@ -270,44 +270,52 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const float* __restrict__ 
 
 // per (b, h): the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
 // and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.  Thread i takes the 16 tokens
-// ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.
+// ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.  The sums
+// run in fp64: dA adds up terms that cancel to a few parts in a thousand of their magnitude.
 __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dt, const float* __restrict__ A,
                                                       const float2* __restrict__ qx, const float* __restrict__ xdy,
                                                       const float* __restrict__ dfinal,
                                                       const float* __restrict__ hfinal, float* __restrict__ ddt,
-                                                      float* __restrict__ dAp, float* __restrict__ dDp, int64_t L,
+                                                      double* __restrict__ dAp, double* __restrict__ dDp, int64_t L,
                                                       int H, int P, int N)
 {
     constexpr int kPer = 16;
-    __shared__ float red[kT / kWave];
+    __shared__ double sc[kT];
     const int h = blockIdx.x % H;
     const int64_t b = blockIdx.x / H;
     const int64_t bh = b * H + h;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    auto block_sum = [&](float v) {
-        v = group_sum<kWave>(v);
+    const int tid = threadIdx.x;
+    // inclusive prefix sum over the block's threads, in fp64 (Hillis-Steele in LDS)
+    auto block_scan = [&](double v) {
         __syncthreads();
-        if (lane == 0) red[wave] = v;
+        sc[tid] = v;
         __syncthreads();
-        float s = 0.f;
-#pragma unroll
-        for (int w = 0; w < kT / kWave; ++w) s += red[w];
-        return s;
+        for (int off = 1; off < kT; off <<= 1) {
+            const double o = tid >= off ? sc[tid - off] : 0.0;
+            __syncthreads();
+            sc[tid] += o;
+            __syncthreads();
+        }
+        return sc[tid];
     };
-    float fh = 0.f;
+    auto block_sum = [&](double v) {
+        block_scan(v);
+        return sc[kT - 1];
+    };
+    double fh = 0.0;
     if (dfinal) {
         const int64_t PN = (int64_t)P * N;
-        for (int64_t i = tid; i < PN; i += kT) fh += dfinal[bh * PN + i] * hfinal[bh * PN + i];
+        for (int64_t i = tid; i < PN; i += kT) fh += (double)dfinal[bh * PN + i] * hfinal[bh * PN + i];
     }
-    float carry = block_sum(fh);
-    const float a = A[h];
-    float dA_acc = 0.f, dD_acc = 0.f;
+    double carry = block_sum(fh);
+    const double a = A[h];
+    double dA_acc = 0.0, dD_acc = 0.0;
     const int64_t span = (int64_t)kT * kPer;
     for (int64_t hi = L; hi > 0; hi -= span) {
         // this thread's tokens: [hi - kPer (tid + 1), hi - kPer tid), latest first
         const int64_t t1 = hi - (int64_t)kPer * tid;
         float qs[kPer], xs[kPer];
-        float own = 0.f;
+        double own = 0.0;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
@@ -320,31 +328,23 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
             xs[k] = v.y;
             own += v.x;
         }
-        const float incl = wave_inclusive_sum(own);
-        __syncthreads();
-        if (lane == kWave - 1) red[wave] = incl;
-        __syncthreads();
-        float before = 0.f, total = 0.f;
-#pragma unroll
-        for (int w = 0; w < kT / kWave; ++w) {
-            before += w < wave ? red[w] : 0.f;
-            total += red[w];
-        }
-        float run = carry + before + incl - own;           // everything after this thread's tokens
+        const double incl = block_scan(own);
+        const double total = sc[kT - 1];
+        double run = carry + incl - own;                    // everything after this thread's tokens
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
             run += qs[k];
             if (t >= 0 && t < L) {
                 const int64_t r = (b * L + t) * H + h;
-                ddt[r] = fmaf(a, run, xs[k]);
-                dA_acc += dt[r] * run;
+                ddt[r] = (float)(a * run + xs[k]);
+                dA_acc += (double)dt[r] * run;
             }
         }
         carry += total;
     }
-    const float sa = block_sum(dA_acc);
-    const float sd = block_sum(dD_acc);
+    const double sa = block_sum(dA_acc);
+    const double sd = block_sum(dD_acc);
     if (tid == 0) {
         dAp[bh] = sa;
         dDp[bh] = sd;
@@ -383,17 +383,17 @@ __global__ __launch_bounds__(kT) void bwd_group_sum_kernel(const float* __restri
     }
 }
 
-__global__ __launch_bounds__(kT) void bwd_heads_kernel(const float* __restrict__ dAp, const float* __restrict__ dDp,
+__global__ __launch_bounds__(kT) void bwd_heads_kernel(const double* __restrict__ dAp, const double* __restrict__ dDp,
                                                        float* __restrict__ dA, float* __restrict__ dD, int batch, int H)
 {
     for (int h = blockIdx.x * kT + threadIdx.x; h < H; h += gridDim.x * kT) {
-        float sa = 0.f, sd = 0.f;
+        double sa = 0.0, sd = 0.0;
         for (int b = 0; b < batch; ++b) {
             sa += dAp[(int64_t)b * H + h];
             sd += dDp[(int64_t)b * H + h];
         }
-        dA[h] = sa;
-        dD[h] = sd;
+        dA[h] = (float)sa;
+        dD[h] = (float)sd;
     }
 }
 
@@ -441,8 +441,8 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.zeros = take(std::max<int64_t>(H, 1) * 4);
     w.qx = take(B * d.seqlen * H * 8);
     w.xdy = take(B * d.seqlen * H * 4);
-    w.dAp = take(B * H * 4);
-    w.dDp = take(B * H * 4);
+    w.dAp = take(B * H * 8);
+    w.dDp = take(B * H * 8);
     w.total = std::max<size_t>(o, 256);
     return w;
 }
@@ -518,13 +518,15 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
                            F(w.yhat), F(w.du_rev), dx, qx, xdy, L, H, P, Q, nc);
         SSD_TRY(hipGetLastError());
         hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, qx, xdy, dfinal,
-                           F(w.hfinal), ddt, F(w.dAp), F(w.dDp), L, H, P, N);
+                           F(w.hfinal), ddt, reinterpret_cast<double*>(ws + w.dAp), reinterpret_cast<double*>(ws + w.dDp), L,
+                           H, P, N);
         SSD_TRY(hipGetLastError());
     }
     hipLaunchKernelGGL((bwd_group_sum_kernel<float>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
                        F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
-    hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, F(w.dAp), F(w.dDp), dA, dD, B, H);
+    hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, reinterpret_cast<double*>(ws + w.dAp),
+                       reinterpret_cast<double*>(ws + w.dDp), dA, dD, B, H);
     SSD_TRY(hipGetLastError());
 #undef SSD_TRY
     return hipSuccess;

@@ -64,7 +64,7 @@ def _bind(lib):
     lib.ssd_oracle_step.restype = ctypes.c_int
     lib.ssd_oracle_step.argtypes = [_dp] * 8 + [_i64] * 5 + [ctypes.c_int]
     lib.ssd_oracle_backward.restype = ctypes.c_int
-    lib.ssd_oracle_backward.argtypes = [_dp] * 16 + [_i64] * 6 + [ctypes.c_int]
+    lib.ssd_oracle_backward.argtypes = [_dp] * 17 + [_i64] * 6 + [ctypes.c_int]
     lib.ssd_oracle_selective_scan.restype = ctypes.c_int
     lib.ssd_oracle_selective_scan.argtypes = [_dp] * 9 + [_i64] * 4 + [ctypes.c_int]
     lib.ssd_oracle_max_threads.restype = ctypes.c_int
@@ -150,17 +150,19 @@ def backward(x, dt, A, B, C, D, init, dy, dfinal=None, nthreads: int = 0, lib=No
 
     Shapes as in ``forward`` (dy like x, dfinal like init).  Returns a dict with dx, ddt, dA, dB,
     dC, dD and dinit (dinit is returned even when init is None: the gradient w.r.t. a zero
-    initial state)."""
+    initial state), and dA_scale: per head the size of the per-token products dA is formed from
+    in a chunked pass, sum_t T_t (sum_p |dy yhat| + sum_p |u du|) with T_t the prefix sum of dt
+    (dA's terms cancel strongly, so its errors are measured against this scale)."""
     x, dt, A, B, C, D, init, dy, dfinal = (_f64(a) for a in (x, dt, A, B, C, D, init, dy, dfinal))
     b, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     assert dy.shape == x.shape and (dfinal is None or dfinal.shape == (b, H, P, N))
     out = dict(dx=np.empty((b, L, H, P)), ddt=np.empty((b, L, H)), dA=np.empty(H), dB=np.empty((b, L, G, N)),
-               dC=np.empty((b, L, G, N)), dD=np.empty(H), dinit=np.empty((b, H, P, N)))
+               dC=np.empty((b, L, G, N)), dD=np.empty(H), dinit=np.empty((b, H, P, N)), dA_scale=np.empty(H))
     rc = (lib or _load()).ssd_oracle_backward(
         _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init), _ptr(dy), _ptr(dfinal),
         _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]), _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]),
-        _ptr(out["dinit"]), b, L, H, P, N, G, int(nthreads))
+        _ptr(out["dinit"]), _ptr(out["dA_scale"]), b, L, H, P, N, G, int(nthreads))
     if rc != 0:
         raise ValueError("ssd_oracle_backward rejected its arguments")
     return out

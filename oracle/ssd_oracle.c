@@ -156,11 +156,16 @@ int ssd_oracle_step(double* state, const double* x, const double* dt, const doub
  *
  * Every state h_t of one (b, h) is kept (L x P x N doubles), so this is for test sizes.
  * Per-head parts of dB and dC are summed over the group at the end. */
+/* dA_scale[h]: the size of what dA is computed from when it is formed, as a chunked pass does, from
+ * suffix sums over tokens of q_t = dy_t . yhat_t - u_t . du_t (yhat = y - D x): an error in q_t
+ * reaches dA weighted by T_t = sum_{t' <= t} dt_t', so the scale is
+ * sum over (b, t) of T_t (sum_p |dy_t[p] yhat_t[p]| + sum_p |u_t[p] du_t[p]|).  dA's terms cancel
+ * strongly, so its errors are measured against this scale.  May be NULL. */
 int ssd_oracle_backward(const double* x, const double* dt, const double* A, const double* Bm, const double* Cm,
                         const double* D, const double* init, const double* dy, const double* dfinal, double* dx,
-                        double* ddt, double* dA, double* dB, double* dC, double* dD, double* dinit, int64_t batch,
-                        int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                        int nthreads)
+                        double* ddt, double* dA, double* dB, double* dC, double* dD, double* dinit,
+                        double* dA_scale, int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                        int64_t dstate, int64_t ngroups, int nthreads)
 {
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 ||
         nheads % ngroups != 0)
@@ -172,7 +177,11 @@ int ssd_oracle_backward(const double* x, const double* dt, const double* A, cons
     double* dCh = (double*)calloc((size_t)(batch * L * nheads * N) + 1, sizeof(double));
     double* dAbh = (double*)calloc((size_t)(batch * nheads) + 1, sizeof(double));
     double* dDbh = (double*)calloc((size_t)(batch * nheads) + 1, sizeof(double));
-    if (!dBh || !dCh || !dAbh || !dDbh) { free(dBh); free(dCh); free(dAbh); free(dDbh); return -2; }
+    double* dSbh = (double*)calloc((size_t)(batch * nheads) + 1, sizeof(double));
+    if (!dBh || !dCh || !dAbh || !dDbh || !dSbh) {
+        free(dBh); free(dCh); free(dAbh); free(dDbh); free(dSbh);
+        return -2;
+    }
 #ifdef _OPENMP
     if (nthreads > 0) omp_set_num_threads(nthreads);
 #else
@@ -195,7 +204,7 @@ int ssd_oracle_backward(const double* x, const double* dt, const double* A, cons
             }
         }
         for (int64_t i = 0; i < PN; ++i) gs[i] = dfinal ? dfinal[bh * PN + i] : 0.0;
-        double dA_acc = 0.0, dD_acc = 0.0;
+        double dA_acc = 0.0, dD_acc = 0.0, dS_acc = 0.0;
         for (int64_t t = L - 1; t >= 0; --t) {
             const int64_t bt = b * L + t;
             const double dtv = dt[bt * nheads + h];
@@ -227,6 +236,16 @@ int ssd_oracle_backward(const double* x, const double* dt, const double* A, cons
             for (int64_t i = 0; i < PN; ++i) da += gs[i] * hs[t * PN + i];
             ddt[bt * nheads + h] = xdu + A[h] * a * da;
             dA_acc += dtv * a * da;
+            {
+                double T = 0.0, mag = 0.0;
+                for (int64_t j = 0; j <= t; ++j) T += dt[(b * L + j) * nheads + h];
+                for (int64_t p = 0; p < P; ++p) {
+                    double yh = 0.0;
+                    for (int64_t n = 0; n < N; ++n) yh += hs[(t + 1) * PN + p * N + n] * Ct[n];
+                    mag += fabs(dyt[p] * yh) + fabs(dtv * xt[p] * du[p]);
+                }
+                dS_acc += T * mag;
+            }
             dD_acc += xdy;
             for (int64_t i = 0; i < PN; ++i) gs[i] *= a;
         }
@@ -234,15 +253,21 @@ int ssd_oracle_backward(const double* x, const double* dt, const double* A, cons
             for (int64_t i = 0; i < PN; ++i) dinit[bh * PN + i] = gs[i];
         dAbh[bh] = dA_acc;
         dDbh[bh] = dD_acc;
+        dSbh[bh] = dS_acc;
         free(hs);
         free(gs);
         free(du);
     }
     for (int64_t h = 0; h < nheads; ++h) {
-        double sa = 0.0, sd = 0.0;
-        for (int64_t b = 0; b < batch; ++b) { sa += dAbh[b * nheads + h]; sd += dDbh[b * nheads + h]; }
+        double sa = 0.0, sd = 0.0, ss = 0.0;
+        for (int64_t b = 0; b < batch; ++b) {
+            sa += dAbh[b * nheads + h];
+            sd += dDbh[b * nheads + h];
+            ss += dSbh[b * nheads + h];
+        }
         dA[h] = sa;
         dD[h] = sd;
+        if (dA_scale) dA_scale[h] = ss;
     }
     for (int64_t bt = 0; bt < batch * L; ++bt)
         for (int64_t g = 0; g < ngroups; ++g)
@@ -259,6 +284,7 @@ int ssd_oracle_backward(const double* x, const double* dt, const double* A, cons
     free(dCh);
     free(dAbh);
     free(dDbh);
+    free(dSbh);
     return 0;
 }
 

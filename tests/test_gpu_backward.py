@@ -54,7 +54,9 @@ def test_backward_matches_oracle(c):
     assert slice_rel_err(g["dB"], r["dB"], 2) <= tol, "dB"
     assert slice_rel_err(g["dC"], r["dC"], 2) <= tol, "dC"
     assert slice_rel_err(g["dinit"], r["dinit"], 1) <= tol, "dinit"
-    assert _rel_all(g["dA"], r["dA"]) <= tol, "dA"
+    # dA adds up per-token terms that cancel to ~1e-3 of their size: its error is measured against
+    # the size of the products it is formed from (the pass computes it in fp32 for both input types)
+    assert np.max(np.abs(g["dA"] - r["dA"]) / r["dA_scale"]) <= 1e-5, "dA"
     assert _rel_all(g["dD"], r["dD"]) <= tol, "dD"
 
 
