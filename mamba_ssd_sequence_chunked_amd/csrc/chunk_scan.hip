@@ -19,12 +19,17 @@
 // S_in C^T), so a lane holds 4 consecutive head-dimension values of one row:
 //   * C rows of a wavefront are read once from global memory straight into
 //     operand fragments (the state axis is contiguous, and it is the
-//     contraction axis of both C.B^T and S_in.C^T) and kept in registers.
+//     contraction axis of both C.B^T and S_in.C^T) through range-checked
+//     buffer loads (rows past the sequence read as zero) and kept in
+//     registers.  They are issued first, and the per-head decay tables come
+//     by asynchronous copies right after, so that the prologue is one round
+//     trip to memory: no wait for a register load also waits for the copies.
 //   * the heads' S_in tiles (in slabs of 32 state columns) and the source
 //     tokens' x and B tiles reach LDS through asynchronous global->LDS
-//     copies; source tokens stream through a 2-deep ring of 32-token stages,
-//     the next stage in flight while the current one is multiplied, and
-//     every byte of x, B and S_in is read once per workgroup.  Tiles are
+//     copies.  Slabs are double-buffered (odd slabs in the ring slot that the
+//     source tokens use last), source tokens stream through a 2-deep ring of
+//     32-token stages, the next stage in flight while the current one is
+//     multiplied, and every byte of x, B and S_in is read once per workgroup.  Tiles are
 //     XOR-swizzled by 16-byte chunk, so the 16-byte operand reads and the
 //     transpose reads (x is kept token-major and read token-wise with
 //     ds_read_b64_tr_b16) are bank-conflict free.  Rows past the sequence
@@ -130,8 +135,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
-    __shared__ float cst[HB * kMaxQ];
-    __shared__ float dtt[HB * kMaxQ];
+    __shared__ __attribute__((aligned(16))) float cst[HB * kMaxQ];
+    __shared__ __attribute__((aligned(16))) float dtt[HB * kMaxQ];
     __shared__ float vst[HB * kMaxQ];          // exp(cs[e(s)] - cs[s]) dt[s], e(s) = last token of s's stage
     __shared__ int lst[kVarlen ? kMaxQ : 1];   // first token of each token's sequence, chunk-relative
     __shared__ __attribute__((aligned(1024))) unsigned char region[S::region];
@@ -162,14 +167,49 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const int rbk[2] = {pair, nrb - 1 - pair};
     const bool has[2] = {2 * pair < nrb, 2 * pair < nrb - 1};
 
-    // ---- asynchronous copies: the heads' S_in tiles (first slab), then the first stages of the ring
+    // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots),
+    // by range-checked buffer loads (rows past the chunk's tokens and missing blocks read as zero).
+    // Issued first: no later wait for them then also waits for the asynchronous copies below.
+    Vec8<T> cf[2][S::NP / 32];
+    {
+        const T* cb = Cm + ((b * seqlen + t0) * ngroups + g) * (int64_t)N;
+        const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(cb), 0, ((len - 1) * ngroups + 1) * N * (int)sizeof(T), kBufferDword3);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int l = 16 * rbk[j] + r16;
+            const bool rok = has[j] && l < len;
+#pragma unroll
+            for (int ks = 0; ks < NK; ++ks) {
+                const int col = 32 * ks + 8 * grp;
+                buffer_load8(cf[j][ks], crs, rok && col < N ? (l * ngroups * N + col) * (int)sizeof(T) : kDropped);
+            }
+        }
+    }
+    // ---- decay tables by asynchronous copies: per head, the chunk's Q cumulative log-decays and dt
+    // values (contiguous), one wavefront instruction each.  Heads past the workgroup copy its last head
+    // (computed on, never stored); slots past Q repeat the row's last values (never used unmasked).
+    const int wu = __builtin_amdgcn_readfirstlane(wave);           // (wave-uniform, and known to be)
+#pragma unroll
+    for (int k = 0; k < (2 * HB + kWaves - 1) / kWaves; ++k) {
+        const int q = wu + k * kWaves;
+        if (q >= 2 * HB) break;
+        const int hh = q >> 1;
+        const float* row = ((q & 1) ? dt_chunked : dA_cs) + (((int64_t)b * nheads + h0 + min(hh, nh - 1)) * nc + c) * Q;
+        dma16(row + min(4 * lane, Q - 4), ((q & 1) ? lds_addr(dtt) : lds_addr(cst)) + hh * (kMaxQ * 4));
+    }
+
+    // ---- then the heads' S_in tiles (first two slabs) and the first stages of the ring
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
+    // slab buffers: even slabs in the slab area, odd slabs in the last ring slot (free until the stage loop)
+    auto sbuf = [&](int sl) -> unsigned char* { return (sl & 1) ? region + (kStages - 1) * S::stage_bytes : stile; };
     auto issue_s = [&](int sl) {
-        tiles_load_async<S::S_CH, P, HB, kWaves>(lds_addr(region) + S::ring_bytes, S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
+        tiles_load_async<S::S_CH, P, HB, kWaves>(lds_addr(region) + ((sl & 1) ? (kStages - 1) * S::stage_bytes : S::ring_bytes), S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
             return ent + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N + min(sl * SW + ch * EPC, N - EPC);
         });
     };
     issue_s(0);
+    if (S::NSL > 1) issue_s(1);
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
         const unsigned stg = lds_addr(region) + (sb % kStages) * S::stage_bytes;
@@ -189,29 +229,16 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     float dsk[HB];                                                  // skip weights D of the heads
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh) dsk[hh] = Dv[h0 + min(hh, nh - 1)];
-
-    // ---- decay tables
-    for (int i = tid; i < HB * kMaxQ; i += kThreads) {
-        const int hh = i / kMaxQ, l = i % kMaxQ;
-        const int64_t o = (((int64_t)b * nheads + h0 + min(hh, nh - 1)) * nc + c) * Q + min(l, Q - 1);
-        const float cv = dA_cs[o], dv = dt_chunked[o];
-        const bool ok = hh < nh && l < Q;
-        cst[i] = select(ok, cv, 0.f);
-        dtt[i] = select(ok, dv, 0.f);
-    }
     if constexpr (kVarlen) {
         for (int l = tid; l < kMaxQ; l += kThreads) lst[l] = tstart[t0 + min(l, len - 1)] - (int)t0;
     }
-    // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots)
-    Vec8<T> cf[2][S::NP / 32];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int l = 16 * rbk[j] + r16;
-        const T* crow = Cm + ((b * seqlen + t0 + max(0, min(l, len - 1))) * ngroups + g) * N;
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) load8(cf[j][ks], crow + min(32 * ks + 8 * grp, N - 8));
-#pragma unroll
-        for (int ks = 0; ks < NK; ++ks) cf[j][ks] = masked(cf[j][ks], has[j] && l < len && 32 * ks + 8 * grp < N);
+    // the tables have landed once only the copies issued after them may still fly
+    constexpr int kAfter = (1 + (S::NSL > 1)) * (HB * P * S::S_CH / 64 / kWaves) + (kStages - 1) * S::per_wave;
+    if constexpr (!kVarlen && S::uniform && (HB * P * S::S_CH / 64) % kWaves == 0 && kAfter < 64) {
+        if (nsb >= kStages - 1) wait_vmem_below<kAfter>();
+        else wait_vmem();
+    } else {
+        wait_vmem();
     }
     __syncthreads();
     for (int i = tid; i < HB * kMaxQ; i += kThreads) {
@@ -221,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         if constexpr (kVarlen) vst[i] = select(sidx >= lst[e], v, 0.f);
         else vst[i] = v;
     }
-    wait_vmem();                   // S_in tiles, the first stages, the tables' and C's loads
+    wait_vmem();                   // S_in slabs and the first stages
     __syncthreads();
 
     // y^T accumulators: acc[j][hh][pt] lane (r16, grp) holds y[16 rb_j + r16][16 pt + 4 grp + q]
@@ -237,15 +264,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
     for (int sl = 0; sl < S::NSL; ++sl) {
         if (sl > 0) {
-            __syncthreads();
-            issue_s(sl);
-            wait_vmem();
+            __syncthreads();                       // slab sl-1 consumed: its buffer takes slab sl+1
+            if (sl + 1 < S::NSL) {
+                issue_s(sl + 1);
+                wait_vmem_below<HB * P * S::S_CH / 64 / kWaves>();
+            } else {
+                wait_vmem();
+            }
             __syncthreads();
         }
         // every S_in fragment serves both row blocks (a missing row block has zero C fragments)
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
-            const unsigned char* stl = stile + hh * S::sh_bytes;
+            const unsigned char* stl = sbuf(sl) + hh * S::sh_bytes;
 #pragma unroll
             for (int kk = 0; kk < SW / 32; ++kk)
 #pragma unroll
@@ -273,6 +304,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         }
     }
 
+    if (S::NSL > 1) __syncthreads();               // the last ring slot held odd slabs
     // ---- intra-chunk term, one 32-token stage at a time
     for (int sb = 0; sb < nsb; ++sb) {
         const int s0 = sb * kSB;

@@ -308,16 +308,28 @@ __device__ __forceinline__ void swz_row_slots(Vec8<float>& f, const unsigned cha
     }
 }
 
-// Store 4 consecutive elements through a buffer resource: one instruction
-// whatever the offset; a store whose offset (voff + soff) reaches the
-// resource's size is dropped by the hardware, which masks rows (voff) and
-// heads (soff) without branching.  kDropped marks a dropped store: resources
-// here stay below 2^30 bytes, and two kDropped offsets still sum below 2^32.
+// Buffer-resource accesses: one instruction whatever the offset; a store
+// whose offset (voff + soff) reaches the resource's size is dropped by the
+// hardware and such a load reads zeros, which masks rows (voff) and heads
+// (soff) without branching.  kDropped marks a dropped access: resources here
+// stay below 2^30 bytes, and two kDropped offsets still sum below 2^32.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kBufferDword3 = 0x00020000;     // raw buffer, 32-bit data format, range-checked
 constexpr int kDropped = 0x40000000;
 
+// Load 8 consecutive elements (the fp32 form reads two 16-byte halves, at voff and voff + 16).
+__device__ __forceinline__ void buffer_load8(Vec8<bf16>& f, __amdgpu_buffer_rsrc_t r, int voff) {
+    f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+__device__ __forceinline__ void buffer_load8(Vec8<float>& f, __amdgpu_buffer_rsrc_t r, int voff) {
+    const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+    const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Store 4 consecutive elements.
 __device__ __forceinline__ void buffer_store4(__amdgpu_buffer_rsrc_t r, int voff, int soff, const f32x4& v, bf16) {
     bf16x4 q;
     q[0] = static_cast<bf16>(v[0]); q[1] = static_cast<bf16>(v[1]);
