@@ -33,6 +33,8 @@
 // on the fp32 matrix-core path; dx, dB and dC are rounded to bf16 once at the end.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -82,7 +84,7 @@ template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ x, const float* __restrict__ dt,
                                                       const float* __restrict__ Bm, const float* __restrict__ Cm,
                                                       const float* __restrict__ dy, float* __restrict__ dy_rev,
-                                                      float* __restrict__ B_rev, float* __restrict__ C_rev,
+                                                      TD* __restrict__ B_rev, TD* __restrict__ C_rev,
                                                       TD* __restrict__ dy_revD, TD* __restrict__ u_revD,
                                                       TD* __restrict__ Crep_rev, TD* __restrict__ Brep, int batch,
                                                       int64_t L, int nc, int Q, int H, int P, int N, int G, int nsplit)
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
         store8(dy_revD + r * P + 8 * v, ad);
         store8(u_revD + r * P + 8 * v, ud);
     }
-    // 2. per (b, tau, g): B_rev, C_rev (fp32)
+    // 2. per (b, tau, g): B_rev, C_rev (TD: exact, B and C hold values of the inputs' type)
     const int64_t n2 = (int64_t)batch * Lp * G * (N / 8);
     for (int64_t i = gtid(); i < n2; i += grid_stride()) {
         const int v = (int)(i % (N / 8));
@@ -137,8 +139,14 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
             vb.zero();
             vc.zero();
         }
-        store8(B_rev + r * N + 8 * v, vb);
-        store8(C_rev + r * N + 8 * v, vc);
+        Vec8<TD> ob, oc;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            ob.set(k, vb.get(k));
+            oc.set(k, vc.get(k));
+        }
+        store8(B_rev + r * N + 8 * v, ob);
+        store8(C_rev + r * N + 8 * v, oc);
     }
     // 3. per (split, b, tau, h): C copied per head, reversed; per (split, b, t, h): B copied per head (TD)
     const int64_t n3 = (int64_t)nsplit * batch * Lp * H * (Nh / 8);
@@ -429,8 +437,8 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.hfinal = take(B * H * P * N * 4);
     w.yhat = take(B * d.seqlen * H * P * 4);
     w.dy_rev = take(B * Lp * H * P * 4);
-    w.B_rev = take(B * Lp * G * N * 4);
-    w.C_rev = take(B * Lp * G * N * 4);
+    w.B_rev = take(B * Lp * G * N * elemD);
+    w.C_rev = take(B * Lp * G * N * elemD);
     w.dy_revD = take(B * Lp * H * P * elemD);
     w.u_revD = take(B * Lp * H * P * elemD);
     w.Crep_rev = take(B * Lp * H * N * elemD);
@@ -450,12 +458,14 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
 namespace {
 
 // The pass on fp32 arrays (x, B, C, dy and the outputs dx, dB, dC), with the dB / dC passes'
-// operands in TD: x_d, dy_d are x, dy in TD (the caller's own arrays when TD is their type).
+// operands in TD: x_d, dy_d, B_d, C_d are x, dy, B, C in TD (the caller's own arrays when TD is
+// their type).  With bf16 inputs, B and C hold bf16 values, so the fp32 readout passes take them in
+// bf16 and form C.B^T on the bf16 matrix cores (exact products, fp32 sums).
 template <typename TD>
 hipError_t run_backward(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
                         const float* D, const float* init, const float* dy, const float* dfinal, const TD* x_d,
-                        const TD* dy_d, float* dx, float* ddt, float* dA, float* dB, float* dC, float* dD,
-                        float* dinit, const Dims& d, void* workspace, hipStream_t s)
+                        const TD* dy_d, const TD* B_d, const TD* C_d, float* dx, float* ddt, float* dA, float* dB,
+                        float* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t s)
 {
     const BwdLayout w = bwd_layout(d, (int)sizeof(TD));
     unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -474,7 +484,10 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     // forward recompute in fp32: chunk states, entry states, the final state, yhat = y - D x
     SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
     SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
-    SSD_TRY(launch_chunk_scan_f32out<float>(x, Bm, Cm, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
+    if constexpr (std::is_same_v<TD, bf16>)
+        SSD_TRY(launch_chunk_scan_f32_bf16bc(x, B_d, C_d, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
+    else
+        SSD_TRY(launch_chunk_scan_f32out<float>(x, Bm, Cm, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
     // tables, adjoint chunk states (into the chunk-state buffer, free again), adjoint passing
     const int64_t nrows = (int64_t)B * H * nc;
     hipLaunchKernelGGL(bwd_tables_kernel, dim3(grid_for(nrows * Q)), dim3(kT), 0, s, F(w.cs), F(w.W), F(w.Z), F(w.dtp),
@@ -488,7 +501,7 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)nsplit * B * Lp * H * (Nh / 8));
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, F(w.dy_rev),
-                       F(w.B_rev), F(w.C_rev), TT(w.dy_revD), TT(w.u_revD), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q,
+                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q,
                        H, P, N, G, nsplit);
     SSD_TRY(hipGetLastError());
     hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
@@ -496,8 +509,12 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     SSD_TRY(hipGetLastError());
     // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
-    SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp), F(w.Gout_rev),
-                                            zeros, F(w.du_rev), dr, s));
+    if constexpr (std::is_same_v<TD, bf16>)
+        SSD_TRY(launch_chunk_scan_f32_bf16bc(F(w.dy_rev), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp),
+                                             F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
+    else
+        SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
+                                                F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
     // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half
     const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     const Dims dcd{d.batch, L, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
@@ -573,8 +590,8 @@ hipError_t launch_backward_f32(const float* x, const float* dt, const float* A, 
                                float* ddt, float* dA, float* dB, float* dC, float* dD, float* dinit, const Dims& d,
                                void* workspace, hipStream_t s)
 {
-    return run_backward<float>(x, dt, A, Bm, Cm, D, init, dy, dfinal, x, dy, dx, ddt, dA, dB, dC, dD, dinit, d,
-                               workspace, s);
+    return run_backward<float>(x, dt, A, Bm, Cm, D, init, dy, dfinal, x, dy, Bm, Cm, dx, ddt, dA, dB, dC, dD, dinit,
+                               d, workspace, s);
 }
 
 hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* Bm, const bf16* Cm,
@@ -598,8 +615,8 @@ hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, 
     hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Cm, C32, nb / 8);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = run_backward<bf16>(x32, dt, A, B32, C32, D, init, dy32, dfinal, x, dy, dx32, ddt, dA, dB32, dC32, dD, dinit, d,
-                           workspace, s);
+    e = run_backward<bf16>(x32, dt, A, B32, C32, D, init, dy32, dfinal, x, dy, Bm, Cm, dx32, ddt, dA, dB32, dC32, dD,
+                           dinit, d, workspace, s);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dx32, dx, nx / 8);
     hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dB32, dB, nb / 8);

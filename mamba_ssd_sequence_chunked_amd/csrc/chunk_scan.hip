@@ -71,7 +71,7 @@ constexpr int kMaxQ = 256;
 constexpr int kWaves = 4;                      // one row-block pair per wavefront
 constexpr int kThreads = 64 * kWaves;
 
-template <typename T, int P, int NK, int HB, int STG, int SW, bool V = false>
+template <typename T, typename TB, int P, int NK, int HB, int STG, int SW, bool V = false>
 struct ScanCfg {
     static constexpr int kHeads = HB;
     static constexpr int kStages = STG;                            // depth of the source-token ring
@@ -80,10 +80,11 @@ struct ScanCfg {
     static constexpr int SWD = SW;                                 // state columns of S_in per LDS slab
     static constexpr int NSL = NP / SW;                            // slabs
     static constexpr int X_CH = P * (int)sizeof(T) / 16;           // chunks per x row
-    static constexpr int B_CH = NP * (int)sizeof(T) / 16;          // chunks per B row
+    static constexpr int EPB = 16 / (int)sizeof(TB);              // B / C elements per 16-byte chunk
+    static constexpr int B_CH = NP * (int)sizeof(TB) / 16;         // chunks per B row
     static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in slab row
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
-    static constexpr int b_bytes = kSB * NP * (int)sizeof(T);
+    static constexpr int b_bytes = kSB * NP * (int)sizeof(TB);
     static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
     static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head
     static constexpr int ring_bytes = STG * stage_bytes;
@@ -109,17 +110,27 @@ struct ScanCfg {
 // and a single head takes a CU alone when it must.
 template <class C> struct TypeBox { using type = C; };
 
-template <typename T, int P, int NK, int HB, bool V>
+template <typename T, typename TB, int P, int NK, int HB, bool V>
 constexpr auto pick_shape() {
-    using C = ScanCfg<T, P, NK, HB, 2, 32, V>;
+    using C = ScanCfg<T, TB, P, NK, HB, 2, 32, V>;
     if constexpr (C::pair_fits || (HB == 1 && C::fits)) return TypeBox<C>{};
-    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2, V>();
+    else if constexpr (HB > 1) return pick_shape<T, TB, P, NK, HB / 2, V>();
     else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
 }
 
-template <typename T, int P, int NK, bool V = false>
-using ScanShape = typename decltype(pick_shape<T, P, NK,
+template <typename T, typename TB, int P, int NK, bool V = false>
+using ScanShape = typename decltype(pick_shape<T, TB, P, NK,
     ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), V>())::type;
+
+// a C fragment as an operand of the S_in product (whose other operand is in T)
+__device__ __forceinline__ const Vec8<float>& as_t(const Vec8<float>& f, float) { return f; }
+__device__ __forceinline__ const Vec8<bf16>& as_t(const Vec8<bf16>& f, bf16) { return f; }
+__device__ __forceinline__ Vec8<float> as_t(const Vec8<bf16>& f, float) {
+    Vec8<float> w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) w.set(e, f.get(e));
+    return w;
+}
 
 // kVarlen: a packed variable-length batch (batch 1; tstart from varlen_meta.hip).  A pair (l, s)
 // of one chunk is kept only when s >= tstart[l] (same sequence); since sequences are contiguous,
@@ -127,9 +138,11 @@ using ScanShape = typename decltype(pick_shape<T, P, NK,
 // times [s >= tstart[e]] per token, which fold into the row decay and the token table; the state
 // entering the chunk reaches only the rows of the sequence holding the chunk's first token.
 // TY: the type y is stored in (T, or float when the caller needs the sum unrounded).
-template <typename T, typename TY, int P, int NK, class S, bool kVarlen>
+// TB: the type of B and C (T, or bf16 under fp32 x and S_in when B and C hold bf16 values: C.B^T then
+// runs on the bf16 matrix cores, its products exact in the fp32 accumulator as on the fp32 ones).
+template <typename T, typename TB, typename TY, int P, int NK, class S, bool kVarlen>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
-    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
+    const T* __restrict__ x, const TB* __restrict__ Bm, const TB* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, TY* __restrict__ y,
     int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
@@ -170,11 +183,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots),
     // by range-checked buffer loads (rows past the chunk's tokens and missing blocks read as zero).
     // Issued first: no later wait for them then also waits for the asynchronous copies below.
-    Vec8<T> cf[2][S::NP / 32];
+    Vec8<TB> cf[2][S::NP / 32];
     {
-        const T* cb = Cm + ((b * seqlen + t0) * ngroups + g) * (int64_t)N;
+        const TB* cb = Cm + ((b * seqlen + t0) * ngroups + g) * (int64_t)N;
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<T*>(cb), 0, ((len - 1) * ngroups + 1) * N * (int)sizeof(T), kBufferDword3);
+            const_cast<TB*>(cb), 0, ((len - 1) * ngroups + 1) * N * (int)sizeof(TB), kBufferDword3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int l = 16 * rbk[j] + r16;
@@ -182,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) {
                 const int col = 32 * ks + 8 * grp;
-                buffer_load8(cf[j][ks], crs, rok && col < N ? (l * ngroups * N + col) * (int)sizeof(T) : kDropped);
+                buffer_load8(cf[j][ks], crs, rok && col < N ? (l * ngroups * N + col) * (int)sizeof(TB) : kDropped);
             }
         }
     }
@@ -217,9 +230,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
             return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(hh, nh - 1) * P + ch * EPC;
         });
-        const T* bg = Bm + (int64_t)g * N;
+        const TB* bg = Bm + (int64_t)g * N;
         tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
-            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
+            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * S::EPB, N - S::EPB);
         });
     };
 #pragma unroll
@@ -283,8 +296,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 for (int pt = 0; pt < P / 16; ++pt) {
                     Vec8<T> af;
                     swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
-                    mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
-                    mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
+                    mma(acc[0][hh][pt], af, as_t(cf[0][sl * (SW / 32) + kk], T{}));
+                    mma(acc[1][hh][pt], af, as_t(cf[1][sl * (SW / 32) + kk], T{}));
                 }
         }
     }
@@ -328,7 +341,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 gt[st2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NK; ++ks) {
-                    Vec8<T> af;
+                    Vec8<TB> af;
                     swz_load8<S::B_CH>(af, bt, 16 * st2 + r16, 32 * ks + 8 * grp);
                     mma(gt[st2], af, cf[j][ks]);
                 }
@@ -422,11 +435,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 }
 
-template <typename T, typename TY, int P, int NK, bool V>
-hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
+template <typename T, typename TB, typename TY, int P, int NK, bool V>
+hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                   const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
 {
-    using S = ScanShape<T, P, NK, V>;
+    using S = ScanShape<T, TB, P, NK, V>;
     static_assert(S::fits, "LDS budget");
     constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
@@ -437,20 +450,20 @@ hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const fl
     const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        x, B, C, dtc, cs, entry, D, tstart, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, typename TY, bool V>
-hipError_t launch_any(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
+template <typename T, typename TB, typename TY, bool V>
+hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                       const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
 #define SSD_SCAN_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+    if (d.headdim == PP && nki == KK) return launch<T, TB, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -465,7 +478,7 @@ hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt
                              const float* dA_cs, const T* entry_states, const float* D, T* y,
                              const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+    return launch_any<T, T, T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
 }
 
 template <typename T>
@@ -473,7 +486,14 @@ hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, float* y,
                                     const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+    return launch_any<T, T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+}
+
+hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                        const float* dA_cs, const float* entry_states, const float* D, float* y,
+                                        const Dims& d, hipStream_t stream)
+{
+    return launch_any<float, bf16, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
 }
 
 template <typename T>
@@ -481,7 +501,7 @@ hipError_t launch_chunk_scan_varlen(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, const int* tstart,
                                     T* y, const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
+    return launch_any<T, T, T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
 }
 
 template hipError_t launch_chunk_scan<float>(const float*, const float*, const float*, const float*,

@@ -57,6 +57,12 @@ hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, float* y,
                                     const Dims& d, hipStream_t stream);
 
+// the same in fp32 with B and C given in bf16 (arrays that hold bf16 values): C.B^T on the bf16
+// matrix cores, everything else in fp32
+hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                        const float* dA_cs, const float* entry_states, const float* D, float* y,
+                                        const Dims& d, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
                            const T* C, const float* D, T* y, const Dims& d, hipStream_t stream);
