@@ -435,11 +435,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 }
 
-template <typename T, typename TB, typename TY, int P, int NK, bool V>
-hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                  const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
+template <typename T, typename TB, typename TY, int P, int NK, bool V, class S>
+hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
+                        const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
 {
-    using S = ScanShape<T, TB, P, NK, V>;
     static_assert(S::fits, "LDS budget");
     constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
@@ -454,6 +453,22 @@ hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const 
                        x, B, C, dtc, cs, entry, D, tstart, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
+}
+
+// groups of a single head (the backward's per-head passes) take the one-head shape: a wider one
+// would compute a clamped copy of the head in its other slots
+template <typename T, typename TB, typename TY, int P, int NK, bool V>
+hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
+                  const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
+{
+    using S = ScanShape<T, TB, P, NK, V>;
+    if constexpr (S::kHeads > 1) {
+        if (d.nheads == d.ngroups) {
+            using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V>())::type;
+            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+        }
+    }
+    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
 }
 
 template <typename T, typename TB, typename TY, bool V>
