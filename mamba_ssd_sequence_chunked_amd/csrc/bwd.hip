@@ -76,21 +76,19 @@ __global__ __launch_bounds__(kT) void bwd_tables_kernel(const float* __restrict_
     }
 }
 
-// reversed (front-padded) copies: in fp32 dy (B, Lp, H, P) and B, C (B, Lp, G, N) for the adjoint
-// readout; in TD (the operand type of the dB / dC passes) dy and u = dt x (B, Lp, H, P), C copied
-// per head and reversed, B copied per head, both split into column halves when N > 128:
-// (nsplit, B, Lp|L, H, Nh); eight elements per thread
+// reversed (front-padded) copies: dy (B, Lp, H, P) in fp32 for the adjoint readout; B, C (B, Lp, G, N)
+// in TD, which holds their values exactly (the readout's B and C, and the dB pass's C, read per
+// group); in TD (the operand type of the dB / dC passes) dy and u = dt x (B, Lp, H, P); eight
+// elements per thread
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ x, const float* __restrict__ dt,
                                                       const float* __restrict__ Bm, const float* __restrict__ Cm,
                                                       const float* __restrict__ dy, float* __restrict__ dy_rev,
                                                       TD* __restrict__ B_rev, TD* __restrict__ C_rev,
-                                                      TD* __restrict__ dy_revD, TD* __restrict__ u_revD,
-                                                      TD* __restrict__ Crep_rev, TD* __restrict__ Brep, int batch,
-                                                      int64_t L, int nc, int Q, int H, int P, int N, int G, int nsplit)
+                                                      TD* __restrict__ dy_revD, TD* __restrict__ u_revD, int batch,
+                                                      int64_t L, int nc, int Q, int H, int P, int N, int G)
 {
     const int64_t Lp = (int64_t)nc * Q;
-    const int hpg = H / G, Nh = N / nsplit;
     // 1. per (b, tau, h): dy_rev (fp32 and TD) and u_rev (TD), P / 8 vectors each
     const int64_t n1 = (int64_t)batch * Lp * H * (P / 8);
     for (int64_t i = gtid(); i < n1; i += grid_stride()) {
@@ -147,35 +145,6 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
         }
         store8(B_rev + r * N + 8 * v, ob);
         store8(C_rev + r * N + 8 * v, oc);
-    }
-    // 3. per (split, b, tau, h): C copied per head, reversed; per (split, b, t, h): B copied per head (TD)
-    const int64_t n3 = (int64_t)nsplit * batch * Lp * H * (Nh / 8);
-    for (int64_t i = gtid(); i < n3; i += grid_stride()) {
-        const int v = (int)(i % (Nh / 8));
-        int64_t r = i / (Nh / 8);                  // (k, b, tau, h)
-        const int h = (int)(r % H);
-        r /= H;
-        const int64_t tau = r % Lp;
-        r /= Lp;
-        const int64_t b = r % batch;
-        const int k = (int)(r / batch);
-        const int g = h / hpg;
-        const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<float> vc;
-        Vec8<TD> vcd;
-        if (t >= 0) load8(vc, Cm + ((b * L + t) * G + g) * N + k * Nh + 8 * v);
-        else vc.zero();
-#pragma unroll
-        for (int q = 0; q < 8; ++q) vcd.set(q, vc.get(q));
-        store8(Crep_rev + (((k * batch + b) * Lp + tau) * H + h) * Nh + 8 * v, vcd);
-        if (tau < L) {
-            Vec8<float> vb;
-            Vec8<TD> vbd;
-            load8(vb, Bm + ((b * L + tau) * G + g) * N + k * Nh + 8 * v);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) vbd.set(q, vb.get(q));
-            store8(Brep + (((k * batch + b) * L + tau) * H + h) * Nh + 8 * v, vbd);
-        }
     }
 }
 
@@ -441,8 +410,6 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.C_rev = take(B * Lp * G * N * elemD);
     w.dy_revD = take(B * Lp * H * P * elemD);
     w.u_revD = take(B * Lp * H * P * elemD);
-    w.Crep_rev = take(B * Lp * H * N * elemD);
-    w.Brep = take(B * d.seqlen * H * N * elemD);
     w.du_rev = take(B * Lp * H * P * 4);
     w.dBh_rev = take(B * Lp * H * N * 4);
     w.dCh = take(B * d.seqlen * H * N * 4);
@@ -499,10 +466,9 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
                        dinit, B, H, P, N, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
-    const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)nsplit * B * Lp * H * (Nh / 8));
+    const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, F(w.dy_rev),
-                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), TT(w.Crep_rev), TT(w.Brep), B, L, nc, Q,
-                       H, P, N, G, nsplit);
+                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), B, L, nc, Q, H, P, N, G);
     SSD_TRY(hipGetLastError());
     hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
                        F(w.entry), TT(w.SinT), nrows, P, N, nsplit);
@@ -515,17 +481,18 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     else
         SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
                                                 F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
-    // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half
+    // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half;
+    // the x role (C reversed, B) is read from the group's array by every head of the group
     const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     const Dims dcd{d.batch, L, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
+    const XLayout xg{(int64_t)G * N, H / G, N};
     for (int k = 0; k < nsplit; ++k) {
-        SSD_TRY(launch_chunk_scan_f32out<TD>(TT(w.Crep_rev) + (int64_t)k * B * Lp * H * Nh, TT(w.dy_revD),
-                                             TT(w.u_revD), F(w.dtp), F(w.csp),
-                                             TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P, zeros,
-                                             F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
-        SSD_TRY(launch_chunk_scan_f32out<TD>(TT(w.Brep) + (int64_t)k * B * L * H * Nh, x_d, dy_d, F(w.dtc), F(w.cs),
-                                             TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
-                                             F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
+        SSD_TRY(launch_chunk_scan_f32out_xl<TD>(TT(w.C_rev) + (int64_t)k * Nh, xg, TT(w.dy_revD), TT(w.u_revD),
+                                                F(w.dtp), F(w.csp), TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P,
+                                                zeros, F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
+        SSD_TRY(launch_chunk_scan_f32out_xl<TD>(B_d + (int64_t)k * Nh, xg, x_d, dy_d, F(w.dtc), F(w.cs),
+                                                TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
+                                                F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
     }
     // per token (all rows in parallel), then the suffix sums per (b, h), then the group and batch sums
     {

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const TB* __restrict__ Bm, const TB* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, TY* __restrict__ y,
-    int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
+    XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
     __shared__ __attribute__((aligned(16))) float cst[HB * kMaxQ];
@@ -226,9 +226,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
         const unsigned stg = lds_addr(region) + (sb % kStages) * S::stage_bytes;
-        const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
+        const T* xs = x + (b * seqlen + t0) * xl.row;
         tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
-            return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(hh, nh - 1) * P + ch * EPC;
+            return xs + (int64_t)min(s0 + r, len - 1) * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs +
+                   ch * EPC;
         });
         const TB* bg = Bm + (int64_t)g * N;
         tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 
 template <typename T, typename TB, typename TY, int P, int NK, bool V, class S>
 hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                        const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
+                        const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d, hipStream_t stream)
 {
     static_assert(S::fits, "LDS budget");
     constexpr int HB = S::kHeads;
@@ -450,7 +451,7 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
     hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       x, B, C, dtc, cs, entry, D, tstart, y, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
+                       x, B, C, dtc, cs, entry, D, tstart, y, xl, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
@@ -459,26 +460,28 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
 // would compute a clamped copy of the head in its other slots
 template <typename T, typename TB, typename TY, int P, int NK, bool V>
 hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                  const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
+                  const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d, hipStream_t stream)
 {
     using S = ScanShape<T, TB, P, NK, V>;
     if constexpr (S::kHeads > 1) {
         if (d.nheads == d.ngroups) {
             using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V>())::type;
-            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
         }
     }
-    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
 }
 
 template <typename T, typename TB, typename TY, bool V>
 hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                      const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream)
+                      const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream,
+                      XLayout xl = XLayout{0, 0, 0})
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
+    if (xl.hdiv == 0) xl = XLayout{d.nheads * d.headdim, 1, (int)d.headdim};     // x in (B, L, H, P)
 #define SSD_SCAN_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, TB, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, d, stream);
+    if (d.headdim == PP && nki == KK) return launch<T, TB, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -502,6 +505,14 @@ hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const fl
                                     const Dims& d, hipStream_t stream)
 {
     return launch_any<T, T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+}
+
+template <typename T>
+hipError_t launch_chunk_scan_f32out_xl(const T* x, const XLayout& xl, const T* B, const T* C, const float* dt_chunked,
+                                       const float* dA_cs, const T* entry_states, const float* D, float* y,
+                                       const Dims& d, hipStream_t stream)
+{
+    return launch_any<T, T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream, xl);
 }
 
 hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
@@ -531,6 +542,12 @@ template hipError_t launch_chunk_scan_f32out<float>(const float*, const float*, 
 template hipError_t launch_chunk_scan_f32out<bf16>(const bf16*, const bf16*, const bf16*, const float*,
                                                    const float*, const bf16*, const float*, float*,
                                                    const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_f32out_xl<float>(const float*, const XLayout&, const float*, const float*,
+                                                       const float*, const float*, const float*, const float*,
+                                                       float*, const Dims&, hipStream_t);
+template hipError_t launch_chunk_scan_f32out_xl<bf16>(const bf16*, const XLayout&, const bf16*, const bf16*,
+                                                      const float*, const float*, const bf16*, const float*, float*,
+                                                      const Dims&, hipStream_t);
 template hipError_t launch_chunk_scan_varlen<float>(const float*, const float*, const float*, const float*,
                                                     const float*, const float*, const float*, const int*, float*,
                                                     const Dims&, hipStream_t);

@@ -11,6 +11,14 @@ struct Dims {
     int64_t nchunks() const { return (seqlen + chunk - 1) / chunk; }
 };
 
+// Where stage 4 finds the x row of token t, head h: x + t * row + (h / hdiv) * hs (elements); the
+// caller's (B, L, H, P) array is {H * P, 1, P}.  The backward's per-head passes read an array shared
+// by the heads of a group ({G * N, H / G, N}).
+struct XLayout {
+    int64_t row;
+    int hdiv, hs;
+};
+
 hipError_t launch_dA_cumsum(const float* dt, const float* A, float* dA_cs, float* dt_chunked,
                             const Dims& d, hipStream_t stream);
 
@@ -57,6 +65,12 @@ hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, float* y,
                                     const Dims& d, hipStream_t stream);
 
+// stage 4 with y in fp32 and x read through an XLayout
+template <typename T>
+hipError_t launch_chunk_scan_f32out_xl(const T* x, const XLayout& xl, const T* B, const T* C, const float* dt_chunked,
+                                       const float* dA_cs, const T* entry_states, const float* D, float* y,
+                                       const Dims& d, hipStream_t stream);
+
 // the same in fp32 with B and C given in bf16 (arrays that hold bf16 values): C.B^T on the bf16
 // matrix cores, everything else in fp32
 hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
@@ -75,7 +89,7 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
     size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, u_rev, B_rev,
-        C_rev, dy_revD, u_revD, Crep_rev, Brep, du_rev, dBh_rev, dCh, zeros, qx, xdy, dAp, dDp, total;
+        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, zeros, qx, xdy, dAp, dDp, total;
 };
 BwdLayout bwd_layout(const Dims& d, int elem_bytes);
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
