@@ -76,7 +76,8 @@ __global__ __launch_bounds__(kT) void bwd_tables_kernel(const float* __restrict_
     }
 }
 
-// reversed (front-padded) copies: dy (B, Lp, H, P) in fp32 for the adjoint readout; B, C (B, Lp, G, N)
+// reversed (front-padded) copies: dy (B, Lp, H, P) in fp32 for the fp32 adjoint readout (if dy_rev is
+// given); B, C (B, Lp, G, N)
 // in TD, which holds their values exactly (the readout's B and C, and the dB pass's C, read per
 // group); in TD (the operand type of the dB / dC passes) dy and u = dt x (B, Lp, H, P); eight
 // elements per thread
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
             ad.zero();
             ud.zero();
         }
-        store8(dy_rev + r * P + 8 * v, a);
+        if (dy_rev) store8(dy_rev + r * P + 8 * v, a);
         store8(dy_revD + r * P + 8 * v, ad);
         store8(u_revD + r * P + 8 * v, ud);
     }
@@ -149,8 +150,8 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
 }
 
 // S_in^T per chunk and head, split into column halves: (nsplit, B, nc, H, Nh, P) from (B, nc, H, P, N)
-template <typename TD>
-__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const float* __restrict__ src, TD* __restrict__ dst,
+template <typename TS, typename TD>
+__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const TS* __restrict__ src, TD* __restrict__ dst,
                                                            int64_t nblk, int P, int N, int nsplit)
 {
     const int Nh = N / nsplit;
@@ -162,17 +163,19 @@ __global__ __launch_bounds__(kT) void bwd_transpose_kernel(const float* __restri
         r /= Nh;
         const int64_t blk = r % nblk;              // (b, c, h)
         const int k = (int)(r / nblk);
-        dst[i] = from_f32<TD>(src[(blk * P + p) * N + k * Nh + j]);
+        dst[i] = from_f32<TD>(to_f32(src[(blk * P + p) * N + k * Nh + j]));
     }
 }
 
 // backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
-// order as T (P x N) and transposed (split into column halves, N x P); dinit at the end
+// order (P x N: fp32, or for TD = bf16 as bf16 hi / lo planes, the lo plane lo_off elements after
+// the hi one) and transposed in TD (split into column halves, N x P); dinit at the end
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
-                                                         const float* __restrict__ dfinal, float* __restrict__ Gout_rev,
+                                                         const float* __restrict__ dfinal, void* __restrict__ Gout_rev,
                                                          TD* __restrict__ GoutT_rev, float* __restrict__ dinit,
-                                                         int batch, int H, int P, int N, int Q, int nc, int nsplit)
+                                                         int64_t lo_off, int batch, int H, int P, int N, int Q, int nc,
+                                                         int nsplit)
 {
     const int PN = P * N, Nh = N / nsplit;
     const int h = blockIdx.y;
@@ -184,7 +187,15 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
     float4 s = dfinal ? *reinterpret_cast<const float4*>(dfinal + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = nc - 1; c >= 0; --c) {
         const int cr = nc - 1 - c;
-        store4(Gout_rev + ((b * nc + cr) * H + h) * (int64_t)PN + e, s.x, s.y, s.z, s.w);
+        const int64_t go = ((b * nc + cr) * H + h) * (int64_t)PN + e;
+        if constexpr (std::is_same_v<TD, bf16>) {
+            auto rem = [](float v) { return v - static_cast<float>(static_cast<bf16>(v)); };
+            bf16* gh = static_cast<bf16*>(Gout_rev) + go;
+            store4(gh, s.x, s.y, s.z, s.w);
+            store4(gh + lo_off, rem(s.x), rem(s.y), rem(s.z), rem(s.w));
+        } else {
+            store4(static_cast<float*>(Gout_rev) + go, s.x, s.y, s.z, s.w);
+        }
         const float sv[4] = {s.x, s.y, s.z, s.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -449,12 +460,17 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     hipLaunchKernelGGL(fill_zero_kernel, dim3(1), dim3(kT), 0, s, zeros, (int64_t)H);
     SSD_TRY(hipGetLastError());
     // forward recompute in fp32: chunk states, entry states, the final state, yhat = y - D x
+    // (bf16 inputs: the fp32 states leave as bf16 hi / lo planes, st elements apart, and the readout
+    // passes take split bf16 products)
+    const int64_t st = (int64_t)B * nc * H * P * N;
     SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
-    SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
-    if constexpr (std::is_same_v<TD, bf16>)
-        SSD_TRY(launch_chunk_scan_f32_bf16bc(x, B_d, C_d, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
-    else
+    if constexpr (std::is_same_v<TD, bf16>) {
+        SSD_TRY(launch_state_passing_split(F(w.states), F(w.cs), init, TT(w.entry), st, F(w.hfinal), d, s));
+        SSD_TRY(launch_chunk_scan_split(x_d, B_d, C_d, F(w.dtc), F(w.cs), TT(w.entry), st, zeros, F(w.yhat), d, s));
+    } else {
+        SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
         SSD_TRY(launch_chunk_scan_f32out<float>(x, Bm, Cm, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
+    }
     // tables, adjoint chunk states (into the chunk-state buffer, free again), adjoint passing
     const int64_t nrows = (int64_t)B * H * nc;
     hipLaunchKernelGGL(bwd_tables_kernel, dim3(grid_for(nrows * Q)), dim3(kT), 0, s, F(w.cs), F(w.W), F(w.Z), F(w.dtp),
@@ -462,22 +478,27 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     SSD_TRY(hipGetLastError());
     SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
     hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
-                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, F(w.Gout_rev), TT(w.GoutT_rev),
-                       dinit, B, H, P, N, Q, nc, nsplit);
+                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, (void*)(ws + w.Gout_rev),
+                       TT(w.GoutT_rev), dinit, st, B, H, P, N, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
-    hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, F(w.dy_rev),
+    float* const dy_rev32 = std::is_same_v<TD, bf16> ? nullptr : F(w.dy_rev);
+    hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, dy_rev32,
                        TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), B, L, nc, Q, H, P, N, G);
     SSD_TRY(hipGetLastError());
-    hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(grid_for((int64_t)B * nc * H * P * N)), dim3(kT), 0, s,
-                       F(w.entry), TT(w.SinT), nrows, P, N, nsplit);
+    if constexpr (std::is_same_v<TD, bf16>)
+        hipLaunchKernelGGL((bwd_transpose_kernel<bf16, bf16>), dim3(grid_for(st)), dim3(kT), 0, s, TT(w.entry),
+                           TT(w.SinT), nrows, P, N, nsplit);
+    else
+        hipLaunchKernelGGL((bwd_transpose_kernel<float, float>), dim3(grid_for(st)), dim3(kT), 0, s, F(w.entry),
+                           TT(w.SinT), nrows, P, N, nsplit);
     SSD_TRY(hipGetLastError());
     // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
     if constexpr (std::is_same_v<TD, bf16>)
-        SSD_TRY(launch_chunk_scan_f32_bf16bc(F(w.dy_rev), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp),
-                                             F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
+        SSD_TRY(launch_chunk_scan_split(TT(w.dy_revD), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev),
+                                        st, zeros, F(w.du_rev), dr, s));
     else
         SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
                                                 F(w.Gout_rev), zeros, F(w.du_rev), dr, s));

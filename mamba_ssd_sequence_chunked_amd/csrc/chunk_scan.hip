@@ -71,9 +71,10 @@ constexpr int kMaxQ = 256;
 constexpr int kWaves = 4;                      // one row-block pair per wavefront
 constexpr int kThreads = 64 * kWaves;
 
-template <typename T, typename TB, int P, int NK, int HB, int STG, int SW, bool V = false>
+template <typename T, typename TB, int P, int NK, int HB, int STG, int SW, bool V = false, int SP = 1>
 struct ScanCfg {
     static constexpr int kHeads = HB;
+    static constexpr bool kSplit = SP == 2;                       // S_in as bf16 hi and lo planes
     static constexpr int kStages = STG;                            // depth of the source-token ring
     static constexpr int EPC = 16 / (int)sizeof(T);               // elements per 16-byte chunk
     static constexpr int NP = 32 * NK;                             // state width padded to the contraction block
@@ -86,9 +87,14 @@ struct ScanCfg {
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
     static constexpr int b_bytes = kSB * NP * (int)sizeof(TB);
     static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
-    static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head
+    static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head (one plane)
     static constexpr int ring_bytes = STG * stage_bytes;
-    static constexpr int main_bytes = ring_bytes + HB * sh_bytes;
+    static constexpr int s_inst = HB * SP * P * S_CH / 64;          // copy instructions of one slab (all heads)
+    // odd slabs go to the ring slot that the source tokens use last when they fit there, else after
+    // the even slabs' area
+    static constexpr bool odd_in_ring = HB * SP * sh_bytes <= stage_bytes;
+    static constexpr int main_bytes = ring_bytes + HB * SP * sh_bytes * (NSL > 1 && !odd_in_ring ? 2 : 1);
+    static constexpr int odd_off = odd_in_ring ? (STG - 1) * stage_bytes : ring_bytes + HB * SP * sh_bytes;
     static constexpr int region = main_bytes;
     static constexpr int tab_bytes = 3 * 4 * HB * kMaxQ + (V ? 4 * kMaxQ : 0);   // cs, dt, per-token decay factor
                                                                                 // (+ sequence starts)
@@ -110,17 +116,17 @@ struct ScanCfg {
 // and a single head takes a CU alone when it must.
 template <class C> struct TypeBox { using type = C; };
 
-template <typename T, typename TB, int P, int NK, int HB, bool V>
+template <typename T, typename TB, int P, int NK, int HB, bool V, int SP = 1>
 constexpr auto pick_shape() {
-    using C = ScanCfg<T, TB, P, NK, HB, 2, 32, V>;
+    using C = ScanCfg<T, TB, P, NK, HB, 2, 32, V, SP>;
     if constexpr (C::pair_fits || (HB == 1 && C::fits)) return TypeBox<C>{};
-    else if constexpr (HB > 1) return pick_shape<T, TB, P, NK, HB / 2, V>();
+    else if constexpr (HB > 1) return pick_shape<T, TB, P, NK, HB / 2, V, SP>();
     else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
 }
 
-template <typename T, typename TB, int P, int NK, bool V = false>
+template <typename T, typename TB, int P, int NK, bool V = false, int SP = 1>
 using ScanShape = typename decltype(pick_shape<T, TB, P, NK,
-    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), V>())::type;
+    ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), V, SP>())::type;
 
 // a C fragment as an operand of the S_in product (whose other operand is in T)
 __device__ __forceinline__ const Vec8<float>& as_t(const Vec8<float>& f, float) { return f; }
@@ -140,12 +146,16 @@ __device__ __forceinline__ Vec8<float> as_t(const Vec8<bf16>& f, float) {
 // TY: the type y is stored in (T, or float when the caller needs the sum unrounded).
 // TB: the type of B and C (T, or bf16 under fp32 x and S_in when B and C hold bf16 values: C.B^T then
 // runs on the bf16 matrix cores, its products exact in the fp32 accumulator as on the fp32 ones).
+// S::kSplit (T = bf16, TY = float): the fp32 products of the backward's readout passes from bf16
+// ones, with x, B, C holding bf16 values: S_in comes as two bf16 planes, hi at entry and lo at
+// entry + lo_off (hi + lo = the fp32 state to 2^-18), G is split the same way in registers, and
+// each product is taken twice on the bf16 matrix cores (hi, then lo) into the fp32 accumulators.
 template <typename T, typename TB, typename TY, int P, int NK, class S, bool kVarlen>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const TB* __restrict__ Bm, const TB* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
-    const T* __restrict__ entry, const float* __restrict__ Dv, const int* __restrict__ tstart, TY* __restrict__ y,
-    XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
+    const T* __restrict__ entry, int64_t lo_off, const float* __restrict__ Dv, const int* __restrict__ tstart,
+    TY* __restrict__ y, XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
     __shared__ __attribute__((aligned(16))) float cst[HB * kMaxQ];
@@ -214,11 +224,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 
     // ---- then the heads' S_in tiles (first two slabs) and the first stages of the ring
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
-    // slab buffers: even slabs in the slab area, odd slabs in the last ring slot (free until the stage loop)
-    auto sbuf = [&](int sl) -> unsigned char* { return (sl & 1) ? region + (kStages - 1) * S::stage_bytes : stile; };
+    // slab buffers: even slabs in the slab area, odd slabs in the last ring slot (free until the stage
+    // loop) or, when they do not fit there, after the even ones
+    auto sbuf = [&](int sl) -> unsigned char* { return (sl & 1) ? region + S::odd_off : stile; };
     auto issue_s = [&](int sl) {
-        tiles_load_async<S::S_CH, P, HB, kWaves>(lds_addr(region) + ((sl & 1) ? (kStages - 1) * S::stage_bytes : S::ring_bytes), S::sh_bytes, [&](int hh, int r, int ch) -> const void* {
-            return ent + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N + min(sl * SW + ch * EPC, N - EPC);
+        // tiles 0 .. HB-1 the heads' (hi) slabs, HB .. 2 HB-1 their lo slabs (split mode)
+        tiles_load_async<S::S_CH, P, HB * (S::kSplit ? 2 : 1), kWaves>(lds_addr(region) + ((sl & 1) ? S::odd_off : S::ring_bytes), S::sh_bytes, [&](int t, int r, int ch) -> const void* {
+            const int hh = t % HB;
+            return ent + (t >= HB ? lo_off : 0) + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N +
+                   min(sl * SW + ch * EPC, N - EPC);
         });
     };
     issue_s(0);
@@ -247,8 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         for (int l = tid; l < kMaxQ; l += kThreads) lst[l] = tstart[t0 + min(l, len - 1)] - (int)t0;
     }
     // the tables have landed once only the copies issued after them may still fly
-    constexpr int kAfter = (1 + (S::NSL > 1)) * (HB * P * S::S_CH / 64 / kWaves) + (kStages - 1) * S::per_wave;
-    if constexpr (!kVarlen && S::uniform && (HB * P * S::S_CH / 64) % kWaves == 0 && kAfter < 64) {
+    constexpr int kAfter = (1 + (S::NSL > 1)) * (S::s_inst / kWaves) + (kStages - 1) * S::per_wave;
+    if constexpr (!kVarlen && S::uniform && S::s_inst % kWaves == 0 && kAfter < 64) {
         if (nsb >= kStages - 1) wait_vmem_below<kAfter>();
         else wait_vmem();
     } else {
@@ -281,7 +295,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             __syncthreads();                       // slab sl-1 consumed: its buffer takes slab sl+1
             if (sl + 1 < S::NSL) {
                 issue_s(sl + 1);
-                wait_vmem_below<HB * P * S::S_CH / 64 / kWaves>();
+                wait_vmem_below<S::s_inst / kWaves>();
             } else {
                 wait_vmem();
             }
@@ -299,6 +313,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
                     mma(acc[0][hh][pt], af, as_t(cf[0][sl * (SW / 32) + kk], T{}));
                     mma(acc[1][hh][pt], af, as_t(cf[1][sl * (SW / 32) + kk], T{}));
+                    if constexpr (S::kSplit) {
+                        swz_load8<S::S_CH>(af, stl + HB * S::sh_bytes, 16 * pt + r16, 32 * kk + 8 * grp);
+                        mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
+                        mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
+                    }
                 }
         }
     }
@@ -356,17 +375,22 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     const float* vr = vst + hh * kMaxQ + s0 + 4 * grp;
                     const float4 va = *reinterpret_cast<const float4*>(vr);
                     const float4 vb = *reinterpret_cast<const float4*>(vr + 16);
-                    Vec8<T> gf;
-                    gf.set(0, gt[0][0] * (u * va.x)); gf.set(1, gt[0][1] * (u * va.y));
-                    gf.set(2, gt[0][2] * (u * va.z)); gf.set(3, gt[0][3] * (u * va.w));
-                    gf.set(4, gt[1][0] * (u * vb.x)); gf.set(5, gt[1][1] * (u * vb.y));
-                    gf.set(6, gt[1][2] * (u * vb.z)); gf.set(7, gt[1][3] * (u * vb.w));
+                    Vec8<T> gf, gl;                               // gl: the lo parts (split mode)
+                    auto gset = [&](int i, float v) {
+                        if constexpr (S::kSplit) split_set(gf, gl, i, v);
+                        else gf.set(i, v);
+                    };
+                    gset(0, gt[0][0] * (u * va.x)); gset(1, gt[0][1] * (u * va.y));
+                    gset(2, gt[0][2] * (u * va.z)); gset(3, gt[0][3] * (u * va.w));
+                    gset(4, gt[1][0] * (u * vb.x)); gset(5, gt[1][1] * (u * vb.y));
+                    gset(6, gt[1][2] * (u * vb.z)); gset(7, gt[1][3] * (u * vb.w));
                     const unsigned char* xt = stg + hh * S::xh_bytes;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
                         Vec8<T> xf;
                         swz_row_slots<S::X_CH>(xf, xt, 0, 16 * pt);
                         mma(acc[j][hh][pt], xf, gf);
+                        if constexpr (S::kSplit) mma(acc[j][hh][pt], xf, gl);
                     }
                 }
             } else {
@@ -377,7 +401,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     const float* dtr = dtt + hh * kMaxQ;
                         const float cl = csr[lrow];
                     const int rst = kVarlen ? lst[min(lrow, kMaxQ - 1)] : 0;   // first token of the row's sequence
-                    Vec8<T> gf;                                   // G[lrow][s], s = s0 + 16 st2 + 4 grp + i
+                    Vec8<T> gf, gl;                               // G[lrow][s], s = s0 + 16 st2 + 4 grp + i
 #pragma unroll
                     for (int st2 = 0; st2 < 2; ++st2) {
                         const int sb4 = s0 + 16 * st2 + 4 * grp;
@@ -387,7 +411,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float v = gt[st2][i] * (__expf(cl - cv[i]) * dv[i]);
-                            gf.set(4 * st2 + i, select(sb4 + i <= lrow && (!kVarlen || sb4 + i >= rst), v, 0.f));
+                            const float g = select(sb4 + i <= lrow && (!kVarlen || sb4 + i >= rst), v, 0.f);
+                            if constexpr (S::kSplit) split_set(gf, gl, 4 * st2 + i, g);
+                            else gf.set(4 * st2 + i, g);
                         }
                     }
                     const unsigned char* xt = stg + hh * S::xh_bytes;
@@ -396,6 +422,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                         Vec8<T> xf;
                         swz_row_slots<S::X_CH>(xf, xt, 0, 16 * pt);
                         mma(acc[j][hh][pt], xf, gf);
+                        if constexpr (S::kSplit) mma(acc[j][hh][pt], xf, gl);
                     }
                 }
                 // skip term: x of the block's own rows is in this stage's tiles
@@ -438,9 +465,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 
 template <typename T, typename TB, typename TY, int P, int NK, bool V, class S>
 hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                        const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d, hipStream_t stream)
+                        int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
+                        hipStream_t stream)
 {
     static_assert(S::fits, "LDS budget");
+    static_assert(!S::kSplit || (std::is_same_v<T, bf16> && std::is_same_v<TB, bf16> && std::is_same_v<TY, float>),
+                  "split products: bf16 operands, fp32 output");
     constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
     const int hpg = (int)(d.nheads / d.ngroups);
@@ -451,37 +481,40 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
     hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
-                       x, B, C, dtc, cs, entry, D, tstart, y, xl, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
+                       x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
     return hipGetLastError();
 }
 
 // groups of a single head (the backward's per-head passes) take the one-head shape: a wider one
 // would compute a clamped copy of the head in its other slots
-template <typename T, typename TB, typename TY, int P, int NK, bool V>
+template <typename T, typename TB, typename TY, int P, int NK, bool V, int SP>
 hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
-                  const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d, hipStream_t stream)
+                  int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
+                  hipStream_t stream)
 {
-    using S = ScanShape<T, TB, P, NK, V>;
+    using S = ScanShape<T, TB, P, NK, V, SP>;
     if constexpr (S::kHeads > 1) {
         if (d.nheads == d.ngroups) {
-            using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V>())::type;
-            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
+            using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V, SP>())::type;
+            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d,
+                                                         stream);
         }
     }
-    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
+    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream);
 }
 
-template <typename T, typename TB, typename TY, bool V>
+template <typename T, typename TB, typename TY, bool V, int SP = 1>
 hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                       const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream,
-                      XLayout xl = XLayout{0, 0, 0})
+                      XLayout xl = XLayout{0, 0, 0}, int64_t lo_off = 0)
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
     if (xl.hdiv == 0) xl = XLayout{d.nheads * d.headdim, 1, (int)d.headdim};     // x in (B, L, H, P)
 #define SSD_SCAN_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, TB, TY, PP, KK, V>(x, B, C, dtc, cs, entry, D, tstart, y, xl, d, stream);
+    if (d.headdim == PP && nki == KK) \
+        return launch<T, TB, TY, PP, KK, V, SP>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -520,6 +553,14 @@ hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf1
                                         const Dims& d, hipStream_t stream)
 {
     return launch_any<float, bf16, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+}
+
+hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                   const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
+                                   const Dims& d, hipStream_t stream)
+{
+    return launch_any<bf16, bf16, float, false, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, y, d, stream,
+                                                   XLayout{0, 0, 0}, lo_off);
 }
 
 template <typename T>

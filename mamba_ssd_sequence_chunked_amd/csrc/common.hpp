@@ -108,6 +108,15 @@ __device__ __forceinline__ void mma(f32x4& acc, const Vec8<float>& a, const Vec8
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
+// An fp32 value as a pair of bf16 values: hi = bf16(v), lo = bf16(v - hi) (v - hi is exact in fp32),
+// so |v - hi - lo| <= 2^-9 |v - hi| <= 2^-18 |v| (normal range).  A product with a bf16-valued
+// operand then takes two bf16 matrix-core products, hi and lo, instead of the fp32 ones.
+__device__ __forceinline__ void split_set(Vec8<bf16>& hi, Vec8<bf16>& lo, int i, float v) {
+    const bf16 h = static_cast<bf16>(v);
+    hi.v[i] = h;
+    lo.v[i] = static_cast<bf16>(v - static_cast<float>(h));
+}
+
 // LDS pointer for a generic pointer known to point into LDS: the low 32 bits
 // of such a flat address are the LDS address (taken as an integer, so no
 // null-pointer check of a generic -> local cast is generated).

@@ -53,6 +53,10 @@ template <typename T>
 hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, const float* init,
                                 T* entry_states, float* final_states, const Dims& d,
                                 hipStream_t stream);
+// the entry states as bf16 hi / lo planes (hi = bf16(S), lo = bf16(S - hi); lo plane at entry_hi + lo_off)
+hipError_t launch_state_passing_split(const float* chunk_states, const float* dA_cs, const float* init,
+                                      bf16* entry_hi, int64_t lo_off, float* final_states, const Dims& d,
+                                      hipStream_t stream);
 
 template <typename T>
 hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt_chunked,
@@ -76,6 +80,11 @@ hipError_t launch_chunk_scan_f32out_xl(const T* x, const XLayout& xl, const T* B
 hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
                                         const float* dA_cs, const float* entry_states, const float* D, float* y,
                                         const Dims& d, hipStream_t stream);
+// the same result to within 2^-18 of each product, from bf16 products: x, B, C given in bf16 (arrays that
+// hold bf16 values), the entry states as two bf16 planes (hi at entry_hi, lo at entry_hi + lo_off)
+hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                   const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
+                                   const Dims& d, hipStream_t stream);
 
 template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,

@@ -17,7 +17,10 @@
 // in flight.  A workgroup covers 1024 elements of a single (batch, head), so
 // the chunk decay is one uniform value per chunk.  The running state stays
 // in fp32; entry states are rounded to T once, as the next stage consumes
-// them as matrix-core operands.
+// them as matrix-core operands (or, for the backward's split products, given
+// as bf16 hi and lo planes that carry the fp32 state to 2^-18).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,7 +41,7 @@ template <typename T, bool kVarlen>
 __global__ __launch_bounds__(256) void state_passing_kernel(
     const float* __restrict__ chunk_states, const float* __restrict__ dA_cs,
     const float* __restrict__ init, T* __restrict__ entry, float* __restrict__ final_states,
-    const int4* __restrict__ cmeta, int nheads, int PN, int Q, int nc)
+    const int4* __restrict__ cmeta, int64_t lo_off, int nheads, int PN, int Q, int nc)
 {
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
@@ -80,6 +83,12 @@ __global__ __launch_bounds__(256) void state_passing_kernel(
         const float4 sc = *reinterpret_cast<const float4*>(src + c * stride);
         const float dec = __expf(cs[(int64_t)c * Q]);
         store4(dst + c * stride, s.x, s.y, s.z, s.w);
+        if constexpr (std::is_same_v<T, bf16>) {
+            if (lo_off) {                   // the rounding remainders as a second plane
+                auto rem = [](float v) { return v - static_cast<float>(static_cast<bf16>(v)); };
+                store4(dst + lo_off + c * stride, rem(s.x), rem(s.y), rem(s.z), rem(s.w));
+            }
+        }
         s.x = fmaf(dec, s.x, sc.x);
         s.y = fmaf(dec, s.y, sc.y);
         s.z = fmaf(dec, s.z, sc.z);
@@ -100,7 +109,21 @@ hipError_t launch_state_passing(const float* chunk_states, const float* dA_cs, c
     dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads,
               (unsigned)d.batch);
     hipLaunchKernelGGL((state_passing_kernel<T, false>), grid, dim3(256), 0, stream, chunk_states, dA_cs, init,
-                       entry_states, final_states, nullptr, (int)d.nheads, PN, (int)d.chunk, (int)d.nchunks());
+                       entry_states, final_states, nullptr, (int64_t)0, (int)d.nheads, PN, (int)d.chunk,
+                       (int)d.nchunks());
+    return hipGetLastError();
+}
+
+hipError_t launch_state_passing_split(const float* chunk_states, const float* dA_cs, const float* init,
+                                      bf16* entry_hi, int64_t lo_off, float* final_states, const Dims& d,
+                                      hipStream_t stream)
+{
+    if (d.batch == 0) return hipSuccess;
+    const int PN = (int)(d.headdim * d.dstate);
+    dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads,
+              (unsigned)d.batch);
+    hipLaunchKernelGGL((state_passing_kernel<bf16, false>), grid, dim3(256), 0, stream, chunk_states, dA_cs, init,
+                       entry_hi, final_states, nullptr, lo_off, (int)d.nheads, PN, (int)d.chunk, (int)d.nchunks());
     return hipGetLastError();
 }
 
@@ -112,7 +135,7 @@ hipError_t launch_state_passing_varlen(const float* chunk_states, const float* d
     const int PN = (int)(d.headdim * d.dstate);
     dim3 grid((unsigned)((PN + kElemsPerBlock - 1) / kElemsPerBlock), (unsigned)d.nheads, 1u);
     hipLaunchKernelGGL((state_passing_kernel<T, true>), grid, dim3(256), 0, stream, chunk_states, dA_cs, nullptr,
-                       entry_states, final_states, reinterpret_cast<const int4*>(cmeta), (int)d.nheads, PN,
+                       entry_states, final_states, reinterpret_cast<const int4*>(cmeta), (int64_t)0, (int)d.nheads, PN,
                        (int)d.chunk, (int)d.nchunks());
     return hipGetLastError();
 }
