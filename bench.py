@@ -364,7 +364,7 @@ def main():
         bwd = dict(workload=f"{args.workload} backward: dx, ddt, dA, dB, dC, dD, dinit for a random dL/dy",
                    calls=args.backward_calls, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
                    time_over_forward=round(us / (ms_per_step * 1e3), 2),
-                   note="bf16 inputs are widened to fp32 for the decay-gradient path (see the library header)")
+                   note="the decay-gradient path takes fp32-accurate products: bf16 hi + lo pairs on the bf16 matrix cores (see the library header)")
         print(f"[bench] backward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del dyb, bws, gx, gB, gC
 

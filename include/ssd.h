@@ -131,9 +131,11 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
  *   dinit float (batch, nheads, headdim, dstate): the gradient of the initial state (written
  *     also when init_states is NULL)
  *   workspace of at least ssd_backward_workspace_bytes() bytes
- * dstate must be one of 16, 32, 64, 128, 256 and nheads * dstate <= 2^20.  With bf16 inputs the
- * pass widens them to fp32 and computes in fp32 (the decay gradients cancel too much for bf16
- * operands); dx, dB, dC are rounded to bf16 once. */
+ * dstate must be one of 16, 32, 64, 128, 256 and nheads * dstate <= 2^20.  The decay gradients
+ * cancel too much for bf16 operands: fp32 inputs take the fp32 matrix cores for the recompute, the
+ * adjoint states and the readouts; with bf16 inputs each fp32 operand there is carried as a pair of
+ * bf16 values (hi + lo, the fp32 value to 2^-18) and multiplied on the bf16 matrix cores with fp32
+ * sums; dx, dB, dC are rounded to bf16 once. */
 size_t ssd_backward_workspace_bytes(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                                     int64_t ngroups, int64_t chunk_size, int dtype);
 int ssd_backward(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,

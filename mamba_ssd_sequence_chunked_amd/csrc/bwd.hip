@@ -28,9 +28,14 @@
 //
 // The gradient of the log-decays is a suffix sum of differences of two nearly equal products per
 // token, and dA sums it over all tokens: rounding the matrix-core operands to bf16 (as the forward
-// does) leaves ddt and dA with errors of several percent up to several hundred percent, against
-// ~1e-5 in fp32.  Inputs in bf16 are therefore widened to fp32 (exactly) and the whole pass runs
-// on the fp32 matrix-core path; dx, dB and dC are rounded to bf16 once at the end.
+// does) leaves dA with errors up to several times its size (up to ~4e-5 of the size of its terms),
+// against ~1e-8 with fp32 operands.  The recompute, the adjoint chunk states and the two readouts
+// therefore take fp32 operands: on the fp32 matrix cores for fp32 inputs; for bf16 inputs (x, B, C,
+// dy hold bf16 values) each fp32 operand -- the weighted B or C, the decay-weighted C.B^T, the
+// entry and adjoint states -- is split into bf16 hi + lo (the value to 2^-18) and each product is
+// taken twice on the bf16 matrix cores into fp32 sums (dA then within ~1e-7 of its terms' size).
+// The per-head dB / dC passes take plain operands of the inputs' type; dx, dB and dC are rounded
+// to the inputs' type once at the end.
 #include <algorithm>
 
 #include <type_traits>
@@ -76,21 +81,20 @@ __global__ __launch_bounds__(kT) void bwd_tables_kernel(const float* __restrict_
     }
 }
 
-// reversed (front-padded) copies: dy (B, Lp, H, P) in fp32 for the fp32 adjoint readout (if dy_rev is
-// given); B, C (B, Lp, G, N)
-// in TD, which holds their values exactly (the readout's B and C, and the dB pass's C, read per
-// group); in TD (the operand type of the dB / dC passes) dy and u = dt x (B, Lp, H, P); eight
+// reversed (front-padded) copies, inputs in TD: dy (B, Lp, H, P) in fp32 for the fp32 adjoint readout
+// (if dy_rev is given); B, C (B, Lp, G, N) in TD (the readout's B and C, and the dB pass's C, read
+// per group); in TD (the operand type of the later passes) dy and u = dt x (B, Lp, H, P); eight
 // elements per thread
 template <typename TD>
-__global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ x, const float* __restrict__ dt,
-                                                      const float* __restrict__ Bm, const float* __restrict__ Cm,
-                                                      const float* __restrict__ dy, float* __restrict__ dy_rev,
+__global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, const float* __restrict__ dt,
+                                                      const TD* __restrict__ Bm, const TD* __restrict__ Cm,
+                                                      const TD* __restrict__ dy, float* __restrict__ dy_rev,
                                                       TD* __restrict__ B_rev, TD* __restrict__ C_rev,
                                                       TD* __restrict__ dy_revD, TD* __restrict__ u_revD, int batch,
                                                       int64_t L, int nc, int Q, int H, int P, int N, int G)
 {
     const int64_t Lp = (int64_t)nc * Q;
-    // 1. per (b, tau, h): dy_rev (fp32 and TD) and u_rev (TD), P / 8 vectors each
+    // 1. per (b, tau, h): dy_rev (fp32 and TD) and u = dt x reversed (TD), P / 8 vectors each
     const int64_t n1 = (int64_t)batch * Lp * H * (P / 8);
     for (int64_t i = gtid(); i < n1; i += grid_stride()) {
         const int v = (int)(i % (P / 8));
@@ -99,16 +103,17 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
         const int64_t bt = r / H;
         const int64_t b = bt / Lp, tau = bt % Lp;
         const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<float> a, xv;
+        Vec8<float> a;
         Vec8<TD> ad, ud;
         if (t >= 0) {
             const int64_t o = ((b * L + t) * H + h) * P + 8 * v;
-            load8(a, dy + o);
+            Vec8<TD> xv;
+            load8(ad, dy + o);
             load8(xv, x + o);
             const float d = dt[(b * L + t) * H + h];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
-                ad.set(k, a.get(k));
+                a.set(k, ad.get(k));
                 ud.set(k, d * xv.get(k));
             }
         } else {
@@ -129,20 +134,14 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const float* __restrict__ 
         const int64_t bt = r / G;
         const int64_t b = bt / Lp, tau = bt % Lp;
         const int64_t t = unrev(tau, Q, nc, L);
-        Vec8<float> vb, vc;
+        Vec8<TD> ob, oc;
         if (t >= 0) {
             const int64_t o = ((b * L + t) * G + g) * N + 8 * v;
-            load8(vb, Bm + o);
-            load8(vc, Cm + o);
+            load8(ob, Bm + o);
+            load8(oc, Cm + o);
         } else {
-            vb.zero();
-            vc.zero();
-        }
-        Vec8<TD> ob, oc;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            ob.set(k, vb.get(k));
-            oc.set(k, vc.get(k));
+            ob.zero();
+            oc.zero();
         }
         store8(B_rev + r * N + 8 * v, ob);
         store8(C_rev + r * N + 8 * v, oc);
@@ -216,10 +215,11 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
 // per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
 // gradients need: q = dy . yhat - dt x . du and x . du (into qx as (q, x.du)) and x . dy.
 // 16 lanes share a row (P / 16 values each), so a wavefront reads four whole rows per load.
-__global__ __launch_bounds__(kT) void bwd_rows_kernel(const float* __restrict__ x, const float* __restrict__ dt,
-                                                      const float* __restrict__ Dv, const float* __restrict__ dy,
+template <typename TD>
+__global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, const float* __restrict__ dt,
+                                                      const float* __restrict__ Dv, const TD* __restrict__ dy,
                                                       const float* __restrict__ yhat, const float* __restrict__ du_rev,
-                                                      float* __restrict__ dx, float2* __restrict__ qx,
+                                                      TD* __restrict__ dx, float2* __restrict__ qx,
                                                       float* __restrict__ xdy_out, int64_t L, int H, int P, int Q, int nc)
 {
     const int64_t Lp = (int64_t)nc * Q;
@@ -235,16 +235,15 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const float* __restrict__ 
         const float dtv = dt[r], dh = Dv[h];
         float dyy = 0.f, xdu = 0.f, xdy = 0.f;
         for (int p = 4 * sub; p < P; p += 64) {
-            const float4 xv = *reinterpret_cast<const float4*>(x + r * P + p);
-            const float4 dv = *reinterpret_cast<const float4*>(dy + r * P + p);
+            const float4 xv = load4f(x + r * P + p);
+            const float4 dv = load4f(dy + r * P + p);
             const float4 yv = *reinterpret_cast<const float4*>(yhat + r * P + p);
             const float4 uv = *reinterpret_cast<const float4*>(du_rev + rr * P + p);
             dyy += dv.x * yv.x + dv.y * yv.y + dv.z * yv.z + dv.w * yv.w;
             xdu += xv.x * uv.x + xv.y * uv.y + xv.z * uv.z + xv.w * uv.w;
             xdy += xv.x * dv.x + xv.y * dv.y + xv.z * dv.z + xv.w * dv.w;
-            *reinterpret_cast<float4*>(dx + r * P + p) =
-                make_float4(fmaf(dtv, uv.x, dh * dv.x), fmaf(dtv, uv.y, dh * dv.y), fmaf(dtv, uv.z, dh * dv.z),
-                            fmaf(dtv, uv.w, dh * dv.w));
+            store4(dx + r * P + p, fmaf(dtv, uv.x, dh * dv.x), fmaf(dtv, uv.y, dh * dv.y), fmaf(dtv, uv.z, dh * dv.z),
+                   fmaf(dtv, uv.w, dh * dv.w));
         }
         dyy = group_sum<16>(dyy);
         xdu = group_sum<16>(xdu);
@@ -416,7 +415,7 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.GoutT_rev = take(st * elemD);
     w.hfinal = take(B * H * P * N * 4);
     w.yhat = take(B * d.seqlen * H * P * 4);
-    w.dy_rev = take(B * Lp * H * P * 4);
+    w.dy_rev = take(elemD == 4 ? B * Lp * H * P * 4 : 0);        // the fp32 readout's operand only
     w.B_rev = take(B * Lp * G * N * elemD);
     w.C_rev = take(B * Lp * G * N * elemD);
     w.dy_revD = take(B * Lp * H * P * elemD);
@@ -435,16 +434,15 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
 
 namespace {
 
-// The pass on fp32 arrays (x, B, C, dy and the outputs dx, dB, dC), with the dB / dC passes'
-// operands in TD: x_d, dy_d, B_d, C_d are x, dy, B, C in TD (the caller's own arrays when TD is
-// their type).  With bf16 inputs, B and C hold bf16 values, so the fp32 readout passes take them in
-// bf16 and form C.B^T on the bf16 matrix cores (exact products, fp32 sums).
+// The pass on the caller's arrays in TD (x, B, C, dy and the outputs dx, dB, dC).  fp32 inputs take
+// the fp32 matrix-core path for the recompute, the adjoint states and the readouts; bf16 inputs take
+// split bf16 products there (see the header), and bf16 operands for the per-head dB / dC passes.
 template <typename TD>
-hipError_t run_backward(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
-                        const float* D, const float* init, const float* dy, const float* dfinal, const TD* x_d,
-                        const TD* dy_d, const TD* B_d, const TD* C_d, float* dx, float* ddt, float* dA, float* dB,
-                        float* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t s)
+hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* Bm, const TD* Cm, const float* D,
+                        const float* init, const TD* dy, const float* dfinal, TD* dx, float* ddt, float* dA, TD* dB,
+                        TD* dC, float* dD, float* dinit, const Dims& d, void* workspace, hipStream_t s)
 {
+    constexpr bool kBf16 = std::is_same_v<TD, bf16>;
     const BwdLayout w = bwd_layout(d, (int)sizeof(TD));
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
@@ -463,11 +461,12 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     // (bf16 inputs: the fp32 states leave as bf16 hi / lo planes, st elements apart, and the readout
     // passes take split bf16 products)
     const int64_t st = (int64_t)B * nc * H * P * N;
-    SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
-    if constexpr (std::is_same_v<TD, bf16>) {
+    if constexpr (kBf16) {
+        SSD_TRY(launch_chunk_state_cumsum_split(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
         SSD_TRY(launch_state_passing_split(F(w.states), F(w.cs), init, TT(w.entry), st, F(w.hfinal), d, s));
-        SSD_TRY(launch_chunk_scan_split(x_d, B_d, C_d, F(w.dtc), F(w.cs), TT(w.entry), st, zeros, F(w.yhat), d, s));
+        SSD_TRY(launch_chunk_scan_split(x, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), st, zeros, F(w.yhat), d, s));
     } else {
+        SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
         SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
         SSD_TRY(launch_chunk_scan_f32out<float>(x, Bm, Cm, F(w.dtc), F(w.cs), F(w.entry), zeros, F(w.yhat), d, s));
     }
@@ -476,18 +475,19 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     hipLaunchKernelGGL(bwd_tables_kernel, dim3(grid_for(nrows * Q)), dim3(kT), 0, s, F(w.cs), F(w.W), F(w.Z), F(w.dtp),
                        F(w.csp), nrows, (int)L, Q, nc);
     SSD_TRY(hipGetLastError());
-    SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
+    if constexpr (kBf16) SSD_TRY(launch_chunk_state_split(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
+    else SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
     hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
                        (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, (void*)(ws + w.Gout_rev),
                        TT(w.GoutT_rev), dinit, st, B, H, P, N, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
-    float* const dy_rev32 = std::is_same_v<TD, bf16> ? nullptr : F(w.dy_rev);
+    float* const dy_rev32 = kBf16 ? nullptr : F(w.dy_rev);
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, dy_rev32,
                        TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), B, L, nc, Q, H, P, N, G);
     SSD_TRY(hipGetLastError());
-    if constexpr (std::is_same_v<TD, bf16>)
+    if constexpr (kBf16)
         hipLaunchKernelGGL((bwd_transpose_kernel<bf16, bf16>), dim3(grid_for(st)), dim3(kT), 0, s, TT(w.entry),
                            TT(w.SinT), nrows, P, N, nsplit);
     else
@@ -496,7 +496,7 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     SSD_TRY(hipGetLastError());
     // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
-    if constexpr (std::is_same_v<TD, bf16>)
+    if constexpr (kBf16)
         SSD_TRY(launch_chunk_scan_split(TT(w.dy_revD), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev),
                                         st, zeros, F(w.du_rev), dr, s));
     else
@@ -511,7 +511,7 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
         SSD_TRY(launch_chunk_scan_f32out_xl<TD>(TT(w.C_rev) + (int64_t)k * Nh, xg, TT(w.dy_revD), TT(w.u_revD),
                                                 F(w.dtp), F(w.csp), TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P,
                                                 zeros, F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
-        SSD_TRY(launch_chunk_scan_f32out_xl<TD>(B_d + (int64_t)k * Nh, xg, x_d, dy_d, F(w.dtc), F(w.cs),
+        SSD_TRY(launch_chunk_scan_f32out_xl<TD>(Bm + (int64_t)k * Nh, xg, x, dy, F(w.dtc), F(w.cs),
                                                 TT(w.SinT) + (int64_t)k * B * nc * H * Nh * P, zeros,
                                                 F(w.dCh) + (int64_t)k * B * L * H * Nh, dcd, s));
     }
@@ -519,7 +519,7 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     {
         float2* qx = reinterpret_cast<float2*>(F(w.qx));
         float* xdy = F(w.xdy);
-        hipLaunchKernelGGL(bwd_rows_kernel, dim3(grid_for(L * H * 16), (unsigned)B), dim3(kT), 0, s, x, dt, D, dy,
+        hipLaunchKernelGGL((bwd_rows_kernel<TD>), dim3(grid_for(L * H * 16), (unsigned)B), dim3(kT), 0, s, x, dt, D, dy,
                            F(w.yhat), F(w.du_rev), dx, qx, xdy, L, H, P, Q, nc);
         SSD_TRY(hipGetLastError());
         hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, qx, xdy, dfinal,
@@ -527,7 +527,7 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
                            H, P, N);
         SSD_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL((bwd_group_sum_kernel<float>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
+    hipLaunchKernelGGL((bwd_group_sum_kernel<TD>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
                        F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
     SSD_TRY(hipGetLastError());
     hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, reinterpret_cast<double*>(ws + w.dAp),
@@ -537,40 +537,11 @@ hipError_t run_backward(const float* x, const float* dt, const float* A, const f
     return hipSuccess;
 }
 
-__global__ __launch_bounds__(kT) void widen_kernel(const bf16* __restrict__ src, float* __restrict__ dst, int64_t n8)
-{
-    for (int64_t i = gtid(); i < n8; i += grid_stride()) {
-        Vec8<bf16> v;
-        load8(v, src + 8 * i);
-        Vec8<float> f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) f.set(k, v.get(k));
-        store8(dst + 8 * i, f);
-    }
-}
-
-__global__ __launch_bounds__(kT) void narrow_kernel(const float* __restrict__ src, bf16* __restrict__ dst, int64_t n8)
-{
-    for (int64_t i = gtid(); i < n8; i += grid_stride()) {
-        Vec8<float> f;
-        load8(f, src + 8 * i);
-        Vec8<bf16> v;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v.set(k, f.get(k));
-        store8(dst + 8 * i, v);
-    }
-}
-
-size_t up256(int64_t bytes) { return (size_t)((bytes + 255) / 256 * 256); }
-
 }  // namespace
 
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs)
 {
-    const size_t base = bwd_layout(d, bf16_inputs ? 2 : 4).total;
-    if (!bf16_inputs) return base;
-    const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
-    return base + 3 * up256(nx * 4) + 4 * up256(nb * 4);      // x, dy, dx and B, C, dB, dC in fp32
+    return bwd_layout(d, bf16_inputs ? 2 : 4).total;
 }
 
 hipError_t launch_backward_f32(const float* x, const float* dt, const float* A, const float* Bm, const float* Cm,
@@ -578,8 +549,7 @@ hipError_t launch_backward_f32(const float* x, const float* dt, const float* A, 
                                float* ddt, float* dA, float* dB, float* dC, float* dD, float* dinit, const Dims& d,
                                void* workspace, hipStream_t s)
 {
-    return run_backward<float>(x, dt, A, Bm, Cm, D, init, dy, dfinal, x, dy, Bm, Cm, dx, ddt, dA, dB, dC, dD, dinit,
-                               d, workspace, s);
+    return run_backward<float>(x, dt, A, Bm, Cm, D, init, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit, d, workspace, s);
 }
 
 hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* Bm, const bf16* Cm,
@@ -587,29 +557,7 @@ hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, 
                                 float* ddt, float* dA, bf16* dB, bf16* dC, float* dD, float* dinit, const Dims& d,
                                 void* workspace, hipStream_t s)
 {
-    const int64_t nx = d.batch * d.seqlen * d.nheads * d.headdim, nb = d.batch * d.seqlen * d.ngroups * d.dstate;
-    unsigned char* p = static_cast<unsigned char*>(workspace) + bwd_layout(d, 2).total;
-    float* x32 = reinterpret_cast<float*>(p);  p += up256(nx * 4);
-    float* dy32 = reinterpret_cast<float*>(p); p += up256(nx * 4);
-    float* dx32 = reinterpret_cast<float*>(p); p += up256(nx * 4);
-    float* B32 = reinterpret_cast<float*>(p);  p += up256(nb * 4);
-    float* C32 = reinterpret_cast<float*>(p);  p += up256(nb * 4);
-    float* dB32 = reinterpret_cast<float*>(p); p += up256(nb * 4);
-    float* dC32 = reinterpret_cast<float*>(p);
-    // element counts are multiples of 8 (headdim and dstate are multiples of 16)
-    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, x, x32, nx / 8);
-    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dy, dy32, nx / 8);
-    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Bm, B32, nb / 8);
-    hipLaunchKernelGGL(widen_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, Cm, C32, nb / 8);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = run_backward<bf16>(x32, dt, A, B32, C32, D, init, dy32, dfinal, x, dy, Bm, Cm, dx32, ddt, dA, dB32, dC32, dD,
-                           dinit, d, workspace, s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nx / 8)), dim3(kT), 0, s, dx32, dx, nx / 8);
-    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dB32, dB, nb / 8);
-    hipLaunchKernelGGL(narrow_kernel, dim3(grid_for(nb / 8)), dim3(kT), 0, s, dC32, dC, nb / 8);
-    return hipGetLastError();
+    return run_backward<bf16>(x, dt, A, Bm, Cm, D, init, dy, dfinal, dx, ddt, dA, dB, dC, dD, dinit, d, workspace, s);
 }
 
 }  // namespace ssd

@@ -24,6 +24,8 @@
 // tokens past the sequence have w = 0 (their copies come from a clamped,
 // valid row).  Workgroups are numbered head block fastest and renumbered so
 // that consecutive ones share an XCD (and the chunk's B in its L2).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -92,7 +94,10 @@ struct VarlenArgs {
     int nseq;
 };
 
-template <typename T, int P, int NK, int HB, bool kOwnCumsum, bool kVarlen>
+// kSplit (T = bf16, x and B holding bf16 values; the backward's fp32 states): the fp32 product w B is
+// split into bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi), together v to 2^-18) and each product is
+// taken twice on the bf16 matrix cores into the fp32 accumulators.
+template <typename T, int P, int NK, int HB, bool kOwnCumsum, bool kVarlen, bool kSplit = false>
 __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ dt_chunked,
     float* __restrict__ dA_cs, const float* __restrict__ dt, const float* __restrict__ A,
@@ -100,6 +105,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     int nc, int nhb, int hpw, int nblocks)
 {
     static_assert(!kVarlen || kOwnCumsum, "the sequence workgroups form their own prefix sums");
+    static_assert(!kSplit || std::is_same_v<T, bf16>, "split products take bf16 operands");
     using S = StateCfg<T, P, NK, HB>;
     constexpr int EPC = S::EPC, NT = S::NT, PT = S::PT;
     __shared__ __attribute__((aligned(1024))) unsigned char ring[kStages * S::stage_bytes];
@@ -238,12 +244,19 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
         for (int pt = 0; pt < PT; ++pt) swz_row_slots<S::X_CH>(xf[pt], xt, 0, pr + 16 * pt);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            Vec8<T> bf;
+            Vec8<T> bf, bl;                                   // bl: the lo parts (split mode)
             swz_row_slots<S::B_CH>(bf, bt, 0, n0 + 16 * nt);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) bf.set(e, bf.get(e) * wv[e]);
+            for (int e = 0; e < 8; ++e) {
+                const float v = bf.get(e) * wv[e];
+                if constexpr (kSplit) split_set(bf, bl, e, v);
+                else bf.set(e, v);
+            }
 #pragma unroll
-            for (int pt = 0; pt < PT; ++pt) mma(acc[nt][pt], bf, xf[pt]);
+            for (int pt = 0; pt < PT; ++pt) {
+                mma(acc[nt][pt], bf, xf[pt]);
+                if constexpr (kSplit) mma(acc[nt][pt], bl, xf[pt]);
+            }
         }
     }
 
@@ -262,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     }
 }
 
-template <typename T, int P, int NK, bool OWN, bool VARLEN>
+template <typename T, int P, int NK, bool OWN, bool VARLEN, bool SPLIT>
 hipError_t launch(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
                   const VarlenArgs& va, const Dims& d, hipStream_t stream)
 {
@@ -275,20 +288,20 @@ hipError_t launch(const T* x, const T* B, float* dtc, float* cs, const float* dt
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb;
     const int64_t nseqwg = VARLEN ? (int64_t)va.nseq * d.ngroups * nhb : 0;
     if (nblocks + nseqwg == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB, OWN, VARLEN>), dim3((unsigned)(nblocks + nseqwg)),
+    hipLaunchKernelGGL((chunk_state_kernel<T, P, NK, HB, OWN, VARLEN, SPLIT>), dim3((unsigned)(nblocks + nseqwg)),
                        dim3(kThreads), 0, stream, x, B, dtc, cs, dt, A, out, va, (int)d.seqlen, (int)d.nheads,
                        (int)d.ngroups, (int)d.dstate, (int)d.chunk, nc, nhb, hpw, (int)nblocks);
     return hipGetLastError();
 }
 
-template <typename T, bool OWN, bool VARLEN>
+template <typename T, bool OWN, bool VARLEN, bool SPLIT = false>
 hipError_t launch_any(const T* x, const T* B, float* dtc, float* cs, const float* dt, const float* A, float* out,
                       const VarlenArgs& va, const Dims& d, hipStream_t stream)
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
 #define SSD_CS_CASE(PP, KK) \
-    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, OWN, VARLEN>(x, B, dtc, cs, dt, A, out, va, d, stream);
+    if (d.headdim == PP && nki == KK) return launch<T, PP, KK, OWN, VARLEN, SPLIT>(x, B, dtc, cs, dt, A, out, va, d, stream);
 #define SSD_CS_P(PP) SSD_CS_CASE(PP, 1) SSD_CS_CASE(PP, 2) SSD_CS_CASE(PP, 4) SSD_CS_CASE(PP, 8)
     SSD_CS_P(16) SSD_CS_P(32) SSD_CS_P(64) SSD_CS_P(128)
 #undef SSD_CS_P
@@ -312,6 +325,20 @@ hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, co
                                      float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream)
 {
     return launch_any<T, true, false>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, VarlenArgs{}, d, stream);
+}
+
+hipError_t launch_chunk_state_split(const bf16* x, const bf16* B, const float* dt_chunked, const float* dA_cs,
+                                    float* chunk_states, const Dims& d, hipStream_t stream)
+{
+    return launch_any<bf16, false, false, true>(x, B, const_cast<float*>(dt_chunked), const_cast<float*>(dA_cs),
+                                                nullptr, nullptr, chunk_states, VarlenArgs{}, d, stream);
+}
+
+hipError_t launch_chunk_state_cumsum_split(const bf16* x, const bf16* B, const float* dt, const float* A,
+                                           float* dt_chunked, float* dA_cs, float* chunk_states, const Dims& d,
+                                           hipStream_t stream)
+{
+    return launch_any<bf16, true, false, true>(x, B, dt_chunked, dA_cs, dt, A, chunk_states, VarlenArgs{}, d, stream);
 }
 
 template <typename T>

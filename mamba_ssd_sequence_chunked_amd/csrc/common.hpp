@@ -98,6 +98,13 @@ __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float
 __device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
     *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
 }
+// 4 consecutive elements as fp32 (8 B bf16 / 16 B fp32, aligned to that size)
+__device__ __forceinline__ float4 load4f(const bf16* p) {
+    const bf16x4 q = *reinterpret_cast<const bf16x4*>(p);
+    return make_float4(static_cast<float>(q[0]), static_cast<float>(q[1]), static_cast<float>(q[2]),
+                       static_cast<float>(q[3]));
+}
+__device__ __forceinline__ float4 load4f(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
 // acc (16x16 fp32 tile) += A (16 x 32) * B (32 x 16).
 __device__ __forceinline__ void mma(f32x4& acc, const Vec8<bf16>& a, const Vec8<bf16>& b) {

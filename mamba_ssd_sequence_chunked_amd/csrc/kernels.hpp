@@ -31,6 +31,14 @@ template <typename T>
 hipError_t launch_chunk_state_cumsum(const T* x, const T* B, const float* dt, const float* A, float* dt_chunked,
                                      float* dA_cs, float* chunk_states, const Dims& d, hipStream_t stream);
 
+// stage 2 (alone / with stage 1) in fp32 from bf16 products: x and B given in bf16 (arrays that hold bf16
+// values), the weighted B split into bf16 hi + lo (each product to within 2^-18)
+hipError_t launch_chunk_state_split(const bf16* x, const bf16* B, const float* dt_chunked, const float* dA_cs,
+                                    float* chunk_states, const Dims& d, hipStream_t stream);
+hipError_t launch_chunk_state_cumsum_split(const bf16* x, const bf16* B, const float* dt, const float* A,
+                                           float* dt_chunked, float* dA_cs, float* chunk_states, const Dims& d,
+                                           hipStream_t stream);
+
 // packed variable-length batches (d.batch == 1, d.seqlen = total tokens)
 hipError_t launch_varlen_meta(const int* cu_seqlens, int64_t nseq, int64_t total, int64_t chunk, int* tstart,
                               int* cmeta, hipStream_t stream);
@@ -97,14 +105,14 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
-    size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, u_rev, B_rev,
+    size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, B_rev,
         C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, zeros, qx, xdy, dAp, dDp, total;
 };
 BwdLayout bwd_layout(const Dims& d, int elem_bytes);
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
 
-// bf16 inputs: widened to fp32 for the precision-critical parts, the dB / dC passes on the bf16
-// operands, dx / dB / dC rounded back once (see bwd.hip)
+// bf16 inputs: the precision-critical products as split bf16 pairs (fp32 to 2^-18), the dB / dC
+// passes on the bf16 operands, dx / dB / dC rounded to bf16 once (see bwd.hip)
 hipError_t launch_backward_bf16(const bf16* x, const float* dt, const float* A, const bf16* B, const bf16* C,
                                 const float* D, const float* init, const bf16* dy, const float* dfinal, bf16* dx,
                                 float* ddt, float* dA, bf16* dB, bf16* dC, float* dD, float* dinit, const Dims& d,
