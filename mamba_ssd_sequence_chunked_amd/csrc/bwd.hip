@@ -148,41 +148,76 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, 
     }
 }
 
-// S_in^T per chunk and head, split into column halves: (nsplit, B, nc, H, Nh, P) from (B, nc, H, P, N)
-template <typename TS, typename TD>
-__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const TS* __restrict__ src, TD* __restrict__ dst,
+// A state per (b, c, h) block, (P x N) row-major, transposed and split into column halves:
+// dst[((k nblk + blk) Nh + j) P + p] = src[(blk P + p) N + k Nh + j], Nh = N / nsplit.  Workgroup =
+// (block, half, 64-row slice): the slice goes through an LDS tile (4-byte words, rows padded by one
+// word, so both phases are free of bank conflicts) with 16-byte global reads and writes.
+template <typename E>
+__global__ __launch_bounds__(kT) void bwd_transpose_kernel(const E* __restrict__ src, E* __restrict__ dst,
                                                            int64_t nblk, int P, int N, int nsplit)
 {
-    const int Nh = N / nsplit;
-    const int64_t n = (int64_t)nsplit * nblk * Nh * P;
-    for (int64_t i = gtid(); i < n; i += grid_stride()) {
-        const int p = (int)(i % P);
-        int64_t r = i / P;
-        const int j = (int)(r % Nh);
-        r /= Nh;
-        const int64_t blk = r % nblk;              // (b, c, h)
-        const int k = (int)(r / nblk);
-        dst[i] = from_f32<TD>(to_f32(src[(blk * P + p) * N + k * Nh + j]));
+    constexpr int kR = 64;                               // rows per slice
+    constexpr int V = 16 / (int)sizeof(E);               // elements per 16-byte access
+    constexpr int kW = 4 / (int)sizeof(E);               // elements per LDS word
+    __shared__ uint32_t tile[kR * (128 / kW + 1)];
+    const int Nh = N / nsplit, WS = Nh / kW + 1;
+    const int npc = (P + kR - 1) / kR;
+    int64_t id = blockIdx.x;
+    const int pc = (int)(id % npc);
+    id /= npc;
+    const int k = (int)(id % nsplit);
+    const int64_t blk = id / nsplit;
+    const int p0 = pc * kR, rows = min(kR, P - p0);
+    const E* sp = src + (blk * P + p0) * (int64_t)N + k * Nh;
+    for (int i = threadIdx.x; i < rows * (Nh / V); i += kT) {
+        const int r = i / (Nh / V), c = (i % (Nh / V)) * V;
+        const uint4 v = *reinterpret_cast<const uint4*>(sp + (int64_t)r * N + c);
+        uint32_t* t = tile + r * WS + c / kW;
+        t[0] = v.x; t[1] = v.y; t[2] = v.z; t[3] = v.w;
+    }
+    __syncthreads();
+    E* dp = dst + (((int64_t)k * nblk + blk) * Nh) * P + p0;
+    if constexpr (kW == 2) {
+        // a thread takes a column pair (the two halves of a word) and 8 rows: two 16-byte stores
+        for (int i = threadIdx.x; i < (Nh / 2) * (rows / 8); i += kT) {
+            const int pr = (i % (rows / 8)) * 8, n2 = i / (rows / 8);
+            uint32_t w[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) w[e] = tile[(pr + e) * WS + n2];
+            uint4 lo, hi;
+            lo.x = (w[0] & 0xffffu) | (w[1] << 16); hi.x = (w[0] >> 16) | (w[1] & 0xffff0000u);
+            lo.y = (w[2] & 0xffffu) | (w[3] << 16); hi.y = (w[2] >> 16) | (w[3] & 0xffff0000u);
+            lo.z = (w[4] & 0xffffu) | (w[5] << 16); hi.z = (w[4] >> 16) | (w[5] & 0xffff0000u);
+            lo.w = (w[6] & 0xffffu) | (w[7] << 16); hi.w = (w[6] >> 16) | (w[7] & 0xffff0000u);
+            *reinterpret_cast<uint4*>(dp + (int64_t)(2 * n2) * P + pr) = lo;
+            *reinterpret_cast<uint4*>(dp + (int64_t)(2 * n2 + 1) * P + pr) = hi;
+        }
+    } else {
+        for (int i = threadIdx.x; i < Nh * (rows / 4); i += kT) {
+            const int pr = (i % (rows / 4)) * 4, n = i / (rows / 4);
+            uint4 o;
+            o.x = tile[pr * WS + n]; o.y = tile[(pr + 1) * WS + n];
+            o.z = tile[(pr + 2) * WS + n]; o.w = tile[(pr + 3) * WS + n];
+            *reinterpret_cast<uint4*>(dp + (int64_t)n * P + pr) = o;
+        }
     }
 }
 
 // backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
 // order (P x N: fp32, or for TD = bf16 as bf16 hi / lo planes, the lo plane lo_off elements after
-// the hi one) and transposed in TD (split into column halves, N x P); dinit at the end
+// the hi one); dinit at the end
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
                                                          const float* __restrict__ dfinal, void* __restrict__ Gout_rev,
-                                                         TD* __restrict__ GoutT_rev, float* __restrict__ dinit,
-                                                         int64_t lo_off, int batch, int H, int P, int N, int Q, int nc,
-                                                         int nsplit)
+                                                         float* __restrict__ dinit, int64_t lo_off, int H, int P,
+                                                         int N, int Q, int nc)
 {
-    const int PN = P * N, Nh = N / nsplit;
+    const int PN = P * N;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int e = blockIdx.x * (4 * kT) + 4 * threadIdx.x;
     if (e >= PN) return;
     const int64_t bh = b * H + h;
-    const int p = e / N, n0 = e % N;
     float4 s = dfinal ? *reinterpret_cast<const float4*>(dfinal + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = nc - 1; c >= 0; --c) {
         const int cr = nc - 1 - c;
@@ -194,13 +229,6 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
             store4(gh + lo_off, rem(s.x), rem(s.y), rem(s.z), rem(s.w));
         } else {
             store4(static_cast<float*>(Gout_rev) + go, s.x, s.y, s.z, s.w);
-        }
-        const float sv[4] = {s.x, s.y, s.z, s.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = n0 + q, k = n / Nh, j = n % Nh;
-            GoutT_rev[((((int64_t)k * batch + b) * nc + cr) * H + h) * (int64_t)Nh * P + (int64_t)j * P + p] =
-                from_f32<TD>(sv[q]);
         }
         const float4 gh = *reinterpret_cast<const float4*>(Ghat + ((b * nc + c) * H + h) * (int64_t)PN + e);
         const float dec = __expf(cs[(bh * nc + c) * Q + Q - 1]);
@@ -479,7 +507,7 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     else SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
     hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
                        (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, (void*)(ws + w.Gout_rev),
-                       TT(w.GoutT_rev), dinit, st, B, H, P, N, Q, nc, nsplit);
+                       dinit, st, H, P, N, Q, nc);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
@@ -487,12 +515,14 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, dy_rev32,
                        TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), B, L, nc, Q, H, P, N, G);
     SSD_TRY(hipGetLastError());
-    if constexpr (kBf16)
-        hipLaunchKernelGGL((bwd_transpose_kernel<bf16, bf16>), dim3(grid_for(st)), dim3(kT), 0, s, TT(w.entry),
-                           TT(w.SinT), nrows, P, N, nsplit);
-    else
-        hipLaunchKernelGGL((bwd_transpose_kernel<float, float>), dim3(grid_for(st)), dim3(kT), 0, s, F(w.entry),
-                           TT(w.SinT), nrows, P, N, nsplit);
+    // S_in^T and Gout^T (the operands of the dC and dB passes; bf16 inputs: their hi planes)
+    const unsigned ntr = (unsigned)(nrows * nsplit * ((P + 63) / 64));
+    if (ntr > 0) {
+        hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(ntr), dim3(kT), 0, s, TT(w.entry), TT(w.SinT), nrows, P,
+                           N, nsplit);
+        hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(ntr), dim3(kT), 0, s, TT(w.Gout_rev), TT(w.GoutT_rev),
+                           nrows, P, N, nsplit);
+    }
     SSD_TRY(hipGetLastError());
     // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
