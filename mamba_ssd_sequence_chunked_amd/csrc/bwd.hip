@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, 
         }
         if (dy_rev) store8(dy_rev + r * P + 8 * v, a);
         store8(dy_revD + r * P + 8 * v, ad);
-        store8(u_revD + r * P + 8 * v, ud);
+        if (u_revD) store8(u_revD + r * P + 8 * v, ud);
     }
     // 2. per (b, tau, g): B_rev, C_rev (TD: exact, B and C hold values of the inputs' type)
     const int64_t n2 = (int64_t)batch * Lp * G * (N / 8);
@@ -447,10 +447,15 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.B_rev = take(B * Lp * G * N * elemD);
     w.C_rev = take(B * Lp * G * N * elemD);
     w.dy_revD = take(B * Lp * H * P * elemD);
-    w.u_revD = take(B * Lp * H * P * elemD);
+    w.u_revD = take(elemD == 2 && bwd_dbc_supported(d) ? 0 : B * Lp * H * P * elemD);
     w.du_rev = take(B * Lp * H * P * 4);
-    w.dBh_rev = take(B * Lp * H * N * 4);
-    w.dCh = take(B * d.seqlen * H * N * 4);
+    // dB, dC: per-head parts summed afterwards, or (bf16 inputs) the group sums formed in the kernels
+    const bool dbc = elemD == 2 && bwd_dbc_supported(d);
+    w.dBh_rev = take(dbc ? 0 : B * Lp * H * N * 4);
+    w.dCh = take(dbc ? 0 : B * d.seqlen * H * N * 4);
+    w.Mp = take(dbc ? (int64_t)bwd_dbc_slices(d) * B * nc * G * d.chunk * d.chunk * 4 : 0);
+    w.dCi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
+    w.dBi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
     w.zeros = take(std::max<int64_t>(H, 1) * 4);
     w.qx = take(B * d.seqlen * H * 8);
     w.xdy = take(B * d.seqlen * H * 4);
@@ -512,8 +517,10 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     // reversed and per-head copies, S_in^T
     const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
     float* const dy_rev32 = kBf16 ? nullptr : F(w.dy_rev);
+    const bool dbc = kBf16 && bwd_dbc_supported(d);          // dB, dC summed over heads in the kernels
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, dy_rev32,
-                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), TT(w.u_revD), B, L, nc, Q, H, P, N, G);
+                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), dbc ? nullptr : TT(w.u_revD), B, L, nc, Q, H, P, N,
+                       G);
     SSD_TRY(hipGetLastError());
     // S_in^T and Gout^T (the operands of the dC and dB passes; bf16 inputs: their hi planes)
     const unsigned ntr = (unsigned)(nrows * nsplit * ((P + 63) / 64));
@@ -532,12 +539,18 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     else
         SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
                                                 F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
-    // per-head dB (reversed) and dC, contraction over the head dimension, one call per column half;
-    // the x role (C reversed, B) is read from the group's array by every head of the group
+    // dB and dC: the group sums formed in the kernels (bwd_dbc.hip), or per-head dB (reversed) and dC,
+    // contraction over the head dimension, one call per column half, summed over heads afterwards
+    // (the x role, C reversed or B, read from the group's array by every head of the group)
+    if constexpr (kBf16) {
+        if (dbc)
+            SSD_TRY(launch_bwd_dbc(x, dy, Bm, Cm, F(w.dtc), F(w.cs), TT(w.SinT), TT(w.GoutT_rev), F(w.Mp), F(w.dCi),
+                                   F(w.dBi), dB, dC, d, s));
+    }
     const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     const Dims dcd{d.batch, L, d.nheads, Nh, d.headdim, d.nheads, d.chunk};
     const XLayout xg{(int64_t)G * N, H / G, N};
-    for (int k = 0; k < nsplit; ++k) {
+    for (int k = 0; k < (dbc ? 0 : nsplit); ++k) {
         SSD_TRY(launch_chunk_scan_f32out_xl<TD>(TT(w.C_rev) + (int64_t)k * Nh, xg, TT(w.dy_revD), TT(w.u_revD),
                                                 F(w.dtp), F(w.csp), TT(w.GoutT_rev) + (int64_t)k * B * nc * H * Nh * P,
                                                 zeros, F(w.dBh_rev) + (int64_t)k * B * Lp * H * Nh, dbd, s));
@@ -557,9 +570,11 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
                            H, P, N);
         SSD_TRY(hipGetLastError());
     }
-    hipLaunchKernelGGL((bwd_group_sum_kernel<TD>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
-                       F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
-    SSD_TRY(hipGetLastError());
+    if (!dbc) {
+        hipLaunchKernelGGL((bwd_group_sum_kernel<TD>), dim3(grid_for((int64_t)B * L * G * (N / 4))), dim3(kT), 0, s,
+                           F(w.dBh_rev), F(w.dCh), dB, dC, B, L, H, N, G, Q, nc, nsplit);
+        SSD_TRY(hipGetLastError());
+    }
     hipLaunchKernelGGL(bwd_heads_kernel, dim3(1), dim3(kT), 0, s, reinterpret_cast<double*>(ws + w.dAp),
                        reinterpret_cast<double*>(ws + w.dDp), dA, dD, B, H);
     SSD_TRY(hipGetLastError());

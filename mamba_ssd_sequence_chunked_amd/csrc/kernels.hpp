@@ -106,8 +106,16 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
     size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, B_rev,
-        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, zeros, qx, xdy, dAp, dDp, total;
+        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, Mp, dCi, dBi, zeros, qx, xdy, dAp, dDp, total;
 };
+// dB and dC summed over the heads inside the kernels (bwd_dbc.hip): bf16 inputs, headdim % 32 == 0,
+// chunk % 64 == 0; Mp holds bwd_dbc_slices() partial sums of the (B, nc, G, Q, Q) score matrices,
+// dCi / dBi (B, L, G, N) the state terms
+bool bwd_dbc_supported(const Dims& d);
+int bwd_dbc_slices(const Dims& d);
+hipError_t launch_bwd_dbc(const bf16* x, const bf16* dy, const bf16* B, const bf16* C, const float* dtc,
+                          const float* cs, const bf16* SinT, const bf16* GoutT_rev, float* Mp, float* dCi, float* dBi,
+                          bf16* dB, bf16* dC, const Dims& d, hipStream_t stream);
 BwdLayout bwd_layout(const Dims& d, int elem_bytes);
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
 

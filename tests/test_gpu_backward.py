@@ -19,6 +19,13 @@ CASES = [
     (1, 200, 4, 64, 256, 2, 128, "bf16", True, False),
     (2, 77, 6, 128, 16, 3, 64, "f32", False, True),
     (1, 1000, 4, 64, 128, 1, 256, "bf16", True, True),
+    # bf16 shapes for the in-kernel group sums of dB / dC: every head size, state width and chunk
+    # multiple of 64, groups, and 32 heads per group (partial sums over two slices of the heads)
+    (1, 300, 32, 32, 64, 1, 64, "bf16", True, True),
+    (2, 200, 6, 128, 32, 3, 192, "bf16", False, True),
+    (1, 130, 4, 32, 16, 2, 64, "bf16", True, False),
+    # and one the per-head passes take (chunk not a multiple of 64, head size 16)
+    (1, 100, 4, 16, 32, 1, 32, "bf16", False, True),
 ]
 
 
