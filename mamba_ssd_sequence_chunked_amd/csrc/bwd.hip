@@ -241,14 +241,15 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
 }
 
 // per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
-// gradients need: q = dy . yhat - dt x . du and x . du (into qx as (q, x.du)) and x . dy.
+// gradients need: dy . yhat, x . du and x . dy.
 // 16 lanes share a row (P / 16 values each), so a wavefront reads four whole rows per load.
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, const float* __restrict__ dt,
                                                       const float* __restrict__ Dv, const TD* __restrict__ dy,
                                                       const float* __restrict__ yhat, const float* __restrict__ du_rev,
-                                                      TD* __restrict__ dx, float2* __restrict__ qx,
-                                                      float* __restrict__ xdy_out, int64_t L, int H, int P, int Q, int nc)
+                                                      TD* __restrict__ dx, float* __restrict__ yd_out,
+                                                      float* __restrict__ xdu_out, float* __restrict__ xdy_out, int64_t L,
+                                                      int H, int P, int Q, int nc)
 {
     const int64_t Lp = (int64_t)nc * Q;
     const int64_t b = blockIdx.y;                                // one grid row per batch row
@@ -277,18 +278,21 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, 
         xdu = group_sum<16>(xdu);
         xdy = group_sum<16>(xdy);
         if (sub == 0) {
-            qx[r] = make_float2(dyy - dtv * xdu, xdu);
+            yd_out[r] = dyy;
+            xdu_out[r] = xdu;
             xdy_out[r] = xdy;
         }
     }
 }
 
-// per (b, h): the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
+// per (b, h): with q_t = dy_t . yhat_t - dt_t x_t . du_t,
+// the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
 // and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.  Thread i takes the 16 tokens
 // ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.  The sums
 // run in fp64: dA adds up terms that cancel to a few parts in a thousand of their magnitude.
 __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dt, const float* __restrict__ A,
-                                                      const float2* __restrict__ qx, const float* __restrict__ xdy,
+                                                      const float* __restrict__ yd, const float* __restrict__ xdu,
+                                                      const float* __restrict__ xdy,
                                                       const float* __restrict__ dfinal,
                                                       const float* __restrict__ hfinal, float* __restrict__ ddt,
                                                       double* __restrict__ dAp, double* __restrict__ dDp, int64_t L,
@@ -334,14 +338,16 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
-            float2 v = make_float2(0.f, 0.f);
+            float q = 0.f, xu = 0.f;
             if (t >= 0 && t < L) {
-                v = qx[(b * L + t) * H + h];
-                dD_acc += xdy[(b * L + t) * H + h];
+                const int64_t r = (b * L + t) * H + h;
+                xu = xdu[r];
+                q = yd[r] - dt[r] * xu;
+                dD_acc += xdy[r];
             }
-            qs[k] = v.x;
-            xs[k] = v.y;
-            own += v.x;
+            qs[k] = q;
+            xs[k] = xu;
+            own += q;
         }
         const double incl = block_scan(own);
         const double total = sc[kT - 1];
@@ -442,13 +448,14 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.Gout_rev = take(st * 4);
     w.GoutT_rev = take(st * elemD);
     w.hfinal = take(B * H * P * N * 4);
-    w.yhat = take(B * d.seqlen * H * P * 4);
+    w.yhat = take(elemD == 4 ? B * d.seqlen * H * P * 4 : 0);          // fp32 pass only (the bf16 one
+                                                                       // reduces yhat and du in place)
     w.dy_rev = take(elemD == 4 ? B * Lp * H * P * 4 : 0);        // the fp32 readout's operand only
     w.B_rev = take(B * Lp * G * N * elemD);
     w.C_rev = take(B * Lp * G * N * elemD);
     w.dy_revD = take(B * Lp * H * P * elemD);
     w.u_revD = take(elemD == 2 && bwd_dbc_supported(d) ? 0 : B * Lp * H * P * elemD);
-    w.du_rev = take(B * Lp * H * P * 4);
+    w.du_rev = take(elemD == 4 ? B * Lp * H * P * 4 : 0);
     // dB, dC: per-head parts summed afterwards, or (bf16 inputs) the group sums formed in the kernels
     const bool dbc = elemD == 2 && bwd_dbc_supported(d);
     w.dBh_rev = take(dbc ? 0 : B * Lp * H * N * 4);
@@ -457,7 +464,8 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.dCi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
     w.dBi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
     w.zeros = take(std::max<int64_t>(H, 1) * 4);
-    w.qx = take(B * d.seqlen * H * 8);
+    w.yd = take(B * d.seqlen * H * 4);
+    w.xdu = take(B * d.seqlen * H * 4);
     w.xdy = take(B * d.seqlen * H * 4);
     w.dAp = take(B * H * 8);
     w.dDp = take(B * H * 8);
@@ -497,7 +505,9 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     if constexpr (kBf16) {
         SSD_TRY(launch_chunk_state_cumsum_split(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
         SSD_TRY(launch_state_passing_split(F(w.states), F(w.cs), init, TT(w.entry), st, F(w.hfinal), d, s));
-        SSD_TRY(launch_chunk_scan_split(x, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), st, zeros, F(w.yhat), d, s));
+        // yhat is reduced to dy . yhat per (token, head) as it leaves the accumulators
+        const ScanEpi ey{dy, x, dt, D, nullptr, F(w.yd), nullptr, L};
+        SSD_TRY(launch_chunk_scan_split_dot(x, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), st, zeros, ey, d, s));
     } else {
         SSD_TRY(launch_chunk_state_cumsum<float>(x, Bm, dt, A, F(w.dtc), F(w.cs), F(w.states), d, s));
         SSD_TRY(launch_state_passing<float>(F(w.states), F(w.cs), init, F(w.entry), F(w.hfinal), d, s));
@@ -533,10 +543,12 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     SSD_TRY(hipGetLastError());
     // du: the adjoint readout, on the reversed sequence, in fp32
     const Dims dr{d.batch, Lp, d.nheads, d.headdim, d.dstate, d.ngroups, d.chunk};
-    if constexpr (kBf16)
-        SSD_TRY(launch_chunk_scan_split(TT(w.dy_revD), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev),
-                                        st, zeros, F(w.du_rev), dr, s));
-    else
+    if constexpr (kBf16) {
+        // du leaves the accumulators as dx = dt du + D dy, x . du and x . dy
+        const ScanEpi eu{dy, x, dt, D, dx, F(w.xdu), F(w.xdy), L};
+        SSD_TRY(launch_chunk_scan_split_grad(TT(w.dy_revD), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp),
+                                             TT(w.Gout_rev), st, zeros, eu, dr, s));
+    } else
         SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
                                                 F(w.Gout_rev), zeros, F(w.du_rev), dr, s));
     // dB and dC: the group sums formed in the kernels (bwd_dbc.hip), or per-head dB (reversed) and dC,
@@ -560,12 +572,13 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     }
     // per token (all rows in parallel), then the suffix sums per (b, h), then the group and batch sums
     {
-        float2* qx = reinterpret_cast<float2*>(F(w.qx));
-        float* xdy = F(w.xdy);
-        hipLaunchKernelGGL((bwd_rows_kernel<TD>), dim3(grid_for(L * H * 16), (unsigned)B), dim3(kT), 0, s, x, dt, D, dy,
-                           F(w.yhat), F(w.du_rev), dx, qx, xdy, L, H, P, Q, nc);
-        SSD_TRY(hipGetLastError());
-        hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, qx, xdy, dfinal,
+        if (!kBf16) {
+            hipLaunchKernelGGL((bwd_rows_kernel<TD>), dim3(grid_for(L * H * 16), (unsigned)B), dim3(kT), 0, s, x, dt, D,
+                               dy, F(w.yhat), F(w.du_rev), dx, F(w.yd), F(w.xdu), F(w.xdy), L, H, P, Q, nc);
+            SSD_TRY(hipGetLastError());
+        }
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, F(w.yd), F(w.xdu), F(w.xdy),
+                           dfinal,
                            F(w.hfinal), ddt, reinterpret_cast<double*>(ws + w.dAp), reinterpret_cast<double*>(ws + w.dDp), L,
                            H, P, N);
         SSD_TRY(hipGetLastError());

@@ -150,12 +150,14 @@ __device__ __forceinline__ Vec8<float> as_t(const Vec8<bf16>& f, float) {
 // ones, with x, B, C holding bf16 values: S_in comes as two bf16 planes, hi at entry and lo at
 // entry + lo_off (hi + lo = the fp32 state to 2^-18), G is split the same way in registers, and
 // each product is taken twice on the bf16 matrix cores (hi, then lo) into the fp32 accumulators.
-template <typename T, typename TB, typename TY, int P, int NK, class S, bool kVarlen>
+// EPI (split mode): 0 stores y; 1 and 2 reduce it per (token, head) as ScanEpi describes (kernels.hpp).
+template <typename T, typename TB, typename TY, int P, int NK, class S, bool kVarlen, int EPI = 0>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     const T* __restrict__ x, const TB* __restrict__ Bm, const TB* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, int64_t lo_off, const float* __restrict__ Dv, const int* __restrict__ tstart,
-    TY* __restrict__ y, XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks)
+    TY* __restrict__ y, XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks,
+    ScanEpi epi)
 {
     constexpr int EPC = S::EPC, HB = S::kHeads, kStages = S::kStages, SW = S::SWD;
     __shared__ __attribute__((aligned(16))) float cst[HB * kMaxQ];
@@ -442,7 +444,69 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         }
     }
 
-    {
+    if constexpr (EPI == 1) {
+        // o1 = dy . y per (token, head): 4 columns per lane and tile, then the 4 lanes of a row
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 16 * rbk[j] + r16;
+            const bool rok = has[j] && row < len;
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) {
+                const bool ok = rok && hh < nh;
+                const int64_t r = (b * seqlen + t0 + min(row, len - 1)) * nheads + h0 + min(hh, nh - 1);
+                float dot = 0.f;
+                if (ok) {
+                    const bf16* dr = epi.dy + r * P + 4 * grp;
+#pragma unroll
+                    for (int pt = 0; pt < P / 16; ++pt) {
+                        const float4 d4 = load4f(dr + 16 * pt);
+                        const f32x4 v = acc[j][hh][pt];
+                        dot += v[0] * d4.x + v[1] * d4.y + v[2] * d4.z + v[3] * d4.w;
+                    }
+                }
+                dot += __shfl_xor(dot, 16, kWave);
+                dot += __shfl_xor(dot, 32, kWave);
+                if (ok && grp == 0) epi.o1[r] = dot;
+            }
+        }
+    } else if constexpr (EPI == 2) {
+        // du on the reversed sequence: row t0 + row is the caller's token seqlen - 1 - (t0 + row)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int row = 16 * rbk[j] + r16;
+            const int64_t t = (int64_t)seqlen - 1 - (t0 + row);
+            const bool rok = has[j] && row < len && t >= 0 && t < epi.L;
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh) {
+                const bool ok = rok && hh < nh;
+                const int h = h0 + min(hh, nh - 1);
+                const int64_t r = (b * epi.L + min(max(t, (int64_t)0), epi.L - 1)) * nheads + h;
+                float xu = 0.f, xd = 0.f;
+                if (ok) {
+                    const float dtv = epi.dt[r], dh = epi.D[h];
+                    const int64_t o = r * P + 4 * grp;
+#pragma unroll
+                    for (int pt = 0; pt < P / 16; ++pt) {
+                        const float4 x4 = load4f(epi.x + o + 16 * pt);
+                        const float4 d4 = load4f(epi.dy + o + 16 * pt);
+                        const f32x4 u = acc[j][hh][pt];
+                        store4(epi.dx + o + 16 * pt, fmaf(dtv, u[0], dh * d4.x), fmaf(dtv, u[1], dh * d4.y),
+                               fmaf(dtv, u[2], dh * d4.z), fmaf(dtv, u[3], dh * d4.w));
+                        xu += x4.x * u[0] + x4.y * u[1] + x4.z * u[2] + x4.w * u[3];
+                        xd += x4.x * d4.x + x4.y * d4.y + x4.z * d4.z + x4.w * d4.w;
+                    }
+                }
+                xu += __shfl_xor(xu, 16, kWave);
+                xu += __shfl_xor(xu, 32, kWave);
+                xd += __shfl_xor(xd, 16, kWave);
+                xd += __shfl_xor(xd, 32, kWave);
+                if (ok && grp == 0) {
+                    epi.o1[r] = xu;
+                    epi.o2[r] = xd;
+                }
+            }
+        }
+    } else {
         TY* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc(yb, 0, len * nheads * P * (int)sizeof(TY), kBufferDword3);
@@ -463,10 +527,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 }
 
-template <typename T, typename TB, typename TY, int P, int NK, bool V, class S>
+template <typename T, typename TB, typename TY, int P, int NK, bool V, class S, int EPI>
 hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                         int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
-                        hipStream_t stream)
+                        hipStream_t stream, const ScanEpi& epi)
 {
     static_assert(S::fits, "LDS budget");
     static_assert(!S::kSplit || (std::is_same_v<T, bf16> && std::is_same_v<TB, bf16> && std::is_same_v<TY, float>),
@@ -480,41 +544,42 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
     const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V, EPI>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
-                       (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks);
+                       (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks, epi);
     return hipGetLastError();
 }
 
 // groups of a single head (the backward's per-head passes) take the one-head shape: a wider one
 // would compute a clamped copy of the head in its other slots
-template <typename T, typename TB, typename TY, int P, int NK, bool V, int SP>
+template <typename T, typename TB, typename TY, int P, int NK, bool V, int SP, int EPI>
 hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                   int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
-                  hipStream_t stream)
+                  hipStream_t stream, const ScanEpi& epi)
 {
     using S = ScanShape<T, TB, P, NK, V, SP>;
     if constexpr (S::kHeads > 1) {
         if (d.nheads == d.ngroups) {
             using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V, SP>())::type;
-            return launch_shape<T, TB, TY, P, NK, V, S1>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d,
-                                                         stream);
+            return launch_shape<T, TB, TY, P, NK, V, S1, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d,
+                                                              stream, epi);
         }
     }
-    return launch_shape<T, TB, TY, P, NK, V, S>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream);
+    return launch_shape<T, TB, TY, P, NK, V, S, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream,
+                                                     epi);
 }
 
-template <typename T, typename TB, typename TY, bool V, int SP = 1>
+template <typename T, typename TB, typename TY, bool V, int SP = 1, int EPI = 0>
 hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
                       const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream,
-                      XLayout xl = XLayout{0, 0, 0}, int64_t lo_off = 0)
+                      XLayout xl = XLayout{0, 0, 0}, int64_t lo_off = 0, const ScanEpi& epi = ScanEpi{})
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
     if (xl.hdiv == 0) xl = XLayout{d.nheads * d.headdim, 1, (int)d.headdim};     // x in (B, L, H, P)
 #define SSD_SCAN_CASE(PP, KK) \
     if (d.headdim == PP && nki == KK) \
-        return launch<T, TB, TY, PP, KK, V, SP>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream);
+        return launch<T, TB, TY, PP, KK, V, SP, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream, epi);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -561,6 +626,22 @@ hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, 
 {
     return launch_any<bf16, bf16, float, false, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, y, d, stream,
                                                    XLayout{0, 0, 0}, lo_off);
+}
+
+hipError_t launch_chunk_scan_split_dot(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                       const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
+                                       const ScanEpi& epi, const Dims& d, hipStream_t stream)
+{
+    return launch_any<bf16, bf16, float, false, 2, 1>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
+                                                      stream, XLayout{0, 0, 0}, lo_off, epi);
+}
+
+hipError_t launch_chunk_scan_split_grad(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                        const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
+                                        const ScanEpi& epi, const Dims& d, hipStream_t stream)
+{
+    return launch_any<bf16, bf16, float, false, 2, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
+                                                      stream, XLayout{0, 0, 0}, lo_off, epi);
 }
 
 template <typename T>

@@ -93,6 +93,26 @@ hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf1
 hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
                                    const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
                                    const Dims& d, hipStream_t stream);
+// The backward's readout passes with the per-token work folded into the output stage (y not stored):
+//   ..._dot:  o1[b, t, h] = sum_p dy[b, t, h, p] y[b, t, h, p]
+//   ..._grad: y = du on the time-reversed, front-padded sequence (token t = Lp - 1 - row, pads
+//             skipped): dx = dt du + D dy (bf16), o1 = x . du, o2 = x . dy per (b, t, h)
+struct ScanEpi {
+    const bf16* dy;
+    const bf16* x;
+    const float* dt;      // (B, L, H)
+    const float* D;       // (H)
+    bf16* dx;
+    float* o1;
+    float* o2;
+    int64_t L;            // the caller's sequence length
+};
+hipError_t launch_chunk_scan_split_dot(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                       const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
+                                       const ScanEpi& epi, const Dims& d, hipStream_t stream);
+hipError_t launch_chunk_scan_split_grad(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
+                                        const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
+                                        const ScanEpi& epi, const Dims& d, hipStream_t stream);
 
 template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
@@ -106,7 +126,7 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
     size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, B_rev,
-        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, Mp, dCi, dBi, zeros, qx, xdy, dAp, dDp, total;
+        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, Mp, dCi, dBi, zeros, yd, xdu, xdy, dAp, dDp, total;
 };
 // dB and dC summed over the heads inside the kernels (bwd_dbc.hip): bf16 inputs, headdim % 32 == 0,
 // chunk % 64 == 0; Mp holds bwd_dbc_slices() partial sums of the (B, nc, G, Q, Q) score matrices,
