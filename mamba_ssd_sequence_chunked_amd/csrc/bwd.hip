@@ -107,14 +107,15 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, 
         Vec8<TD> ad, ud;
         if (t >= 0) {
             const int64_t o = ((b * L + t) * H + h) * P + 8 * v;
-            Vec8<TD> xv;
             load8(ad, dy + o);
-            load8(xv, x + o);
-            const float d = dt[(b * L + t) * H + h];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                a.set(k, ad.get(k));
-                ud.set(k, d * xv.get(k));
+            for (int k = 0; k < 8; ++k) a.set(k, ad.get(k));
+            if (u_revD) {
+                Vec8<TD> xv;
+                load8(xv, x + o);
+                const float d = dt[(b * L + t) * H + h];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) ud.set(k, d * xv.get(k));
             }
         } else {
             a.zero();

@@ -11,7 +11,7 @@
 // with M = sum over the group's heads of M_h (one Q x Q matrix per batch, chunk and group),
 // S_in,h the state entering the chunk and Gout_h the adjoint state that reaches the chunk's last
 // token from later ones.  Three kernels:
-//   bwd_score   M, per (batch, chunk, group, 64-row block, slice of the heads): per head, the
+//   bwd_score   M, per (batch, chunk, group, 128-row block, slice of the heads): per head, the
 //               products dy x^T on the matrix cores (bf16, fp32 sums), then decay and mask in fp32
 //               added into fp32 accumulators; the slices' partial sums go to workspace
 //   bwd_inter   the two state terms, per (batch, chunk, group, 64-row block, half of the state
@@ -33,16 +33,16 @@ namespace ssd {
 namespace {
 
 constexpr int kMaxQ = 256;
-constexpr int kT = 256;                 // 4 wavefronts
-constexpr int kWaves = 4;
+constexpr int kT = 256;                 // bwd_inter, bwd_dbc: 4 wavefronts (64 rows)
+constexpr int kW8 = 8;                  // bwd_score: 8 wavefronts (128 rows)
 
 // Copy rows [0, nrows) of a (rows x CH chunks) swizzled tile, row r from src(r) (a pointer to the
-// row's first element; rows are clamped by the caller), over the workgroup's wavefronts.
-template <int CH, class F>
+// row's first element; rows are clamped by the caller), over the workgroup's NW wavefronts.
+template <int CH, int NW, class F>
 __device__ __forceinline__ void rows_load_async(unsigned base, int nrows, int wu, int lane, F src) {
     using TL = SwzTile<CH>;
     const int ninst = nrows * CH / 64;
-    for (int i = wu; i < ninst; i += kWaves) {
+    for (int i = wu; i < ninst; i += NW) {
         const int pos = i * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
         dma16(src(r) + 8 * (slot ^ (r & TL::kMask)), base + i * 1024u);
@@ -58,14 +58,14 @@ __device__ __forceinline__ void tables_load_async(const float* cs_row, const flo
 }
 
 // ---------------------------------------------------------------------------------------------
-// M partial sums.  Wavefront w of row block rb owns rows l = 16 (4 rb + w) + r16 and the column
-// tiles ct <= 4 rb + w (s < 16 (4 rb + w + 1)); the accumulator of tile ct holds, per lane, row l
+// M partial sums.  Wavefront w of row block rb owns rows l = 16 (8 rb + w) + r16 and the column
+// tiles ct <= 8 rb + w (s < 16 (8 rb + w + 1)); the accumulator of tile ct holds, per lane, row l
 // and columns s = 16 ct + 4 grp + q.  Products are formed as T[s][l] = x_s . dy_l (x rows from the
 // LDS tile, dy rows in registers); for a tile wholly before the rows the decay is split at the
 // tile's last token e: exp(cs[l] - cs[e]) per row times exp(cs[e] - cs[s]) dt[s] per token
 // (tabulated per head), both exponents <= 0; the diagonal tile takes the full decay and the mask.
 template <int P>
-__global__ __launch_bounds__(kT, 2) void bwd_score_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
+__global__ __launch_bounds__(64 * kW8, 1) void bwd_score_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                           const float* __restrict__ dtc, const float* __restrict__ cs,
                                                           float* __restrict__ Mp, int batch, int64_t L, int H, int G,
                                                           int Q, int nc, int nrb, int nsl, int hps, int nblocks)
@@ -89,9 +89,9 @@ __global__ __launch_bounds__(kT, 2) void bwd_score_kernel(const bf16* __restrict
     const int len = (int)min((int64_t)Q, L - t0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
-    const int rbl = 4 * rb + wu;                         // this wavefront's 16-row block
+    const int rbl = kW8 * rb + wu;                       // this wavefront's 16-row block
     const int l = 16 * rbl + r16;
-    const int nrows = min(64 * rb + 64, Q);               // x rows the workgroup reads
+    const int nrows = min(16 * kW8 * (rb + 1), Q);        // x rows the workgroup reads
 
     const __amdgpu_buffer_rsrc_t rdy = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<bf16*>(dy + (b * L + t0) * H * P), 0, len * H * P * 2, kBufferDword3);
@@ -104,8 +104,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_score_kernel(const bf16* __restrict
     auto issue = [&](int j, int q) {
         const int h = g * hpg + j;
         const bf16* xs = x + ((b * L + t0) * H + h) * (int64_t)P;
-        rows_load_async<CH>(lds_addr(xt[q]), nrows, wu, lane,
-                            [&](int r) { return xs + (int64_t)min(r, len - 1) * H * P; });
+        rows_load_async<CH, kW8>(lds_addr(xt[q]), nrows, wu, lane,
+                                 [&](int r) { return xs + (int64_t)min(r, len - 1) * H * P; });
         const int64_t row = ((b * H + h) * nc + c) * (int64_t)Q;
         tables_load_async(cs + row, dtc + row, lds_addr(tab[q][0]), lds_addr(tab[q][1]), wu, lane, Q);
     };
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_score_kernel(const bf16* __restrict
         const float* cst = tab[q][0];
         const float* dtt = tab[q][1];
         // per-token factor exp(cs[e] - cs[s]) dt[s], e = last token of s's 16-token tile
-        for (int s = tid; s < Q; s += kT) vt[s] = __expf(cst[(s | 15)] - cst[s]) * dtt[s];
+        for (int s = tid; s < Q; s += 64 * kW8) vt[s] = __expf(cst[(s | 15)] - cst[s]) * dtt[s];
         __syncthreads();
         const float csl = cst[min(l, Q - 1)];
 #pragma unroll
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
     const int len = (int)min((int64_t)Q, L - t0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
     const int wu = __builtin_amdgcn_readfirstlane(wave);
-    const int l = 64 * rb + 16 * wave + r16;
+    const int l = 16 * (4 * rb + wave) + r16;
     const bool lok = l < len;
 
     const int64_t rbase = (b * L + t0) * H * P;
@@ -229,8 +229,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
         const int h = g * hpg + j;
         const bf16* sp = SinT + ((((int64_t)k * batch + b) * nc + c) * H + h) * (int64_t)NH * P;
         const bf16* gp = GoutT + ((((int64_t)k * batch + b) * nc + (nc - 1 - c)) * H + h) * (int64_t)NH * P;
-        rows_load_async<CH>(lds_addr(tiles[q][0]), NH, wu, lane, [&](int r) { return sp + (int64_t)r * P; });
-        rows_load_async<CH>(lds_addr(tiles[q][1]), NH, wu, lane, [&](int r) { return gp + (int64_t)r * P; });
+        rows_load_async<CH, 4>(lds_addr(tiles[q][0]), NH, wu, lane, [&](int r) { return sp + (int64_t)r * P; });
+        rows_load_async<CH, 4>(lds_addr(tiles[q][1]), NH, wu, lane, [&](int r) { return gp + (int64_t)r * P; });
         const int64_t row = ((b * H + h) * nc + c) * (int64_t)Q;
         tables_load_async(cs + row, dtc + row, lds_addr(tab[q][0]), lds_addr(tab[q][1]), wu, lane, Q);
     };
@@ -323,8 +323,8 @@ __global__ __launch_bounds__(kT) void bwd_dbc_kernel(const bf16* __restrict__ Bm
     // the chunk's B and C rows (state columns of this half), rows past the sequence clamped
     const bf16* bg = Bm + ((b * L + t0) * G + g) * (int64_t)N + k * NH;
     const bf16* cg = Cm + ((b * L + t0) * G + g) * (int64_t)N + k * NH;
-    rows_load_async<CHN>(lds_addr(bt), Q, wu, lane, [&](int rr) { return bg + (int64_t)min(rr, len - 1) * G * N; });
-    rows_load_async<CHN>(lds_addr(ctl), Q, wu, lane, [&](int rr) { return cg + (int64_t)min(rr, len - 1) * G * N; });
+    rows_load_async<CHN, 4>(lds_addr(bt), Q, wu, lane, [&](int rr) { return bg + (int64_t)min(rr, len - 1) * G * N; });
+    rows_load_async<CHN, 4>(lds_addr(ctl), Q, wu, lane, [&](int rr) { return cg + (int64_t)min(rr, len - 1) * G * N; });
     wait_vmem();
     __syncthreads();
 
@@ -402,14 +402,14 @@ hipError_t launch_pn(const bf16* x, const bf16* dy, const bf16* B, const bf16* C
                      int nsl, const Dims& d, hipStream_t s)
 {
     const int nc = (int)d.nchunks(), Q = (int)d.chunk, G = (int)d.ngroups, H = (int)d.nheads, N = (int)d.dstate;
-    const int nrb = Q / 64, nsplit = N / (16 * NT), hpg = H / G;
+    const int nrb = Q / 64, nrb8 = (Q + 16 * kW8 - 1) / (16 * kW8), nsplit = N / (16 * NT), hpg = H / G;
     const int hps = (hpg + nsl - 1) / nsl;
     const int64_t ngroups_all = d.batch * nc * G;
-    const int nb_score = (int)(ngroups_all * nrb * nsl);
+    const int nb_score = (int)(ngroups_all * nrb8 * nsl);
     const int nb_inter = (int)(ngroups_all * nrb * nsplit);
     if (nb_score == 0) return hipSuccess;
-    hipLaunchKernelGGL((bwd_score_kernel<P>), dim3(nb_score), dim3(kT), 0, s, x, dy, dtc, cs, Mp, (int)d.batch,
-                       d.seqlen, H, G, Q, nc, nrb, nsl, hps, nb_score);
+    hipLaunchKernelGGL((bwd_score_kernel<P>), dim3(nb_score), dim3(64 * kW8), 0, s, x, dy, dtc, cs, Mp, (int)d.batch,
+                       d.seqlen, H, G, Q, nc, nrb8, nsl, hps, nb_score);
     hipLaunchKernelGGL((bwd_inter_kernel<P, NT>), dim3(nb_inter), dim3(kT), 0, s, x, dy, dtc, cs, SinT, GoutT_rev,
                        dCi, dBi, (int)d.batch, d.seqlen, H, G, N, Q, nc, nrb, nsplit, nb_inter);
     hipLaunchKernelGGL((bwd_dbc_kernel<NT>), dim3(nb_inter), dim3(kT), 0, s, B, C, Mp, dCi, dBi, dB, dC,

@@ -445,7 +445,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 
     if constexpr (EPI == 1) {
-        // o1 = dy . y per (token, head): 4 columns per lane and tile, then the 4 lanes of a row
+        // o1 = dy . y per (token, head), from the accumulator layout: 4 columns per lane and tile,
+        // then the 4 lanes of a row
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int row = 16 * rbk[j] + r16;
@@ -470,40 +471,67 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             }
         }
     } else if constexpr (EPI == 2) {
-        // du on the reversed sequence: row t0 + row is the caller's token seqlen - 1 - (t0 + row)
+        // dx, x . du, x . dy per (token, head): each wavefront passes its 16-row tiles through LDS (the
+        // ring is free now) and reads them back row-major, CPR lanes per row with 8 consecutive columns
+        // each, so the reads of x and dy and the stores of dx are whole 16-byte pieces of whole rows.
+        constexpr int kPitch = P + 4;                          // floats per staged row
+        constexpr int CPR = P / 8;                             // lanes per row
+        constexpr int RPI = 64 / CPR;                          // rows per pass
+        constexpr int kIter = (16 + RPI - 1) / RPI;
+        static_assert(kWaves * 16 * kPitch * 4 <= S::region, "epilogue staging");
+        float* const ep = reinterpret_cast<float*>(region) + wave * 16 * kPitch;
+        __syncthreads();                                       // every wavefront is done with the ring
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int row = 16 * rbk[j] + r16;
-            const int64_t t = (int64_t)seqlen - 1 - (t0 + row);
-            const bool rok = has[j] && row < len && t >= 0 && t < epi.L;
 #pragma unroll
             for (int hh = 0; hh < HB; ++hh) {
-                const bool ok = rok && hh < nh;
-                const int h = h0 + min(hh, nh - 1);
-                const int64_t r = (b * epi.L + min(max(t, (int64_t)0), epi.L - 1)) * nheads + h;
-                float xu = 0.f, xd = 0.f;
-                if (ok) {
-                    const float dtv = epi.dt[r], dh = epi.D[h];
-                    const int64_t o = r * P + 4 * grp;
 #pragma unroll
-                    for (int pt = 0; pt < P / 16; ++pt) {
-                        const float4 x4 = load4f(epi.x + o + 16 * pt);
-                        const float4 d4 = load4f(epi.dy + o + 16 * pt);
-                        const f32x4 u = acc[j][hh][pt];
-                        store4(epi.dx + o + 16 * pt, fmaf(dtv, u[0], dh * d4.x), fmaf(dtv, u[1], dh * d4.y),
-                               fmaf(dtv, u[2], dh * d4.z), fmaf(dtv, u[3], dh * d4.w));
-                        xu += x4.x * u[0] + x4.y * u[1] + x4.z * u[2] + x4.w * u[3];
-                        xd += x4.x * d4.x + x4.y * d4.y + x4.z * d4.z + x4.w * d4.w;
+                for (int pt = 0; pt < P / 16; ++pt)
+                    *reinterpret_cast<f32x4*>(ep + r16 * kPitch + 16 * pt + 4 * grp) = acc[j][hh][pt];
+                __syncthreads();
+                const int h = h0 + min(hh, nh - 1);
+#pragma unroll
+                for (int it = 0; it < kIter; ++it) {
+                    const int rr = it * RPI + lane / CPR, cc = 8 * (lane % CPR);
+                    const int row = 16 * rbk[j] + rr;
+                    float v[8];
+                    {
+                        const float* e = ep + min(rr, 15) * kPitch + cc;
+                        const float4 a = *reinterpret_cast<const float4*>(e);
+                        const float4 b4 = *reinterpret_cast<const float4*>(e + 4);
+                        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                        v[4] = b4.x; v[5] = b4.y; v[6] = b4.z; v[7] = b4.w;
+                    }
+                    // du on the reversed sequence: row t0 + row is the caller's token seqlen - 1 - (t0 + row)
+                    float s1 = 0.f, s2 = 0.f;
+                    const int64_t t = (int64_t)seqlen - 1 - (t0 + row);
+                    const bool ok = has[j] && rr < 16 && row < len && t >= 0 && t < epi.L && hh < nh;
+                    const int64_t r = (b * epi.L + min(max(t, (int64_t)0), epi.L - 1)) * nheads + h;
+                    if (ok) {
+                        const float dtv = epi.dt[r], dh = epi.D[h];
+                        Vec8<bf16> x8, d8, o8;
+                        load8(x8, epi.x + r * P + cc);
+                        load8(d8, epi.dy + r * P + cc);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xv = x8.get(e), dv = d8.get(e);
+                            o8.set(e, fmaf(dtv, v[e], dh * dv));
+                            s1 += xv * v[e];
+                            s2 += xv * dv;
+                        }
+                        store8(epi.dx + r * P + cc, o8);
+                    }
+#pragma unroll
+                    for (int m = 1; m < CPR; m <<= 1) {
+                        s1 += __shfl_xor(s1, m, kWave);
+                        s2 += __shfl_xor(s2, m, kWave);
+                    }
+                    if (ok && cc == 0) {
+                        epi.o1[r] = s1;
+                        epi.o2[r] = s2;
                     }
                 }
-                xu += __shfl_xor(xu, 16, kWave);
-                xu += __shfl_xor(xu, 32, kWave);
-                xd += __shfl_xor(xd, 16, kWave);
-                xd += __shfl_xor(xd, 32, kWave);
-                if (ok && grp == 0) {
-                    epi.o1[r] = xu;
-                    epi.o2[r] = xd;
-                }
+                __syncthreads();                               // the staging area is rewritten next
             }
         }
     } else {
