@@ -445,9 +445,10 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.csp = take(tab);
     w.states = take(st * 4);
     w.entry = take(st * 4);
-    w.SinT = take(st * elemD);
+    const bool dbc0 = elemD == 2 && bwd_dbc_supported(d);
+    w.SinT = take(dbc0 ? 0 : st * elemD);
     w.Gout_rev = take(st * 4);
-    w.GoutT_rev = take(st * elemD);
+    w.GoutT_rev = take(dbc0 ? 0 : st * elemD);
     w.hfinal = take(B * H * P * N * 4);
     w.yhat = take(elemD == 4 ? B * d.seqlen * H * P * 4 : 0);          // fp32 pass only (the bf16 one
                                                                        // reduces yhat and du in place)
@@ -533,8 +534,8 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
                        TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), dbc ? nullptr : TT(w.u_revD), B, L, nc, Q, H, P, N,
                        G);
     SSD_TRY(hipGetLastError());
-    // S_in^T and Gout^T (the operands of the dC and dB passes; bf16 inputs: their hi planes)
-    const unsigned ntr = (unsigned)(nrows * nsplit * ((P + 63) / 64));
+    // S_in^T and Gout^T for the per-head dC and dB passes (bf16 inputs: of their hi planes)
+    const unsigned ntr = dbc ? 0u : (unsigned)(nrows * nsplit * ((P + 63) / 64));
     if (ntr > 0) {
         hipLaunchKernelGGL((bwd_transpose_kernel<TD>), dim3(ntr), dim3(kT), 0, s, TT(w.entry), TT(w.SinT), nrows, P,
                            N, nsplit);
@@ -557,7 +558,7 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     // (the x role, C reversed or B, read from the group's array by every head of the group)
     if constexpr (kBf16) {
         if (dbc)
-            SSD_TRY(launch_bwd_dbc(x, dy, Bm, Cm, F(w.dtc), F(w.cs), TT(w.SinT), TT(w.GoutT_rev), F(w.Mp), F(w.dCi),
+            SSD_TRY(launch_bwd_dbc(x, dy, Bm, Cm, F(w.dtc), F(w.cs), TT(w.entry), TT(w.Gout_rev), F(w.Mp), F(w.dCi),
                                    F(w.dBi), dB, dC, d, s));
     }
     const Dims dbd{d.batch, Lp, d.nheads, Nh, d.headdim, d.nheads, d.chunk};

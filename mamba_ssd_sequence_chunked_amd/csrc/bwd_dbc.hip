@@ -16,8 +16,8 @@
 //               added into fp32 accumulators; the slices' partial sums go to workspace
 //   bwd_inter   the two state terms, per (batch, chunk, group, 64-row block, half of the state
 //               columns): per head, the rows of dy (x) scaled by their decay and rounded to bf16 as
-//               one operand, S_in^T (Gout^T) tiles from the transposed bf16 copies as the other;
-//               the sum over heads runs in the matrix-core accumulators
+//               one operand, the S_in (Gout) tile (bf16, the hi plane of the pair) read transposed
+//               from LDS as the other; the sum over heads runs in the matrix-core accumulators
 //   bwd_dbc     dC and dB of the group: M (the slices summed, split into bf16 hi + lo) times the
 //               chunk's B and C tiles, plus the state terms, rounded to bf16 once
 // Operands reach LDS by asynchronous global->LDS copies (XOR-swizzled tiles; the next head's
@@ -182,17 +182,18 @@ __global__ __launch_bounds__(64 * kW8, 1) void bwd_score_kernel(const bf16* __re
 // ---------------------------------------------------------------------------------------------
 // The state terms.  Wavefront w owns tokens l = 64 rb + 16 w + r16; products are formed
 // transposed, D[n][l] = sum_p S^T[n][p] (e dy)[l][p], so a lane holds 4 consecutive state columns
-// of its token.  S_in^T and Gout^T come as (nsplit, batch, nc, H, NH, P) bf16 (Gout in reversed
-// chunk order).
+// of its token.  S_in and Gout come as (batch, nc, H, P, N) bf16 (Gout in reversed chunk order); a
+// head's (P x NH) tile is read transposed from LDS (contraction slots p = 32 ks + 4 grp + m and
+// 32 ks + 16 + 4 grp + m), and the dy / x rows are loaded in the same slot order.
 template <int P, int NT>
 __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict__ x, const bf16* __restrict__ dy,
                                                           const float* __restrict__ dtc, const float* __restrict__ cs,
-                                                          const bf16* __restrict__ SinT, const bf16* __restrict__ GoutT,
+                                                          const bf16* __restrict__ Sin, const bf16* __restrict__ Gout,
                                                           float* __restrict__ dCi, float* __restrict__ dBi, int batch,
                                                           int64_t L, int H, int G, int N, int Q, int nc, int nrb,
                                                           int nsplit, int nblocks)
 {
-    constexpr int KS = P / 32, CH = P / 8, NH = 16 * NT;
+    constexpr int KS = P / 32, NH = 16 * NT, CHN = NH / 8;
     constexpr int tile_bytes = NH * P * 2;
     __shared__ __attribute__((aligned(1024))) unsigned char tiles[2][2][tile_bytes];   // [buffer][S_in^T, Gout^T]
     __shared__ __attribute__((aligned(16))) float tab[2][2][kMaxQ];
@@ -219,18 +220,20 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
     auto load_rows = [&](int j, Vec8<bf16> (&fd)[KS], Vec8<bf16> (&fx)[KS]) {
         const int h = g * hpg + j;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int off = lok ? ((l * H + h) * P + 32 * ks + 8 * grp) * 2 : kDropped;
-            buffer_load8(fd[ks], rdy, off);
-            buffer_load8(fx[ks], rx, off);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int off = lok ? ((l * H + h) * P + 32 * ks + 16 * hf + 4 * grp) * 2 : kDropped;
+                buffer_load4(fd[ks], hf, rdy, off);
+                buffer_load4(fx[ks], hf, rx, off);
+            }
     };
     auto issue = [&](int j, int q) {
         const int h = g * hpg + j;
-        const bf16* sp = SinT + ((((int64_t)k * batch + b) * nc + c) * H + h) * (int64_t)NH * P;
-        const bf16* gp = GoutT + ((((int64_t)k * batch + b) * nc + (nc - 1 - c)) * H + h) * (int64_t)NH * P;
-        rows_load_async<CH, 4>(lds_addr(tiles[q][0]), NH, wu, lane, [&](int r) { return sp + (int64_t)r * P; });
-        rows_load_async<CH, 4>(lds_addr(tiles[q][1]), NH, wu, lane, [&](int r) { return gp + (int64_t)r * P; });
+        const bf16* sp = Sin + (((int64_t)b * nc + c) * H + h) * (int64_t)P * N + k * NH;
+        const bf16* gp = Gout + (((int64_t)b * nc + (nc - 1 - c)) * H + h) * (int64_t)P * N + k * NH;
+        rows_load_async<CHN, 4>(lds_addr(tiles[q][0]), P, wu, lane, [&](int r) { return sp + (int64_t)r * N; });
+        rows_load_async<CHN, 4>(lds_addr(tiles[q][1]), P, wu, lane, [&](int r) { return gp + (int64_t)r * N; });
         const int64_t row = ((b * H + h) * nc + c) * (int64_t)Q;
         tables_load_async(cs + row, dtc + row, lds_addr(tab[q][0]), lds_addr(tab[q][1]), wu, lane, Q);
     };
@@ -267,9 +270,9 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 Vec8<bf16> a;
-                swz_load8<CH>(a, tiles[q][0], 16 * nt + r16, 32 * ks + 8 * grp);
+                swz_row_slots<CHN>(a, tiles[q][0], 32 * ks, 16 * nt);
                 mma(accC[nt], a, bC[ks]);
-                swz_load8<CH>(a, tiles[q][1], 16 * nt + r16, 32 * ks + 8 * grp);
+                swz_row_slots<CHN>(a, tiles[q][1], 32 * ks, 16 * nt);
                 mma(accB[nt], a, bB[ks]);
             }
         wait_vmem();
@@ -398,7 +401,7 @@ __global__ __launch_bounds__(kT) void bwd_dbc_kernel(const bf16* __restrict__ Bm
 
 template <int P, int NT>
 hipError_t launch_pn(const bf16* x, const bf16* dy, const bf16* B, const bf16* C, const float* dtc, const float* cs,
-                     const bf16* SinT, const bf16* GoutT_rev, float* Mp, float* dCi, float* dBi, bf16* dB, bf16* dC,
+                     const bf16* Sin, const bf16* Gout_rev, float* Mp, float* dCi, float* dBi, bf16* dB, bf16* dC,
                      int nsl, const Dims& d, hipStream_t s)
 {
     const int nc = (int)d.nchunks(), Q = (int)d.chunk, G = (int)d.ngroups, H = (int)d.nheads, N = (int)d.dstate;
@@ -410,7 +413,7 @@ hipError_t launch_pn(const bf16* x, const bf16* dy, const bf16* B, const bf16* C
     if (nb_score == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_score_kernel<P>), dim3(nb_score), dim3(64 * kW8), 0, s, x, dy, dtc, cs, Mp, (int)d.batch,
                        d.seqlen, H, G, Q, nc, nrb8, nsl, hps, nb_score);
-    hipLaunchKernelGGL((bwd_inter_kernel<P, NT>), dim3(nb_inter), dim3(kT), 0, s, x, dy, dtc, cs, SinT, GoutT_rev,
+    hipLaunchKernelGGL((bwd_inter_kernel<P, NT>), dim3(nb_inter), dim3(kT), 0, s, x, dy, dtc, cs, Sin, Gout_rev,
                        dCi, dBi, (int)d.batch, d.seqlen, H, G, N, Q, nc, nrb, nsplit, nb_inter);
     hipLaunchKernelGGL((bwd_dbc_kernel<NT>), dim3(nb_inter), dim3(kT), 0, s, B, C, Mp, dCi, dBi, dB, dC,
                        (int)d.batch, d.seqlen, G, N, Q, nc, nrb, nsplit, nsl, nb_inter);
@@ -424,13 +427,13 @@ bool bwd_dbc_supported(const Dims& d) { return d.headdim % 32 == 0 && d.headdim 
 int bwd_dbc_slices(const Dims& d) { return (int)std::min<int64_t>(4, std::max<int64_t>(1, d.nheads / d.ngroups / 16)); }
 
 hipError_t launch_bwd_dbc(const bf16* x, const bf16* dy, const bf16* B, const bf16* C, const float* dtc,
-                          const float* cs, const bf16* SinT, const bf16* GoutT_rev, float* Mp, float* dCi, float* dBi,
+                          const float* cs, const bf16* Sin, const bf16* Gout_rev, float* Mp, float* dCi, float* dBi,
                           bf16* dB, bf16* dC, const Dims& d, hipStream_t s)
 {
     const int nsl = bwd_dbc_slices(d);
     const int nh = (int)std::min<int64_t>(d.dstate, 128);
 #define SSD_DBC_CASE(PP, TT) \
-    if (d.headdim == PP && nh == 16 * TT) return launch_pn<PP, TT>(x, dy, B, C, dtc, cs, SinT, GoutT_rev, Mp, dCi, dBi, dB, dC, nsl, d, s);
+    if (d.headdim == PP && nh == 16 * TT) return launch_pn<PP, TT>(x, dy, B, C, dtc, cs, Sin, Gout_rev, Mp, dCi, dBi, dB, dC, nsl, d, s);
 #define SSD_DBC_P(PP) SSD_DBC_CASE(PP, 1) SSD_DBC_CASE(PP, 2) SSD_DBC_CASE(PP, 4) SSD_DBC_CASE(PP, 8)
     SSD_DBC_P(32) SSD_DBC_P(64) SSD_DBC_P(128)
 #undef SSD_DBC_P

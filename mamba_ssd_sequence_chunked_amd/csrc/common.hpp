@@ -338,6 +338,12 @@ constexpr int kDropped = 0x40000000;
 __device__ __forceinline__ void buffer_load8(Vec8<bf16>& f, __amdgpu_buffer_rsrc_t r, int voff) {
     f.v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
 }
+// Load 4 consecutive bf16 elements into half h (elements 4 h .. 4 h + 3) of a fragment.
+__device__ __forceinline__ void buffer_load4(Vec8<bf16>& f, int h, __amdgpu_buffer_rsrc_t r, int voff) {
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    const bf16x4_t q = __builtin_bit_cast(bf16x4_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, 0));
+    f.v[4 * h + 0] = q[0]; f.v[4 * h + 1] = q[1]; f.v[4 * h + 2] = q[2]; f.v[4 * h + 3] = q[3];
+}
 __device__ __forceinline__ void buffer_load8(Vec8<float>& f, __amdgpu_buffer_rsrc_t r, int voff) {
     const float4 a = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
     const float4 b = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, 0, 0));

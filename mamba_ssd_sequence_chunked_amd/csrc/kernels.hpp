@@ -133,8 +133,10 @@ struct BwdLayout {
 // dCi / dBi (B, L, G, N) the state terms
 bool bwd_dbc_supported(const Dims& d);
 int bwd_dbc_slices(const Dims& d);
+// (Sin: the entry states' hi plane (B, nc, H, P, N); Gout_rev: the adjoint states' hi plane, reversed
+// chunk order)
 hipError_t launch_bwd_dbc(const bf16* x, const bf16* dy, const bf16* B, const bf16* C, const float* dtc,
-                          const float* cs, const bf16* SinT, const bf16* GoutT_rev, float* Mp, float* dCi, float* dBi,
+                          const float* cs, const bf16* Sin, const bf16* Gout_rev, float* Mp, float* dCi, float* dBi,
                           bf16* dB, bf16* dC, const Dims& d, hipStream_t stream);
 BwdLayout bwd_layout(const Dims& d, int elem_bytes);
 size_t bwd_workspace_bytes(const Dims& d, bool bf16_inputs);
