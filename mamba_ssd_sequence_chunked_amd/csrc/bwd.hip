@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, 
 {
     const int64_t Lp = (int64_t)nc * Q;
     // 1. per (b, tau, h): dy_rev (fp32 and TD) and u = dt x reversed (TD), P / 8 vectors each
-    const int64_t n1 = (int64_t)batch * Lp * H * (P / 8);
+    const int64_t n1 = dy_rev || dy_revD ? (int64_t)batch * Lp * H * (P / 8) : 0;
     for (int64_t i = gtid(); i < n1; i += grid_stride()) {
         const int v = (int)(i % (P / 8));
         const int64_t r = i / (P / 8);             // (b, tau, h)
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kT) void bwd_prep_kernel(const TD* __restrict__ x, 
             ud.zero();
         }
         if (dy_rev) store8(dy_rev + r * P + 8 * v, a);
-        store8(dy_revD + r * P + 8 * v, ad);
+        if (dy_revD) store8(dy_revD + r * P + 8 * v, ad);
         if (u_revD) store8(u_revD + r * P + 8 * v, ud);
     }
     // 2. per (b, tau, g): B_rev, C_rev (TD: exact, B and C hold values of the inputs' type)
@@ -455,7 +455,7 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.dy_rev = take(elemD == 4 ? B * Lp * H * P * 4 : 0);        // the fp32 readout's operand only
     w.B_rev = take(B * Lp * G * N * elemD);
     w.C_rev = take(B * Lp * G * N * elemD);
-    w.dy_revD = take(B * Lp * H * P * elemD);
+    w.dy_revD = take(elemD == 2 && bwd_dbc_supported(d) ? 0 : B * Lp * H * P * elemD);
     w.u_revD = take(elemD == 2 && bwd_dbc_supported(d) ? 0 : B * Lp * H * P * elemD);
     w.du_rev = take(elemD == 4 ? B * Lp * H * P * 4 : 0);
     // dB, dC: per-head parts summed afterwards, or (bf16 inputs) the group sums formed in the kernels
@@ -527,12 +527,14 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
                        dinit, st, H, P, N, Q, nc);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
-    const int64_t nprep = std::max<int64_t>((int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
+    // (bf16 inputs: the du pass reads dy itself in reversed order; the reversed dy and u copies serve the
+    // per-head dB pass only)
     float* const dy_rev32 = kBf16 ? nullptr : F(w.dy_rev);
     const bool dbc = kBf16 && bwd_dbc_supported(d);          // dB, dC summed over heads in the kernels
+    const int64_t nprep = std::max<int64_t>(dbc ? 0 : (int64_t)B * Lp * H * (P / 8), (int64_t)B * Lp * G * (N / 8));
     hipLaunchKernelGGL((bwd_prep_kernel<TD>), dim3(grid_for(nprep)), dim3(kT), 0, s, x, dt, Bm, Cm, dy, dy_rev32,
-                       TT(w.B_rev), TT(w.C_rev), TT(w.dy_revD), dbc ? nullptr : TT(w.u_revD), B, L, nc, Q, H, P, N,
-                       G);
+                       TT(w.B_rev), TT(w.C_rev), dbc ? nullptr : TT(w.dy_revD), dbc ? nullptr : TT(w.u_revD), B, L, nc,
+                       Q, H, P, N, G);
     SSD_TRY(hipGetLastError());
     // S_in^T and Gout^T for the per-head dC and dB passes (bf16 inputs: of their hi planes)
     const unsigned ntr = dbc ? 0u : (unsigned)(nrows * nsplit * ((P + 63) / 64));
@@ -548,8 +550,8 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     if constexpr (kBf16) {
         // du leaves the accumulators as dx = dt du + D dy, x . du and x . dy
         const ScanEpi eu{dy, x, dt, D, dx, F(w.xdu), F(w.xdy), L};
-        SSD_TRY(launch_chunk_scan_split_grad(TT(w.dy_revD), TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp),
-                                             TT(w.Gout_rev), st, zeros, eu, dr, s));
+        SSD_TRY(launch_chunk_scan_split_grad(dy, TT(w.C_rev), TT(w.B_rev), F(w.dtp), F(w.csp), TT(w.Gout_rev), st,
+                                             zeros, eu, dr, s));
     } else
         SSD_TRY(launch_chunk_scan_f32out<float>(F(w.dy_rev), F(w.C_rev), F(w.B_rev), F(w.dtp), F(w.csp),
                                                 F(w.Gout_rev), zeros, F(w.du_rev), dr, s));

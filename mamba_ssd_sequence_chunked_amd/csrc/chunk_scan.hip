@@ -242,10 +242,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
         const unsigned stg = lds_addr(region) + (sb % kStages) * S::stage_bytes;
-        const T* xs = x + (b * seqlen + t0) * xl.row;
         tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
-            return xs + (int64_t)min(s0 + r, len - 1) * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs +
-                   ch * EPC;
+            const int64_t tau = t0 + min(s0 + r, len - 1);
+            int64_t tok = b * seqlen + tau;
+            if constexpr (EPI == 2) tok = b * xl.rev_L + min((int64_t)seqlen - 1 - tau, xl.rev_L - 1);   // reversed x
+            return x + tok * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs + ch * EPC;
         });
         const TB* bg = Bm + (int64_t)g * N;
         tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
@@ -433,11 +434,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     const T* xt = reinterpret_cast<const T*>(stg + hh * S::xh_bytes);
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
-                        const float4 xl = swz_load4f<S::X_CH>(xt, lrow - s0, 16 * pt + 4 * grp);
-                        acc[j][hh][pt][0] += dsk[hh] * xl.x;
-                        acc[j][hh][pt][1] += dsk[hh] * xl.y;
-                        acc[j][hh][pt][2] += dsk[hh] * xl.z;
-                        acc[j][hh][pt][3] += dsk[hh] * xl.w;
+                        const float4 xv = swz_load4f<S::X_CH>(xt, lrow - s0, 16 * pt + 4 * grp);
+                        acc[j][hh][pt][0] += dsk[hh] * xv.x;
+                        acc[j][hh][pt][1] += dsk[hh] * xv.y;
+                        acc[j][hh][pt][2] += dsk[hh] * xv.z;
+                        acc[j][hh][pt][3] += dsk[hh] * xv.w;
                     }
                 }
             }
@@ -604,7 +605,11 @@ hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, co
 {
     const int64_t nk = (d.dstate + 31) / 32;
     const int nki = nk <= 1 ? 1 : nk <= 2 ? 2 : nk <= 4 ? 4 : 8;
-    if (xl.hdiv == 0) xl = XLayout{d.nheads * d.headdim, 1, (int)d.headdim};     // x in (B, L, H, P)
+    if (xl.hdiv == 0) {                                   // x in (B, L, H, P)
+        xl.row = d.nheads * d.headdim;
+        xl.hdiv = 1;
+        xl.hs = (int)d.headdim;
+    }
 #define SSD_SCAN_CASE(PP, KK) \
     if (d.headdim == PP && nki == KK) \
         return launch<T, TB, TY, PP, KK, V, SP, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream, epi);
@@ -669,7 +674,7 @@ hipError_t launch_chunk_scan_split_grad(const bf16* x, const bf16* B, const bf16
                                         const ScanEpi& epi, const Dims& d, hipStream_t stream)
 {
     return launch_any<bf16, bf16, float, false, 2, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
-                                                      stream, XLayout{0, 0, 0}, lo_off, epi);
+                                                      stream, XLayout{0, 0, 0, epi.L}, lo_off, epi);
 }
 
 template <typename T>

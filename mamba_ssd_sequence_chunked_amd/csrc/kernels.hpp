@@ -17,6 +17,10 @@ struct Dims {
 struct XLayout {
     int64_t row;
     int hdiv, hs;
+    // the caller's sequence length when x is read in reversed token order (the du pass): row tau of the
+    // padded (seqlen) sequence is the caller's token seqlen - 1 - tau, clamped to rev_L - 1 for the
+    // front padding (whose weights are zero)
+    int64_t rev_L;
 };
 
 hipError_t launch_dA_cumsum(const float* dt, const float* A, float* dA_cs, float* dt_chunked,
@@ -96,7 +100,8 @@ hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, 
 // The backward's readout passes with the per-token work folded into the output stage (y not stored):
 //   ..._dot:  o1[b, t, h] = sum_p dy[b, t, h, p] y[b, t, h, p]
 //   ..._grad: y = du on the time-reversed, front-padded sequence (token t = Lp - 1 - row, pads
-//             skipped): dx = dt du + D dy (bf16), o1 = x . du, o2 = x . dy per (b, t, h)
+//             skipped): dx = dt du + D dy (bf16), o1 = x . du, o2 = x . dy per (b, t, h); its x
+//             operand is the caller's dy (B, L, H, P), read in reversed token order
 struct ScanEpi {
     const bf16* dy;
     const bf16* x;
