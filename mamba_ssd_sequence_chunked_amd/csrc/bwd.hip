@@ -242,7 +242,7 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
 }
 
 // per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
-// gradients need: dy . yhat, x . du and x . dy.
+// gradients need: dy . yhat, x . du and x . dy (stored (batch, head, token)).
 // 16 lanes share a row (P / 16 values each), so a wavefront reads four whole rows per load.
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, const float* __restrict__ dt,
@@ -279,25 +279,27 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, 
         xdu = group_sum<16>(xdu);
         xdy = group_sum<16>(xdy);
         if (sub == 0) {
-            yd_out[r] = dyy;
-            xdu_out[r] = xdu;
-            xdy_out[r] = xdy;
+            const int64_t rt = (b * H + h) * L + t;              // (batch, head, token)
+            yd_out[rt] = dyy;
+            xdu_out[rt] = xdu;
+            xdy_out[rt] = xdy;
         }
     }
 }
 
-// per (b, h): with q_t = dy_t . yhat_t - dt_t x_t . du_t,
+// per (b, h): with q_t = dy_t . yhat_t - dt_t x_t . du_t (the three scalars stored (batch, head, token),
+// dt read from the chunked copy (batch, head, padded token)),
 // the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
 // and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.  Thread i takes the 16 tokens
 // ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.  The sums
 // run in fp64: dA adds up terms that cancel to a few parts in a thousand of their magnitude.
-__global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dt, const float* __restrict__ A,
+__global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dtc, const float* __restrict__ A,
                                                       const float* __restrict__ yd, const float* __restrict__ xdu,
                                                       const float* __restrict__ xdy,
                                                       const float* __restrict__ dfinal,
                                                       const float* __restrict__ hfinal, float* __restrict__ ddt,
                                                       double* __restrict__ dAp, double* __restrict__ dDp, int64_t L,
-                                                      int H, int P, int N)
+                                                      int64_t Lp, int H, int P, int N)
 {
     constexpr int kPer = 16;
     __shared__ double sc[kT];
@@ -341,10 +343,10 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
             const int64_t t = t1 - 1 - k;
             float q = 0.f, xu = 0.f;
             if (t >= 0 && t < L) {
-                const int64_t r = (b * L + t) * H + h;
-                xu = xdu[r];
-                q = yd[r] - dt[r] * xu;
-                dD_acc += xdy[r];
+                const int64_t rt = bh * L + t;
+                xu = xdu[rt];
+                q = yd[rt] - dtc[bh * Lp + t] * xu;
+                dD_acc += xdy[rt];
             }
             qs[k] = q;
             xs[k] = xu;
@@ -358,9 +360,8 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
             const int64_t t = t1 - 1 - k;
             run += qs[k];
             if (t >= 0 && t < L) {
-                const int64_t r = (b * L + t) * H + h;
-                ddt[r] = (float)(a * run + xs[k]);
-                dA_acc += (double)dt[r] * run;
+                ddt[(b * L + t) * H + h] = (float)(a * run + xs[k]);
+                dA_acc += (double)dtc[bh * Lp + t] * run;
             }
         }
         carry += total;
@@ -581,10 +582,9 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
                                dy, F(w.yhat), F(w.du_rev), dx, F(w.yd), F(w.xdu), F(w.xdy), L, H, P, Q, nc);
             SSD_TRY(hipGetLastError());
         }
-        hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, dt, A, F(w.yd), F(w.xdu), F(w.xdy),
-                           dfinal,
-                           F(w.hfinal), ddt, reinterpret_cast<double*>(ws + w.dAp), reinterpret_cast<double*>(ws + w.dDp), L,
-                           H, P, N);
+        hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, F(w.dtc), A, F(w.yd), F(w.xdu),
+                           F(w.xdy), dfinal, F(w.hfinal), ddt, reinterpret_cast<double*>(ws + w.dAp),
+                           reinterpret_cast<double*>(ws + w.dDp), L, Lp, H, P, N);
         SSD_TRY(hipGetLastError());
     }
     if (!dbc) {

@@ -468,7 +468,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 }
                 dot += __shfl_xor(dot, 16, kWave);
                 dot += __shfl_xor(dot, 32, kWave);
-                if (ok && grp == 0) epi.o1[r] = dot;
+                if (ok && grp == 0)
+                    epi.o1[((int64_t)b * nheads + h0 + hh) * seqlen + t0 + row] = dot;   // (batch, head, token)
             }
         }
     } else if constexpr (EPI == 2) {
@@ -528,8 +529,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                         s2 += __shfl_xor(s2, m, kWave);
                     }
                     if (ok && cc == 0) {
-                        epi.o1[r] = s1;
-                        epi.o2[r] = s2;
+                        const int64_t rt = ((int64_t)b * nheads + h) * epi.L + t;     // (batch, head, token)
+                        epi.o1[rt] = s1;
+                        epi.o2[rt] = s2;
                     }
                 }
                 __syncthreads();                               // the staging area is rewritten next

@@ -98,9 +98,10 @@ hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, 
                                    const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
                                    const Dims& d, hipStream_t stream);
 // The backward's readout passes with the per-token work folded into the output stage (y not stored):
-//   ..._dot:  o1[b, t, h] = sum_p dy[b, t, h, p] y[b, t, h, p]
+// (o1, o2 indexed (batch, head, token))
+//   ..._dot:  o1[b, h, t] = sum_p dy[b, t, h, p] y[b, t, h, p]
 //   ..._grad: y = du on the time-reversed, front-padded sequence (token t = Lp - 1 - row, pads
-//             skipped): dx = dt du + D dy (bf16), o1 = x . du, o2 = x . dy per (b, t, h); its x
+//             skipped): dx = dt du + D dy (bf16), o1 = x . du, o2 = x . dy per (b, h, t); its x
 //             operand is the caller's dy (B, L, H, P), read in reversed token order
 struct ScanEpi {
     const bf16* dy;
