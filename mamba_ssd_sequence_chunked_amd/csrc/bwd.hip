@@ -464,8 +464,8 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.dBh_rev = take(dbc ? 0 : B * Lp * H * N * 4);
     w.dCh = take(dbc ? 0 : B * d.seqlen * H * N * 4);
     w.Mp = take(dbc ? (int64_t)bwd_dbc_slices(d) * B * nc * G * d.chunk * d.chunk * 4 : 0);
-    w.dCi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
-    w.dBi = take(dbc ? B * d.seqlen * G * N * 4 : 0);
+    w.dCi = take(dbc ? (int64_t)bwd_dbc_slices(d) * B * d.seqlen * G * N * 4 : 0);   // per slice of the heads
+    w.dBi = take(dbc ? (int64_t)bwd_dbc_slices(d) * B * d.seqlen * G * N * 4 : 0);
     w.zeros = take(std::max<int64_t>(H, 1) * 4);
     w.yd = take(B * d.seqlen * H * 4);
     w.xdu = take(B * d.seqlen * H * 4);

@@ -15,7 +15,8 @@
 //               products dy x^T on the matrix cores (bf16, fp32 sums), then decay and mask in fp32
 //               added into fp32 accumulators; the slices' partial sums go to workspace
 //   bwd_inter   the two state terms, per (batch, chunk, group, 64-row block, half of the state
-//               columns): per head, the rows of dy (x) scaled by their decay and rounded to bf16 as
+//               columns, slice of the heads; partial sums per slice): per head, the rows of dy (x)
+//               scaled by their decay and rounded to bf16 as
 //               one operand, the S_in (Gout) tile (bf16, the hi plane of the pair) read transposed
 //               from LDS as the other; the sum over heads runs in the matrix-core accumulators
 //   bwd_dbc     dC and dB of the group: M (the slices summed, split into bf16 hi + lo) times the
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
                                                           const bf16* __restrict__ Sin, const bf16* __restrict__ Gout,
                                                           float* __restrict__ dCi, float* __restrict__ dBi, int batch,
                                                           int64_t L, int H, int G, int N, int Q, int nc, int nrb,
-                                                          int nsplit, int nblocks)
+                                                          int nsplit, int nsl, int hps, int nblocks)
 {
     constexpr int KS = P / 32, NH = 16 * NT, CHN = NH / 8;
     constexpr int tile_bytes = NH * P * 2;
@@ -201,10 +202,12 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
     int id = xcd_logical_block(blockIdx.x, nblocks);
     const int k = id % nsplit; id /= nsplit;
     const int rb = id % nrb; id /= nrb;
+    const int sl = id % nsl; id /= nsl;
     const int g = id % G; id /= G;
     const int c = id % nc;
     const int64_t b = id / nc;
     const int hpg = H / G;
+    const int j0 = sl * hps, j1 = min(hpg, j0 + hps);
     const int64_t t0 = (int64_t)c * Q;
     const int len = (int)min((int64_t)Q, L - t0);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
@@ -242,13 +245,15 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) accC[nt] = accB[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     Vec8<bf16> dyc[KS], xc[KS], dyn[KS], xn[KS];
-    load_rows(0, dyc, xc);
-    issue(0, 0);
+    if (j0 < j1) {
+        load_rows(j0, dyc, xc);
+        issue(j0, 0);
+    }
     wait_vmem();
     __syncthreads();
-    for (int j = 0; j < hpg; ++j) {
-        const int q = j & 1;
-        if (j + 1 < hpg) {
+    for (int j = j0; j < j1; ++j) {
+        const int q = (j - j0) & 1;
+        if (j + 1 < j1) {
             load_rows(j + 1, dyn, xn);
             issue(j + 1, q ^ 1);
         }
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
         }
     }
     if (lok) {
-        const int64_t o = ((b * L + t0 + l) * G + g) * (int64_t)N + k * NH + 4 * grp;
+        const int64_t o = (int64_t)sl * batch * L * G * N + ((b * L + t0 + l) * G + g) * (int64_t)N + k * NH + 4 * grp;
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             *reinterpret_cast<f32x4*>(dCi + o + 16 * nt) = accC[nt];
@@ -389,12 +394,18 @@ __global__ __launch_bounds__(kT) void bwd_dbc_kernel(const bf16* __restrict__ Bm
     }
     if (r < len) {
         const int64_t o = ((b * L + t0 + r) * G + g) * (int64_t)N + k * NH + 4 * grp;
+        const int64_t istride = (int64_t)batch * L * G * N;      // between the state terms' slices
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-            const float4 ic = *reinterpret_cast<const float4*>(dCi + o + 16 * nt);
-            const float4 ib = *reinterpret_cast<const float4*>(dBi + o + 16 * nt);
-            store4(dC + o + 16 * nt, accC[nt][0] + ic.x, accC[nt][1] + ic.y, accC[nt][2] + ic.z, accC[nt][3] + ic.w);
-            store4(dB + o + 16 * nt, accB[nt][0] + ib.x, accB[nt][1] + ib.y, accB[nt][2] + ib.z, accB[nt][3] + ib.w);
+            f32x4 c4 = accC[nt], b4 = accB[nt];
+            for (int z = 0; z < nsl; ++z) {
+                const float4 ic = *reinterpret_cast<const float4*>(dCi + z * istride + o + 16 * nt);
+                const float4 ib = *reinterpret_cast<const float4*>(dBi + z * istride + o + 16 * nt);
+                c4[0] += ic.x; c4[1] += ic.y; c4[2] += ic.z; c4[3] += ic.w;
+                b4[0] += ib.x; b4[1] += ib.y; b4[2] += ib.z; b4[3] += ib.w;
+            }
+            store4(dC + o + 16 * nt, c4[0], c4[1], c4[2], c4[3]);
+            store4(dB + o + 16 * nt, b4[0], b4[1], b4[2], b4[3]);
         }
     }
 }
@@ -409,14 +420,15 @@ hipError_t launch_pn(const bf16* x, const bf16* dy, const bf16* B, const bf16* C
     const int hps = (hpg + nsl - 1) / nsl;
     const int64_t ngroups_all = d.batch * nc * G;
     const int nb_score = (int)(ngroups_all * nrb8 * nsl);
-    const int nb_inter = (int)(ngroups_all * nrb * nsplit);
+    const int nb_inter = (int)(ngroups_all * nrb * nsplit * nsl);
+    const int nb_dbc = (int)(ngroups_all * nrb * nsplit);
     if (nb_score == 0) return hipSuccess;
     hipLaunchKernelGGL((bwd_score_kernel<P>), dim3(nb_score), dim3(64 * kW8), 0, s, x, dy, dtc, cs, Mp, (int)d.batch,
                        d.seqlen, H, G, Q, nc, nrb8, nsl, hps, nb_score);
     hipLaunchKernelGGL((bwd_inter_kernel<P, NT>), dim3(nb_inter), dim3(kT), 0, s, x, dy, dtc, cs, Sin, Gout_rev,
-                       dCi, dBi, (int)d.batch, d.seqlen, H, G, N, Q, nc, nrb, nsplit, nb_inter);
-    hipLaunchKernelGGL((bwd_dbc_kernel<NT>), dim3(nb_inter), dim3(kT), 0, s, B, C, Mp, dCi, dBi, dB, dC,
-                       (int)d.batch, d.seqlen, G, N, Q, nc, nrb, nsplit, nsl, nb_inter);
+                       dCi, dBi, (int)d.batch, d.seqlen, H, G, N, Q, nc, nrb, nsplit, nsl, hps, nb_inter);
+    hipLaunchKernelGGL((bwd_dbc_kernel<NT>), dim3(nb_dbc), dim3(kT), 0, s, B, C, Mp, dCi, dBi, dB, dC,
+                       (int)d.batch, d.seqlen, G, N, Q, nc, nrb, nsplit, nsl, nb_dbc);
     return hipGetLastError();
 }
 

@@ -136,7 +136,7 @@ struct BwdLayout {
 };
 // dB and dC summed over the heads inside the kernels (bwd_dbc.hip): bf16 inputs, headdim % 32 == 0,
 // chunk % 64 == 0; Mp holds bwd_dbc_slices() partial sums of the (B, nc, G, Q, Q) score matrices,
-// dCi / dBi (B, L, G, N) the state terms
+// dCi / dBi as many partial sums of the (B, L, G, N) state terms (the heads split into slices)
 bool bwd_dbc_supported(const Dims& d);
 int bwd_dbc_slices(const Dims& d);
 // (Sin: the entry states' hi plane (B, nc, H, P, N); Gout_rev: the adjoint states' hi plane, reversed
