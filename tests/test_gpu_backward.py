@@ -4,7 +4,7 @@ import pytest
 
 import oracle
 from mamba_ssd_sequence_chunked_amd.inputs import make_inputs, make_random
-from util import TOL, head_slice, slice_rel_err, to_device, to_f64
+from util import TOL, slice_rel_err, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -81,22 +81,24 @@ def test_backward_empty_sequence():
     assert torch.all(g["dA"] == 0) and torch.all(g["dD"] == 0)
 
 
-def test_backward_full_size_sampled():
+def test_backward_full_size():
     """The 2.7B-layer shape (4 x 4096 tokens, 80 heads, N = 128, bf16) in the benchmark's launch
-    configuration; a head's dx, ddt and dinit depend on that head's inputs and the group's B, C
-    only, so sampled (batch, head) pairs are checked against the oracle run on them alone."""
+    configuration (dB and dC summed over the 80 heads in the kernels, four head slices): every
+    gradient against the oracle run on the whole problem, at the small cases' bars."""
     inp = make_inputs("l2p7b")
     b, L, H, P, N, G = inp.dims
     rng = np.random.default_rng(870)
     from mamba_ssd_sequence_chunked_amd.inputs import bf16_bits, bf16_to_f64
     dy = bf16_bits(rng.standard_normal((b, L, H, P)))
     g = _grads(inp, dy, None)
-    for bb, h in ((0, 0), (3, 57)):
-        xs, dts, As, Bs, Cs, Ds, h0 = head_slice(inp, bb, h)
-        dys = bf16_to_f64(np.ascontiguousarray(dy[bb:bb + 1, :, h:h + 1]))
-        r = oracle.backward(xs, dts, As, Bs, Cs, Ds, h0, dys, None)
-        print(f"l2p7b backward b={bb} h={h}", flush=True)
-        assert slice_rel_err(g["dx"][bb:bb + 1, :, h:h + 1], r["dx"], 2) <= TOL["bf16"]
-        assert slice_rel_err(g["ddt"][bb:bb + 1, :, h:h + 1, None], r["ddt"][..., None], 2) <= TOL["bf16"]
-        assert slice_rel_err(g["dinit"][bb:bb + 1, h:h + 1], r["dinit"], 1) <= TOL["bf16"]
-    assert np.all(np.isfinite(g["dB"])) and np.all(np.isfinite(g["dC"])) and np.all(np.isfinite(g["dA"]))
+    print("l2p7b backward: gradients computed, running the oracle", flush=True)
+    r = oracle.backward(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D, inp.f64("init"),
+                        bf16_to_f64(dy), None)
+    tol = TOL["bf16"]
+    assert slice_rel_err(g["dx"], r["dx"], 2) <= tol, "dx"
+    assert slice_rel_err(g["ddt"][..., None], r["ddt"][..., None], 2) <= tol, "ddt"
+    assert slice_rel_err(g["dB"], r["dB"], 2) <= tol, "dB"
+    assert slice_rel_err(g["dC"], r["dC"], 2) <= tol, "dC"
+    assert slice_rel_err(g["dinit"], r["dinit"], 1) <= tol, "dinit"
+    assert np.max(np.abs(g["dA"] - r["dA"]) / r["dA_scale"]) <= 1e-5, "dA"
+    assert _rel_all(g["dD"], r["dD"]) <= tol, "dD"
