@@ -1,20 +1,16 @@
 """Parity at the full workload sizes, in the launch configuration the benchmark
 times (one ssd_forward over the whole batch; ssd_step over the whole decode
-batch), checked on sampled (batch, head) slices that the fp64 oracle
-computes one by one."""
+batch): the forward checked on every (batch, head) slice against the fp64
+oracle run on the whole problem, decode on sampled rows."""
 import numpy as np
 import pytest
 
 import oracle
 from mamba_ssd_sequence_chunked_amd.inputs import (CONFIGS, make_inputs, make_step_inputs,
                                                    make_step_params)
-from util import TOL, head_slice, slice_rel_err, to_device, to_f64
+from util import TOL, slice_rel_err, to_device, to_f64
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
-
-
-def _samples(b, H):
-    return sorted({(0, 0), (b - 1, H - 1), (b // 2, H // 2 + 1), (0, H // 3), (b - 1, 1)})
 
 
 @pytest.mark.parametrize("name", ["l130m", "l2p7b", "long64k"])
@@ -27,14 +23,13 @@ def test_forward_full_size(name):
     y, fin = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], inp.chunk_size, d["init"])
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y.float()).all()) and bool(torch.isfinite(fin).all())
-    worst_y = worst_f = 0.0
-    for (bi, h) in _samples(b, H):
-        xs, dts, As, Bs, Cs, Ds, h0 = head_slice(inp, bi, h)
-        y_ref, f_ref = oracle.forward(xs, dts, As, Bs, Cs, Ds, h0)
-        ey = slice_rel_err(to_f64(y[bi:bi + 1, :, h:h + 1]), y_ref, 2)
-        ef = slice_rel_err(to_f64(fin[bi:bi + 1, h:h + 1]), f_ref, 1)
-        worst_y, worst_f = max(worst_y, ey), max(worst_f, ef)
-    print(f"{name}: worst sampled y err {worst_y:.3e}, final err {worst_f:.3e}")
+    yg, fg = to_f64(y), to_f64(fin)
+    del y, fin, d
+    print(f"{name}: forward done, running the oracle", flush=True)
+    y_ref, f_ref = oracle.forward(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D, inp.f64("init"))
+    worst_y = slice_rel_err(yg, y_ref, 2)
+    worst_f = slice_rel_err(fg, f_ref, 1)
+    print(f"{name}: worst y err over all {b * H} (batch, head) slices {worst_y:.3e}, final err {worst_f:.3e}")
     assert worst_y <= TOL[inp.dtype], worst_y
     assert worst_f <= TOL[inp.dtype], worst_f
 
