@@ -6,25 +6,28 @@
 // The pass therefore reuses the forward's stage kernels, each fed the arrays that put the wanted
 // quantity in the place of y:
 //
-//   forward recompute    chunk states, entry states S_in (rounded to T), the final state, and
-//                        yhat = y - D x in fp32 (chunk_scan with D = 0)
+//   forward recompute    chunk states, entry states S_in, the final state, and yhat = y - D x
+//                        (chunk_scan with D = 0; bf16 inputs: reduced to dy . yhat per token as it
+//                        leaves the accumulators)
 //   adjoint chunk states Ghat_c = sum_{s in c} exp(cs[s]) dy_s C_s^T   (chunk_state with w = exp(cs))
 //   adjoint passing      Gout[c] (adjoint at chunk c's last token from later tokens), backwards
 //                        over chunks from dfinal; what is left at the front is dinit = a_0 g_0
 //   du = g B             chunk_scan on the time-reversed sequence: x <- dy, B <- C, C <- B,
-//                        entry <- Gout, no dt scaling, decays cs'[l'] = cs[last] - cs[l]
-//   dB (per head)        time-reversed chunk_scan with x <- C (copied per head), B <- dy, C <- u = dt x,
-//                        entry <- Gout^T; contraction over the head dimension
-//   dC (per head)        chunk_scan with x <- B (copied per head), B <- x (dt scaled), C <- dy,
-//                        entry <- S_in^T
-//   per token            dx = dt du + D dy; with q_t = dy_t . yhat_t - u_t . du_t the gradient of
-//                        the log-decay dt_t A is the suffix sum of q from t plus <dfinal, h_final>
-//                        (the telescoping of <g_t, h_t> over t), so ddt = A dl + x . du,
-//                        dA = sum dt dl, dD = sum x . dy
-//   dB, dC               per-head parts summed over the heads of each group
+//                        entry <- Gout, no dt scaling, decays cs'[l'] = cs[last] - cs[l] (bf16
+//                        inputs: dy read in reversed order, and du reduced as it leaves the
+//                        accumulators to dx = dt du + D dy, x . du and x . dy per token)
+//   dB, dC               bf16 inputs (headdim % 32 == 0, chunk % 64 == 0): summed over each group's
+//                        heads inside the kernels of bwd_dbc.hip; otherwise per head -- dB by a
+//                        time-reversed chunk_scan with x <- C, B <- dy, C <- u = dt x, entry <-
+//                        Gout^T, dC by a chunk_scan with x <- B, B <- x (dt scaled), C <- dy, entry
+//                        <- S_in^T (the head dimension as the contraction; B and C read from the
+//                        group's arrays) -- and summed over the heads of each group afterwards
+//   per token            with q_t = dy_t . yhat_t - u_t . du_t the gradient of the log-decay dt_t A
+//                        is the suffix sum of q from t plus <dfinal, h_final> (the telescoping of
+//                        <g_t, h_t> over t), so ddt = A dl + x . du, dA = sum dt dl, dD = sum x . dy
 //
 // The reversal pads the sequence in front to whole chunks (zero tokens, unit decay), so the
-// reversed chunks line up with the forward's.  Outputs of the chunk_scan passes stay fp32.
+// reversed chunks line up with the forward's.
 //
 // The gradient of the log-decays is a suffix sum of differences of two nearly equal products per
 // token, and dA sums it over all tokens: rounding the matrix-core operands to bf16 (as the forward
@@ -34,8 +37,8 @@
 // dy hold bf16 values) each fp32 operand -- the weighted B or C, the decay-weighted C.B^T, the
 // entry and adjoint states -- is split into bf16 hi + lo (the value to 2^-18) and each product is
 // taken twice on the bf16 matrix cores into fp32 sums (dA then within ~1e-7 of its terms' size).
-// The per-head dB / dC passes take plain operands of the inputs' type; dx, dB and dC are rounded
-// to the inputs' type once at the end.
+// dB and dC take plain operands of the inputs' type; dx, dB and dC are rounded to the inputs'
+// type once at the end.
 #include <algorithm>
 
 #include <type_traits>
