@@ -71,7 +71,7 @@ constexpr int kMaxQ = 256;
 constexpr int kWaves = 4;                      // one row-block pair per wavefront
 constexpr int kThreads = 64 * kWaves;
 
-template <typename T, typename TB, int P, int NK, int HB, int STG, int SW, bool V = false, int SP = 1>
+template <typename T, int P, int NK, int HB, int STG, int SW, bool V = false, int SP = 1>
 struct ScanCfg {
     static constexpr int kHeads = HB;
     static constexpr bool kSplit = SP == 2;                       // S_in as bf16 hi and lo planes
@@ -81,11 +81,11 @@ struct ScanCfg {
     static constexpr int SWD = SW;                                 // state columns of S_in per LDS slab
     static constexpr int NSL = NP / SW;                            // slabs
     static constexpr int X_CH = P * (int)sizeof(T) / 16;           // chunks per x row
-    static constexpr int EPB = 16 / (int)sizeof(TB);              // B / C elements per 16-byte chunk
-    static constexpr int B_CH = NP * (int)sizeof(TB) / 16;         // chunks per B row
+    static constexpr int EPB = 16 / (int)sizeof(T);              // B / C elements per 16-byte chunk
+    static constexpr int B_CH = NP * (int)sizeof(T) / 16;         // chunks per B row
     static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in slab row
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
-    static constexpr int b_bytes = kSB * NP * (int)sizeof(TB);
+    static constexpr int b_bytes = kSB * NP * (int)sizeof(T);
     static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
     static constexpr int sh_bytes = P * SW * (int)sizeof(T);       // one S_in slab of one head (one plane)
     static constexpr int ring_bytes = STG * stage_bytes;
@@ -116,27 +116,17 @@ struct ScanCfg {
 // and a single head takes a CU alone when it must.
 template <class C> struct TypeBox { using type = C; };
 
-template <typename T, typename TB, int P, int NK, int HB, bool V, int SP = 1>
+template <typename T, int P, int NK, int HB, bool V, int SP = 1>
 constexpr auto pick_shape() {
-    using C = ScanCfg<T, TB, P, NK, HB, 2, 32, V, SP>;
+    using C = ScanCfg<T, P, NK, HB, 2, 32, V, SP>;
     if constexpr (C::pair_fits || (HB == 1 && C::fits)) return TypeBox<C>{};
-    else if constexpr (HB > 1) return pick_shape<T, TB, P, NK, HB / 2, V, SP>();
+    else if constexpr (HB > 1) return pick_shape<T, P, NK, HB / 2, V, SP>();
     else return TypeBox<C>{};                 // does not fit: rejected by a static_assert at launch
 }
 
-template <typename T, typename TB, int P, int NK, bool V = false, int SP = 1>
-using ScanShape = typename decltype(pick_shape<T, TB, P, NK,
+template <typename T, int P, int NK, bool V = false, int SP = 1>
+using ScanShape = typename decltype(pick_shape<T, P, NK,
     ((NK >= 8 ? 128 : 256) / P > 8 ? 8 : (NK >= 8 ? 128 : 256) / P), V, SP>())::type;
-
-// a C fragment as an operand of the S_in product (whose other operand is in T)
-__device__ __forceinline__ const Vec8<float>& as_t(const Vec8<float>& f, float) { return f; }
-__device__ __forceinline__ const Vec8<bf16>& as_t(const Vec8<bf16>& f, bf16) { return f; }
-__device__ __forceinline__ Vec8<float> as_t(const Vec8<bf16>& f, float) {
-    Vec8<float> w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w.set(e, f.get(e));
-    return w;
-}
 
 // kVarlen: a packed variable-length batch (batch 1; tstart from varlen_meta.hip).  A pair (l, s)
 // of one chunk is kept only when s >= tstart[l] (same sequence); since sequences are contiguous,
@@ -144,16 +134,14 @@ __device__ __forceinline__ Vec8<float> as_t(const Vec8<bf16>& f, float) {
 // times [s >= tstart[e]] per token, which fold into the row decay and the token table; the state
 // entering the chunk reaches only the rows of the sequence holding the chunk's first token.
 // TY: the type y is stored in (T, or float when the caller needs the sum unrounded).
-// TB: the type of B and C (T, or bf16 under fp32 x and S_in when B and C hold bf16 values: C.B^T then
-// runs on the bf16 matrix cores, its products exact in the fp32 accumulator as on the fp32 ones).
 // S::kSplit (T = bf16, TY = float): the fp32 products of the backward's readout passes from bf16
 // ones, with x, B, C holding bf16 values: S_in comes as two bf16 planes, hi at entry and lo at
 // entry + lo_off (hi + lo = the fp32 state to 2^-18), G is split the same way in registers, and
 // each product is taken twice on the bf16 matrix cores (hi, then lo) into the fp32 accumulators.
 // EPI (split mode): 0 stores y; 1 and 2 reduce it per (token, head) as ScanEpi describes (kernels.hpp).
-template <typename T, typename TB, typename TY, int P, int NK, class S, bool kVarlen, int EPI = 0>
+template <typename T, typename TY, int P, int NK, class S, bool kVarlen, int EPI = 0>
 __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
-    const T* __restrict__ x, const TB* __restrict__ Bm, const TB* __restrict__ Cm,
+    const T* __restrict__ x, const T* __restrict__ Bm, const T* __restrict__ Cm,
     const float* __restrict__ dt_chunked, const float* __restrict__ dA_cs,
     const T* __restrict__ entry, int64_t lo_off, const float* __restrict__ Dv, const int* __restrict__ tstart,
     TY* __restrict__ y, XLayout xl, int seqlen, int nheads, int ngroups, int N, int Q, int nc, int nhb, int hpw, int nhalf, int nblocks,
@@ -195,11 +183,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     // ---- C rows of this wavefront's row blocks as operand fragments (state axis = contraction slots),
     // by range-checked buffer loads (rows past the chunk's tokens and missing blocks read as zero).
     // Issued first: no later wait for them then also waits for the asynchronous copies below.
-    Vec8<TB> cf[2][S::NP / 32];
+    Vec8<T> cf[2][S::NP / 32];
     {
-        const TB* cb = Cm + ((b * seqlen + t0) * ngroups + g) * (int64_t)N;
+        const T* cb = Cm + ((b * seqlen + t0) * ngroups + g) * (int64_t)N;
         const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<TB*>(cb), 0, ((len - 1) * ngroups + 1) * N * (int)sizeof(TB), kBufferDword3);
+            const_cast<T*>(cb), 0, ((len - 1) * ngroups + 1) * N * (int)sizeof(T), kBufferDword3);
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int l = 16 * rbk[j] + r16;
@@ -207,7 +195,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
             for (int ks = 0; ks < NK; ++ks) {
                 const int col = 32 * ks + 8 * grp;
-                buffer_load8(cf[j][ks], crs, rok && col < N ? (l * ngroups * N + col) * (int)sizeof(TB) : kDropped);
+                buffer_load8(cf[j][ks], crs, rok && col < N ? (l * ngroups * N + col) * (int)sizeof(T) : kDropped);
             }
         }
     }
@@ -248,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             if constexpr (EPI == 2) tok = b * xl.rev_L + min((int64_t)seqlen - 1 - tau, xl.rev_L - 1);   // reversed x
             return x + tok * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs + ch * EPC;
         });
-        const TB* bg = Bm + (int64_t)g * N;
+        const T* bg = Bm + (int64_t)g * N;
         tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
             return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * S::EPB, N - S::EPB);
         });
@@ -314,8 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 for (int pt = 0; pt < P / 16; ++pt) {
                     Vec8<T> af;
                     swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
-                    mma(acc[0][hh][pt], af, as_t(cf[0][sl * (SW / 32) + kk], T{}));
-                    mma(acc[1][hh][pt], af, as_t(cf[1][sl * (SW / 32) + kk], T{}));
+                    mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
+                    mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
                     if constexpr (S::kSplit) {
                         swz_load8<S::S_CH>(af, stl + HB * S::sh_bytes, 16 * pt + r16, 32 * kk + 8 * grp);
                         mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
@@ -364,7 +352,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 gt[st2] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NK; ++ks) {
-                    Vec8<TB> af;
+                    Vec8<T> af;
                     swz_load8<S::B_CH>(af, bt, 16 * st2 + r16, 32 * ks + 8 * grp);
                     mma(gt[st2], af, cf[j][ks]);
                 }
@@ -558,13 +546,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     }
 }
 
-template <typename T, typename TB, typename TY, int P, int NK, bool V, class S, int EPI>
-hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
+template <typename T, typename TY, int P, int NK, bool V, class S, int EPI>
+hipError_t launch_shape(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
                         int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
                         hipStream_t stream, const ScanEpi& epi)
 {
     static_assert(S::fits, "LDS budget");
-    static_assert(!S::kSplit || (std::is_same_v<T, bf16> && std::is_same_v<TB, bf16> && std::is_same_v<TY, float>),
+    static_assert(!S::kSplit || (std::is_same_v<T, bf16> && std::is_same_v<TY, float>),
                   "split products: bf16 operands, fp32 output");
     constexpr int HB = S::kHeads;
     const int nc = (int)d.nchunks();
@@ -575,7 +563,7 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
     const int nhalf = (npairs + kWaves - 1) / kWaves;    // workgroups per (chunk, head block)
     const int64_t nblocks = d.batch * nc * d.ngroups * nhb * nhalf;
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL((chunk_scan_kernel<T, TB, TY, P, NK, S, V, EPI>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((chunk_scan_kernel<T, TY, P, NK, S, V, EPI>), dim3((unsigned)nblocks), dim3(kThreads), 0, stream,
                        x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, (int)d.seqlen, (int)d.nheads, (int)d.ngroups,
                        (int)d.dstate, (int)d.chunk, nc, nhb, hpw, nhalf, (int)nblocks, epi);
     return hipGetLastError();
@@ -583,25 +571,25 @@ hipError_t launch_shape(const T* x, const TB* B, const TB* C, const float* dtc, 
 
 // groups of a single head (the backward's per-head passes) take the one-head shape: a wider one
 // would compute a clamped copy of the head in its other slots
-template <typename T, typename TB, typename TY, int P, int NK, bool V, int SP, int EPI>
-hipError_t launch(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
+template <typename T, typename TY, int P, int NK, bool V, int SP, int EPI>
+hipError_t launch(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
                   int64_t lo_off, const float* D, const int* tstart, TY* y, const XLayout& xl, const Dims& d,
                   hipStream_t stream, const ScanEpi& epi)
 {
-    using S = ScanShape<T, TB, P, NK, V, SP>;
+    using S = ScanShape<T, P, NK, V, SP>;
     if constexpr (S::kHeads > 1) {
         if (d.nheads == d.ngroups) {
-            using S1 = typename decltype(pick_shape<T, TB, P, NK, 1, V, SP>())::type;
-            return launch_shape<T, TB, TY, P, NK, V, S1, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d,
+            using S1 = typename decltype(pick_shape<T, P, NK, 1, V, SP>())::type;
+            return launch_shape<T, TY, P, NK, V, S1, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d,
                                                               stream, epi);
         }
     }
-    return launch_shape<T, TB, TY, P, NK, V, S, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream,
+    return launch_shape<T, TY, P, NK, V, S, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream,
                                                      epi);
 }
 
-template <typename T, typename TB, typename TY, bool V, int SP = 1, int EPI = 0>
-hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, const float* cs, const T* entry,
+template <typename T, typename TY, bool V, int SP = 1, int EPI = 0>
+hipError_t launch_any(const T* x, const T* B, const T* C, const float* dtc, const float* cs, const T* entry,
                       const float* D, const int* tstart, TY* y, const Dims& d, hipStream_t stream,
                       XLayout xl = XLayout{0, 0, 0}, int64_t lo_off = 0, const ScanEpi& epi = ScanEpi{})
 {
@@ -614,7 +602,7 @@ hipError_t launch_any(const T* x, const TB* B, const TB* C, const float* dtc, co
     }
 #define SSD_SCAN_CASE(PP, KK) \
     if (d.headdim == PP && nki == KK) \
-        return launch<T, TB, TY, PP, KK, V, SP, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream, epi);
+        return launch<T, TY, PP, KK, V, SP, EPI>(x, B, C, dtc, cs, entry, lo_off, D, tstart, y, xl, d, stream, epi);
 #define SSD_SCAN_P(PP) SSD_SCAN_CASE(PP, 1) SSD_SCAN_CASE(PP, 2) SSD_SCAN_CASE(PP, 4) SSD_SCAN_CASE(PP, 8)
     SSD_SCAN_P(16) SSD_SCAN_P(32) SSD_SCAN_P(64) SSD_SCAN_P(128)
 #undef SSD_SCAN_P
@@ -629,7 +617,7 @@ hipError_t launch_chunk_scan(const T* x, const T* B, const T* C, const float* dt
                              const float* dA_cs, const T* entry_states, const float* D, T* y,
                              const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+    return launch_any<T, T, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
 }
 
 template <typename T>
@@ -637,7 +625,7 @@ hipError_t launch_chunk_scan_f32out(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, float* y,
                                     const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
+    return launch_any<T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
 }
 
 template <typename T>
@@ -645,29 +633,14 @@ hipError_t launch_chunk_scan_f32out_xl(const T* x, const XLayout& xl, const T* B
                                        const float* dA_cs, const T* entry_states, const float* D, float* y,
                                        const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream, xl);
-}
-
-hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
-                                        const float* dA_cs, const float* entry_states, const float* D, float* y,
-                                        const Dims& d, hipStream_t stream)
-{
-    return launch_any<float, bf16, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream);
-}
-
-hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
-                                   const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
-                                   const Dims& d, hipStream_t stream)
-{
-    return launch_any<bf16, bf16, float, false, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, y, d, stream,
-                                                   XLayout{0, 0, 0}, lo_off);
+    return launch_any<T, float, false>(x, B, C, dt_chunked, dA_cs, entry_states, D, nullptr, y, d, stream, xl);
 }
 
 hipError_t launch_chunk_scan_split_dot(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
                                        const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
                                        const ScanEpi& epi, const Dims& d, hipStream_t stream)
 {
-    return launch_any<bf16, bf16, float, false, 2, 1>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
+    return launch_any<bf16, float, false, 2, 1>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
                                                       stream, XLayout{0, 0, 0}, lo_off, epi);
 }
 
@@ -675,7 +648,7 @@ hipError_t launch_chunk_scan_split_grad(const bf16* x, const bf16* B, const bf16
                                         const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
                                         const ScanEpi& epi, const Dims& d, hipStream_t stream)
 {
-    return launch_any<bf16, bf16, float, false, 2, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
+    return launch_any<bf16, float, false, 2, 2>(x, B, C, dt_chunked, dA_cs, entry_hi, D, nullptr, nullptr, d,
                                                       stream, XLayout{0, 0, 0, epi.L}, lo_off, epi);
 }
 
@@ -684,7 +657,7 @@ hipError_t launch_chunk_scan_varlen(const T* x, const T* B, const T* C, const fl
                                     const float* dA_cs, const T* entry_states, const float* D, const int* tstart,
                                     T* y, const Dims& d, hipStream_t stream)
 {
-    return launch_any<T, T, T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
+    return launch_any<T, T, true>(x, B, C, dt_chunked, dA_cs, entry_states, D, tstart, y, d, stream);
 }
 
 template hipError_t launch_chunk_scan<float>(const float*, const float*, const float*, const float*,
@@ -696,9 +669,6 @@ template hipError_t launch_chunk_scan<bf16>(const bf16*, const bf16*, const bf16
 template hipError_t launch_chunk_scan_f32out<float>(const float*, const float*, const float*, const float*,
                                                     const float*, const float*, const float*, float*,
                                                     const Dims&, hipStream_t);
-template hipError_t launch_chunk_scan_f32out<bf16>(const bf16*, const bf16*, const bf16*, const float*,
-                                                   const float*, const bf16*, const float*, float*,
-                                                   const Dims&, hipStream_t);
 template hipError_t launch_chunk_scan_f32out_xl<float>(const float*, const XLayout&, const float*, const float*,
                                                        const float*, const float*, const float*, const float*,
                                                        float*, const Dims&, hipStream_t);

@@ -87,16 +87,10 @@ hipError_t launch_chunk_scan_f32out_xl(const T* x, const XLayout& xl, const T* B
                                        const float* dA_cs, const T* entry_states, const float* D, float* y,
                                        const Dims& d, hipStream_t stream);
 
-// the same in fp32 with B and C given in bf16 (arrays that hold bf16 values): C.B^T on the bf16
-// matrix cores, everything else in fp32
-hipError_t launch_chunk_scan_f32_bf16bc(const float* x, const bf16* B, const bf16* C, const float* dt_chunked,
-                                        const float* dA_cs, const float* entry_states, const float* D, float* y,
-                                        const Dims& d, hipStream_t stream);
-// the same result to within 2^-18 of each product, from bf16 products: x, B, C given in bf16 (arrays that
-// hold bf16 values), the entry states as two bf16 planes (hi at entry_hi, lo at entry_hi + lo_off)
-hipError_t launch_chunk_scan_split(const bf16* x, const bf16* B, const bf16* C, const float* dt_chunked,
-                                   const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D, float* y,
-                                   const Dims& d, hipStream_t stream);
+// the backward's readouts for bf16 inputs: fp32 results to within 2^-18 of each product from bf16
+// products -- x, B, C given in bf16 (arrays that hold bf16 values), the entry states as two bf16
+// planes (hi at entry_hi, lo at entry_hi + lo_off), the fp32 decayed scores split likewise in
+// registers.
 // The backward's readout passes with the per-token work folded into the output stage (y not stored):
 // (o1, o2 indexed (batch, head, token))
 //   ..._dot:  o1[b, h, t] = sum_p dy[b, t, h, p] y[b, t, h, p]
