@@ -4,8 +4,9 @@
 // Within one chunk (tokens l, s; cs_h the head's in-chunk cumulative log-decay, dt_h its steps), let
 //   M_h[l, s] = (dy_h,l . x_h,s) exp(cs_h[l] - cs_h[s]) dt_h[s]    for s <= l, else 0,
 // the decayed, masked score of the quadratic form (the masked matrix of the mohakchugh blog, section
-// "The Duality") with dy in the place of C.  y_h,l depends on C_l through sum_{s<=l} (C_l . B_s) ... and
-// on B_s through the same products and through the chunk's state, so for a group's B and C
+// "The Duality") with dy in the place of C.  Inside a chunk, y_h,l takes C_l and B_s (s <= l) through
+// the products C_l . B_s of that form; C_l also reads out the state entering the chunk, and B_s also
+// feeds the state the chunk hands on.  So for a group's B and C
 //   dC[l] = sum_s M[l, s] B_s  +  sum_h exp(cs_h[l]) S_in,h^T dy_h,l
 //   dB[s] = sum_l M[l, s] C_l  +  sum_h exp(cs_h[Q-1] - cs_h[s]) dt_h[s] Gout_h^T x_h,s
 // with M = sum over the group's heads of M_h (one Q x Q matrix per batch, chunk and group),
@@ -16,11 +17,12 @@
 //               added into fp32 accumulators; the slices' partial sums go to workspace
 //   bwd_inter   the two state terms, per (batch, chunk, group, 64-row block, half of the state
 //               columns, slice of the heads; partial sums per slice): per head, the rows of dy (x)
-//               scaled by their decay and rounded to bf16 as
-//               one operand, the S_in (Gout) tile (bf16, the hi plane of the pair) read transposed
-//               from LDS as the other; the sum over heads runs in the matrix-core accumulators
+//               scaled by their decay and rounded to bf16 as one operand, the S_in (Gout) tile
+//               (bf16, the hi plane of the pair) read transposed from LDS as the other; the sum
+//               over heads runs in the matrix-core accumulators
 //   bwd_dbc     dC and dB of the group: M (the slices summed, split into bf16 hi + lo) times the
-//               chunk's B and C tiles, plus the state terms, rounded to bf16 once
+//               chunk's B and C tiles, plus the state terms (their slices summed), rounded to bf16
+//               once
 // Operands reach LDS by asynchronous global->LDS copies (XOR-swizzled tiles; the next head's
 // tiles fly while the current head is multiplied) or registers by range-checked buffer loads (rows
 // past the sequence read zero).  Requires headdim % 32 == 0 and chunk % 64 == 0.
@@ -302,7 +304,8 @@ __global__ __launch_bounds__(kT, 2) void bwd_inter_kernel(const bf16* __restrict
 // dC and dB of the group.  Wavefront w owns tokens r = 64 rb + 16 w + r16 (a row of dC, a column
 // of M for dB); D[n][r] = sum_s B^T[n][s] M[r][s] (dC) and sum_l C^T[n][l] M[l][r] (dB), the B and
 // C tiles read transposed from LDS (8 contraction slots per lane: tokens k0 + 4 grp + m and
-// k0 + 16 + 4 grp + m), M (the slices summed in fp32) split into bf16 hi + lo.
+// k0 + 16 + 4 grp + m), M (the slices summed in fp32) split into bf16 hi + lo; the state terms'
+// slices are added before the one rounding to bf16.
 template <int NT>
 __global__ __launch_bounds__(kT) void bwd_dbc_kernel(const bf16* __restrict__ Bm, const bf16* __restrict__ Cm,
                                                      const float* __restrict__ Mp, const float* __restrict__ dCi,
