@@ -525,6 +525,43 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 __syncthreads();                               // the staging area is rewritten next
             }
         }
+    } else if constexpr (std::is_same_v<TY, bf16> && !kVarlen) {
+        // y through LDS (the ring is free now): one row block at a time, each wavefront stages its 16
+        // rows of all the workgroup's heads as bf16, then stores whole token rows -- the heads of a
+        // token are adjacent in y, so a row is HB * P * 2 contiguous bytes -- in 16-byte pieces
+        constexpr int kRowW = HB * P / 2 + 8;                   // 4-byte words per staged row (padded)
+        constexpr int CPR = HB * P * 2 / 16;                    // 16-byte pieces per row
+        constexpr int kIter = (16 * CPR + 63) / 64;
+        static_assert(kWaves * 16 * kRowW * 4 <= S::region, "y staging");
+        unsigned* const ys = reinterpret_cast<unsigned*>(region) + wave * 16 * kRowW;
+        TY* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(yb, 0, len * nheads * P * (int)sizeof(TY), kBufferDword3);
+        __syncthreads();                                        // every wavefront is done with the ring
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+                for (int pt = 0; pt < P / 16; ++pt) {
+                    const f32x4 v = acc[j][hh][pt];
+                    bf16x4 q;
+                    q[0] = static_cast<bf16>(v[0]); q[1] = static_cast<bf16>(v[1]);
+                    q[2] = static_cast<bf16>(v[2]); q[3] = static_cast<bf16>(v[3]);
+                    *reinterpret_cast<bf16x4*>(ys + r16 * kRowW + hh * (P / 2) + 8 * pt + 2 * grp) = q;
+                }
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kIter; ++it) {
+                const int idx = it * 64 + lane, rr = min(idx / CPR, 15), cc = idx % CPR;
+                const int row = 16 * rbk[j] + rr, hh = cc * 8 / P;
+                const uint4 v = *reinterpret_cast<const uint4*>(ys + rr * kRowW + 4 * cc);
+                const bool ok = idx < 16 * CPR && has[j] && row < len && hh < nh;
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs,
+                                                       ok ? (row * nheads * P + cc * 8) * 2 : kDropped, 0, 0);
+            }
+            __syncthreads();                                    // the staging area is rewritten next
+        }
     } else {
         TY* yb = y + ((b * seqlen + t0) * nheads + h0) * (int64_t)P;
         const __amdgpu_buffer_rsrc_t rs =
