@@ -525,7 +525,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 __syncthreads();                               // the staging area is rewritten next
             }
         }
-    } else if constexpr (std::is_same_v<TY, bf16> && !kVarlen) {
+    } else if constexpr (std::is_same_v<TY, bf16>) {
         // y through LDS (the ring is free now): one row block at a time, each wavefront stages its 16
         // rows of all the workgroup's heads as bf16, then stores whole token rows -- the heads of a
         // token are adjacent in y, so a row is HB * P * 2 contiguous bytes -- in 16-byte pieces
