@@ -260,9 +260,38 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
         }
     }
 
-    if (hh < nh && p0 < P) {
-        float* out = seqwg ? va.final_states + (((int64_t)kseq * nheads + h0 + hh) * P) * N
-                           : chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + hh) * P) * N;
+    // The states leave through LDS (the ring is free now), RB row blocks at a time: each wavefront
+    // stages its rows and stores them back as contiguous row pieces of NT * 16 floats, 16 bytes per
+    // lane, instead of 64-byte pieces of 16 rows (when a ring is too small for one row block of
+    // every wavefront, the accumulators are stored directly).
+    constexpr int kPitch = NT * 16 + 4;                          // floats per staged row
+    constexpr int kRing = kStages * S::stage_bytes;
+    constexpr int kBlock = kWaves * 16 * kPitch * 4;             // one row block of every wavefront
+    constexpr int RB = kBlock * PT <= kRing ? PT : (PT % 2 == 0 && kBlock * (PT / 2) <= kRing) ? PT / 2 : 1;
+    constexpr int kPieces = NT * 4;                               // 16-byte pieces per staged row
+    const bool live = hh < nh && p0 < P;
+    float* out = seqwg ? va.final_states + (((int64_t)kseq * nheads + h0 + min(hh, nh - 1)) * P) * N
+                       : chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + min(hh, nh - 1)) * P) * N;
+    if constexpr (kBlock <= kRing) {
+        float* const st = reinterpret_cast<float*>(ring) + wave * RB * 16 * kPitch;
+#pragma unroll
+        for (int r0 = 0; r0 < PT; r0 += RB) {
+            __syncthreads();                   // the ring (first round) or the previous round is free
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+                for (int q = 0; q < RB; ++q)
+                    *reinterpret_cast<f32x4*>(st + (16 * q + r16) * kPitch + 16 * nt + 4 * grp) = acc[nt][r0 + q];
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < RB * 16 * kPieces / 64; ++i) {
+                const int idx = i * 64 + lane, row = idx / kPieces, pc = idx % kPieces;
+                const int n = n0 + 4 * pc;
+                const f32x4 v = *reinterpret_cast<const f32x4*>(st + row * kPitch + 4 * pc);
+                if (live && n < N) *reinterpret_cast<f32x4*>(out + (int64_t)(p0 + 16 * r0 + row) * N + n) = v;
+            }
+        }
+    } else if (live) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int n = n0 + 16 * nt + 4 * grp;
