@@ -461,68 +461,71 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             }
         }
     } else if constexpr (EPI == 2) {
-        // dx, x . du, x . dy per (token, head): each wavefront passes its 16-row tiles through LDS (the
-        // ring is free now) and reads them back row-major, CPR lanes per row with 8 consecutive columns
-        // each, so the reads of x and dy and the stores of dx are whole 16-byte pieces of whole rows.
-        constexpr int kPitch = P + 4;                          // floats per staged row
-        constexpr int CPR = P / 8;                             // lanes per row
-        constexpr int RPI = 64 / CPR;                          // rows per pass
+        // y = du on the reversed sequence (row t0 + row is the caller's token seqlen - 1 - (t0 + row)):
+        // dx = dt du + D dy, o1 = x . du, o2 = x . dy per (token, head).  One row block at a time, each
+        // wavefront stages its 16 rows of all the workgroup's heads in LDS (the ring is free now) and
+        // reads them back row-major, 8 consecutive columns per lane -- a token's heads are adjacent in
+        // x, dy and dx, so those move as 16-byte pieces of HB * P * 2 contiguous bytes -- and P / 8
+        // lanes reduce each (token, head).  (The dot pass reduces straight from the accumulators: with
+        // one array to read, the staging's barriers cost it more than they save.)
+        constexpr int kPitch = HB * P + 4;                     // floats per staged row
+        constexpr int LPR = HB * P / 8;                        // lanes per row
+        constexpr int LPH = P / 8;                             // lanes per (row, head)
+        constexpr int RPI = 64 / LPR;                          // rows per pass
         constexpr int kIter = (16 + RPI - 1) / RPI;
-        static_assert(kWaves * 16 * kPitch * 4 <= S::region, "epilogue staging");
+        static_assert(kWaves * 16 * kPitch * 4 <= S::region && LPR <= 64, "epilogue staging");
         float* const ep = reinterpret_cast<float*>(region) + wave * 16 * kPitch;
-        __syncthreads();                                       // every wavefront is done with the ring
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            __syncthreads();                                   // the ring, or the previous row block, is free
 #pragma unroll
-            for (int hh = 0; hh < HB; ++hh) {
+            for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
                 for (int pt = 0; pt < P / 16; ++pt)
-                    *reinterpret_cast<f32x4*>(ep + r16 * kPitch + 16 * pt + 4 * grp) = acc[j][hh][pt];
-                __syncthreads();
+                    *reinterpret_cast<f32x4*>(ep + r16 * kPitch + hh * P + 16 * pt + 4 * grp) = acc[j][hh][pt];
+            __syncthreads();
+#pragma unroll
+            for (int it = 0; it < kIter; ++it) {
+                const int rr = it * RPI + lane / LPR, c8 = 8 * (lane % LPR);
+                const int hh = c8 / P, row = 16 * rbk[j] + rr;
                 const int h = h0 + min(hh, nh - 1);
-#pragma unroll
-                for (int it = 0; it < kIter; ++it) {
-                    const int rr = it * RPI + lane / CPR, cc = 8 * (lane % CPR);
-                    const int row = 16 * rbk[j] + rr;
-                    float v[8];
-                    {
-                        const float* e = ep + min(rr, 15) * kPitch + cc;
-                        const float4 a = *reinterpret_cast<const float4*>(e);
-                        const float4 b4 = *reinterpret_cast<const float4*>(e + 4);
-                        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-                        v[4] = b4.x; v[5] = b4.y; v[6] = b4.z; v[7] = b4.w;
-                    }
-                    // du on the reversed sequence: row t0 + row is the caller's token seqlen - 1 - (t0 + row)
-                    float s1 = 0.f, s2 = 0.f;
-                    const int64_t t = (int64_t)seqlen - 1 - (t0 + row);
-                    const bool ok = has[j] && rr < 16 && row < len && t >= 0 && t < epi.L && hh < nh;
-                    const int64_t r = (b * epi.L + min(max(t, (int64_t)0), epi.L - 1)) * nheads + h;
-                    if (ok) {
-                        const float dtv = epi.dt[r], dh = epi.D[h];
-                        Vec8<bf16> x8, d8, o8;
-                        load8(x8, epi.x + r * P + cc);
-                        load8(d8, epi.dy + r * P + cc);
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float xv = x8.get(e), dv = d8.get(e);
-                            o8.set(e, fmaf(dtv, v[e], dh * dv));
-                            s1 += xv * v[e];
-                            s2 += xv * dv;
-                        }
-                        store8(epi.dx + r * P + cc, o8);
-                    }
-#pragma unroll
-                    for (int m = 1; m < CPR; m <<= 1) {
-                        s1 += __shfl_xor(s1, m, kWave);
-                        s2 += __shfl_xor(s2, m, kWave);
-                    }
-                    if (ok && cc == 0) {
-                        const int64_t rt = ((int64_t)b * nheads + h) * epi.L + t;     // (batch, head, token)
-                        epi.o1[rt] = s1;
-                        epi.o2[rt] = s2;
-                    }
+                float v[8];
+                {
+                    const float* e = ep + min(rr, 15) * kPitch + c8;
+                    const float4 a = *reinterpret_cast<const float4*>(e);
+                    const float4 b4 = *reinterpret_cast<const float4*>(e + 4);
+                    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+                    v[4] = b4.x; v[5] = b4.y; v[6] = b4.z; v[7] = b4.w;
                 }
-                __syncthreads();                               // the staging area is rewritten next
+                float s1 = 0.f, s2 = 0.f;
+                const int64_t t = (int64_t)seqlen - 1 - (t0 + row);
+                const bool ok = has[j] && rr < 16 && row < len && t >= 0 && t < epi.L && hh < nh;
+                const int64_t tc = min(max(t, (int64_t)0), epi.L - 1);
+                const int64_t r = (b * epi.L + tc) * nheads + h;
+                const int64_t rt = ((int64_t)b * nheads + h) * epi.L + tc;     // (batch, head, token)
+                if (ok) {
+                    const float dtv = epi.dt[r], dh = epi.D[h];
+                    Vec8<bf16> x8, d8, o8;
+                    load8(x8, epi.x + r * P + c8 % P);
+                    load8(d8, epi.dy + r * P + c8 % P);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float xv = x8.get(e), dv = d8.get(e);
+                        o8.set(e, fmaf(dtv, v[e], dh * dv));
+                        s1 += xv * v[e];
+                        s2 += xv * dv;
+                    }
+                    store8(epi.dx + r * P + c8 % P, o8);
+                }
+#pragma unroll
+                for (int m = 1; m < LPH; m <<= 1) {
+                    s1 += __shfl_xor(s1, m, kWave);
+                    s2 += __shfl_xor(s2, m, kWave);
+                }
+                if (ok && c8 % P == 0) {
+                    epi.o1[rt] = s1;
+                    epi.o2[rt] = s2;
+                }
             }
         }
     } else if constexpr (std::is_same_v<TY, bf16>) {
