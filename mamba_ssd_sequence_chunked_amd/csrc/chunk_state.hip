@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     // The states leave through LDS (the ring is free now), RB row blocks at a time: each wavefront
     // stages its rows and stores them back as contiguous row pieces of NT * 16 floats, 16 bytes per
     // lane, instead of 64-byte pieces of 16 rows (when a ring is too small for one row block of
-    // every wavefront, the accumulators are stored directly).
+    // every wavefront, and in the pair-product mode, where the staging measured slower, the
+    // accumulators are stored directly).
     constexpr int kPitch = NT * 16 + 4;                          // floats per staged row
     constexpr int kRing = kStages * S::stage_bytes;
     constexpr int kBlock = kWaves * 16 * kPitch * 4;             // one row block of every wavefront
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     const bool live = hh < nh && p0 < P;
     float* out = seqwg ? va.final_states + (((int64_t)kseq * nheads + h0 + min(hh, nh - 1)) * P) * N
                        : chunk_states + ((((int64_t)b * nc + c) * nheads + h0 + min(hh, nh - 1)) * P) * N;
-    if constexpr (kBlock <= kRing) {
+    if constexpr (kBlock <= kRing && !kSplit) {
         float* const st = reinterpret_cast<float*>(ring) + wave * RB * 16 * kPitch;
 #pragma unroll
         for (int r0 = 0; r0 < PT; r0 += RB) {
