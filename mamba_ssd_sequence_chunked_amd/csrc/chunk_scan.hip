@@ -51,10 +51,13 @@
 //     compiler can overlap one head's LDS reads with another's products.
 //   * the skip term D x is added in the stage holding the rows, from the x
 //     tile already in LDS, in fp32.
-//   * y leaves straight from the accumulators through buffer stores (4
-//     consecutive values per lane); stores of rows past the sequence or of
-//     heads past the workgroup fall outside the buffer's range and are
-//     dropped.
+//   * y leaves through LDS when it is bf16 (the ring is free by then): one
+//     row block at a time, each wavefront stages its 16 rows of all the
+//     workgroup's heads and stores whole token rows -- a token's heads are
+//     adjacent in y, so a row is HB * P * 2 contiguous bytes -- in 16-byte
+//     pieces (fp32 y goes straight from the accumulators, 4 consecutive
+//     values per lane); stores of rows past the sequence or of heads past the
+//     workgroup fall outside the buffer's range and are dropped.
 // Workgroups are numbered head block fastest and renumbered so that
 // consecutive ones share an XCD (and the chunk's B and C in its L2).
 #include <type_traits>
