@@ -144,6 +144,17 @@ int ssd_backward(const void* x, const float* dt, const float* A, const void* B, 
                  int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* The same forward as one pass over the sequence per (batch, head), the state kept on chip (the
+ * chunk-ordered walk of the mohakchugh blog's block-decomposition outline, section "The Tensor Core
+ * Connection"): batch x nheads workgroups each step through the tokens in blocks of 32, so no chunk
+ * size and no workspace.  Arguments, layouts, results and errors as for ssd_forward (y and
+ * final_states to the same tolerance; the sums run in another order), plus SSD_ERR_SHAPE when
+ * headdim x (dstate rounded up to 32, 64, 128 or 256) exceeds 16384 (headdim 128 with dstate > 128).
+ * A workgroup per (batch, head) is little parallelism on a large GPU: ssd_forward is the fast path. */
+int ssd_forward_fused(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                      const float* init_states, void* y, float* final_states, int64_t batch, int64_t seqlen,
+                      int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, void* stream);
+
 /* Packed variable-length batch: nseq sequences stored back to back on one token axis of
  * total_tokens tokens, sequence k being tokens cu_seqlens[k] .. cu_seqlens[k+1]-1 (the padding-free
  * variable-length batches of the ql.gl page, section "Mamba-2 Changes More Than the Algorithm").

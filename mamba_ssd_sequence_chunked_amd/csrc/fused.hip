@@ -1,0 +1,276 @@
+// fused.hip - the chunked forward as one pass over the sequence per (batch, head).
+//
+// The block-decomposition outline of the mohakchugh blog (section "The Tensor Core Connection")
+// walks the chunks in order: each chunk's output is its quadratic, attention-like part plus the
+// state that enters it read out through C, and the state then moves on to the next chunk
+// (ql.gl, "The Core of SSD").  Here one workgroup per (batch, head) does exactly that, over blocks
+// of 32 tokens, with the state kept on chip for the whole sequence -- no chunk states, entry
+// states or cumulative sums go through memory and no workspace is needed:
+//
+//   cs[l]  = sum_{j <= l} dt_j A           (within the block)
+//   y_l    = exp(cs[l]) S C_l  +  sum_{s <= l} (C_l . B_s) exp(cs[l] - cs[s]) dt_s x_s  +  D x_l
+//   S     <- exp(cs[last]) S  +  sum_s x_s (dt_s exp(cs[last] - cs[s])) B_s^T
+//
+// The result is the chunked method's (the decomposition is exact; only the block size and the
+// order of the sums differ), the same roundings included: products on the matrix cores with fp32
+// sums, the decayed scores and the state rounded to the operand type where they enter a product,
+// the running state itself in fp32.  All three products run on the matrix cores:
+//   * G^T (tokens s x token l) = B C^T once per block, decayed and masked in fp32; in the
+//     accumulator layout it is already the B operand of y^T = X^T G^T (the X fragments are read with
+//     the same slot order: slots 0-3 hold tokens 4 grp + m, slots 4-7 tokens 16 + 4 grp + m)
+//   * the state readout S C^T from a copy of the state rounded to the operand type in LDS
+//   * the state update S^T += (w B)^T X straight into the accumulators that hold S^T
+// A workgroup is 4 wavefronts: wavefront w computes y for the block's tokens 16 (w & 1) .. +15
+// and the head-dimension tiles (w >> 1) + 2 i, and holds the state columns n in tiles w + 4 i.
+// This trades the chunked kernels' parallelism over chunks for a sequential walk: batch x heads
+// workgroups, each stepping through seqlen / 32 blocks.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr int kTB = 32;          // tokens per block
+constexpr int kThreads = 256;
+
+template <typename T, int P, int NP>
+__global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
+    const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ Bm,
+    const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ init, T* __restrict__ y,
+    float* __restrict__ final_states, int seqlen, int nheads, int ngroups, int N)
+{
+    constexpr int XP = P + 8, NPP = NP + 8;          // padded LDS rows (elements)
+    constexpr int PT = P / 16, NT = NP / 16, KN = NP / 32;
+    constexpr int YT = (PT + 1) / 2;                 // head-dimension tiles of y per wavefront
+    constexpr int NTW = (NT + 3) / 4;                // state column tiles per wavefront
+    constexpr int EV = 16 / (int)sizeof(T);          // elements per 16-byte access
+    __shared__ __attribute__((aligned(16))) T xs[kTB * XP];
+    __shared__ __attribute__((aligned(16))) T bs[kTB * NPP];
+    __shared__ __attribute__((aligned(16))) T cs_[kTB * NPP];
+    __shared__ __attribute__((aligned(16))) T sp[P * NPP];           // the state rounded to T, rows p
+    __shared__ float cum[kTB], ecs[kTB], wv[kTB], dtv[kTB];
+
+    const int bh = blockIdx.x, h = bh % nheads;
+    const int64_t b = bh / nheads;
+    const int g = h / (nheads / ngroups);
+    const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
+    const int wu = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const float a = A[h], dsk = Dv[h];
+
+    // S^T accumulators: sacc[i][pt] holds, per lane, p = 16 pt + r16 and n = 16 (wu + 4 i) + 4 grp + q
+    f32x4 sacc[NTW][PT];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            const int nt = wu + 4 * i, n = 16 * nt + 4 * grp;
+            f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (init && nt < NT && n < N)
+                v = *reinterpret_cast<const f32x4*>(init + ((int64_t)bh * P + 16 * pt + r16) * N + n);
+            sacc[i][pt] = v;
+        }
+    auto put_state = [&]() {
+#pragma unroll
+        for (int i = 0; i < NTW; ++i) {
+            const int nt = wu + 4 * i;
+            if (nt < NT) {
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+                    T* d = sp + (16 * pt + r16) * NPP + 16 * nt + 4 * grp;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) d[q] = from_f32<T>(sacc[i][pt][q]);
+                }
+            }
+        }
+    };
+    put_state();
+
+    const T* xh = x + (b * seqlen * nheads + h) * (int64_t)P;
+    const T* bg = Bm + (b * seqlen * ngroups + g) * (int64_t)N;
+    const T* cg = Cm + (b * seqlen * ngroups + g) * (int64_t)N;
+    for (int t0 = 0; t0 < seqlen; t0 += kTB) {
+        // the block's x, B, C rows (zero past the sequence and past N) and dt
+        for (int i = tid; i < kTB * P / EV; i += kThreads) {
+            const int r = i / (P / EV), c = (i % (P / EV)) * EV;
+            if constexpr (EV == 8) {
+                Vec8<T> v;
+                if (t0 + r < seqlen) load8(v, xh + (int64_t)(t0 + r) * nheads * P + c);
+                else v.zero();
+                store8(xs + r * XP + c, v);
+            } else {
+                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (t0 + r < seqlen) f = *reinterpret_cast<const float4*>(xh + (int64_t)(t0 + r) * nheads * P + c);
+                *reinterpret_cast<float4*>(xs + r * XP + c) = f;
+            }
+        }
+        for (int i = tid; i < kTB * NP / EV; i += kThreads) {
+            const int r = i / (NP / EV), c = (i % (NP / EV)) * EV;
+            const bool ok = t0 + r < seqlen && c < N;
+            const int64_t o = (int64_t)(t0 + r) * ngroups * N + c;
+            if constexpr (EV == 8) {
+                Vec8<T> vb, vc;
+                if (ok) {
+                    load8(vb, bg + o);
+                    load8(vc, cg + o);
+                } else {
+                    vb.zero();
+                    vc.zero();
+                }
+                store8(bs + r * NPP + c, vb);
+                store8(cs_ + r * NPP + c, vc);
+            } else {
+                float4 fb = make_float4(0.f, 0.f, 0.f, 0.f), fc = fb;
+                if (ok) {
+                    fb = *reinterpret_cast<const float4*>(bg + o);
+                    fc = *reinterpret_cast<const float4*>(cg + o);
+                }
+                *reinterpret_cast<float4*>(bs + r * NPP + c) = fb;
+                *reinterpret_cast<float4*>(cs_ + r * NPP + c) = fc;
+            }
+        }
+        if (tid < kTB) dtv[tid] = t0 + tid < seqlen ? dt[(b * seqlen + t0 + tid) * nheads + h] : 0.f;
+        __syncthreads();
+        // in-block prefix sums of dt A, the readout decays exp(cs) and the state weights
+        if (wu == 0) {
+            const float v = lane < kTB ? dtv[lane] * a : 0.f;
+            const float c = wave_inclusive_sum(v);
+            const float last = __shfl(c, kTB - 1, kWave);
+            if (lane < kTB) {
+                cum[lane] = c;
+                ecs[lane] = __expf(c);
+                wv[lane] = dtv[lane] * __expf(last - c);
+            }
+        }
+        __syncthreads();
+        const float elast = __expf(cum[kTB - 1]);
+
+        // ---- y of the wavefront's tokens l = 16 lt + r16 (the lane's column) and head-dimension tiles
+        const int lt = wu & 1, l = 16 * lt + r16;
+        Vec8<T> gf;                                      // G^T[s][l], slot order as in the header
+        {
+            f32x4 d0 = f32x4{0.f, 0.f, 0.f, 0.f}, d1 = d0;
+#pragma unroll
+            for (int kk = 0; kk < KN; ++kk) {
+                Vec8<T> cf, b0, b1;
+                load8(cf, cs_ + l * NPP + 32 * kk + 8 * grp);
+                load8(b0, bs + r16 * NPP + 32 * kk + 8 * grp);
+                load8(b1, bs + (16 + r16) * NPP + 32 * kk + 8 * grp);
+                mma(d0, b0, cf);
+                mma(d1, b1, cf);
+            }
+            const float cl = cum[l];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s0 = 4 * grp + q, s1 = 16 + s0;
+                gf.set(q, select(s0 <= l, d0[q] * (__expf(fminf(cl - cum[s0], 0.f)) * dtv[s0]), 0.f));
+                gf.set(4 + q, select(s1 <= l, d1[q] * (__expf(fminf(cl - cum[s1], 0.f)) * dtv[s1]), 0.f));
+            }
+        }
+        const float el = ecs[l];
+        const bool lok = t0 + l < seqlen;
+#pragma unroll
+        for (int i = 0; i < YT; ++i) {
+            const int pt = (wu >> 1) + 2 * i;
+            if (pt < PT) {
+                f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KN; ++kk) {
+                    Vec8<T> sf, cf;
+                    load8(sf, sp + (16 * pt + r16) * NPP + 32 * kk + 8 * grp);
+                    load8(cf, cs_ + l * NPP + 32 * kk + 8 * grp);
+                    mma(acc, sf, cf);
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] *= el;
+                Vec8<T> xf;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int s = (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
+                    xf.set(e, to_f32(xs[s * XP + 16 * pt + r16]));
+                }
+                mma(acc, xf, gf);
+                const int p = 16 * pt + 4 * grp;
+                if (lok) {
+                    const T* xr = xs + l * XP + p;
+                    store4(y + ((b * seqlen + t0 + l) * nheads + h) * (int64_t)P + p,
+                           acc[0] + dsk * to_f32(xr[0]), acc[1] + dsk * to_f32(xr[1]),
+                           acc[2] + dsk * to_f32(xr[2]), acc[3] + dsk * to_f32(xr[3]));
+                }
+            }
+        }
+
+        // ---- the state: S^T (n x p) <- exp(cs[last]) S^T + (w B)^T X over the block's tokens (slots s = 8 grp + e)
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+            Vec8<T> xb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xb.set(e, to_f32(xs[(8 * grp + e) * XP + 16 * pt + r16]));
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int nt = wu + 4 * i;
+                if (nt < NT) {
+                    Vec8<T> wb;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int s = 8 * grp + e;
+                        wb.set(e, to_f32(bs[s * NPP + 16 * nt + r16]) * wv[s]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) sacc[i][pt][q] *= elast;
+                    mma(sacc[i][pt], wb, xb);
+                }
+            }
+        }
+        __syncthreads();                                 // every read of this block's tiles and state is done
+        put_state();                                     // (read after the next block's first barrier)
+    }
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        const int nt = wu + 4 * i, n = 16 * nt + 4 * grp;
+        if (nt < NT && n < N) {
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                *reinterpret_cast<f32x4*>(final_states + ((int64_t)bh * P + 16 * pt + r16) * N + n) = sacc[i][pt];
+        }
+    }
+}
+
+template <typename T, int P, int NP>
+hipError_t launch(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
+                  const float* init, T* y, float* final_states, const Dims& d, hipStream_t s)
+{
+    const int64_t nblocks = d.batch * d.nheads;
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL((ssd_fused_kernel<T, P, NP>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, x, dt, A, B, C,
+                       D, init, y, final_states, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int fused_state_width(int64_t dstate) { return dstate <= 32 ? 32 : dstate <= 64 ? 64 : dstate <= 128 ? 128 : 256; }
+
+bool fused_supported(const Dims& d) { return d.headdim * fused_state_width(d.dstate) <= 16384; }
+
+template <typename T>
+hipError_t launch_ssd_fused(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
+                            const float* init, T* y, float* final_states, const Dims& d, hipStream_t s)
+{
+    const int np = fused_state_width(d.dstate);
+#define SSD_FUSED_CASE(PP, NN) \
+    if (d.headdim == PP && np == NN) return launch<T, PP, NN>(x, dt, A, B, C, D, init, y, final_states, d, s);
+#define SSD_FUSED_P(PP) SSD_FUSED_CASE(PP, 32) SSD_FUSED_CASE(PP, 64) SSD_FUSED_CASE(PP, 128)
+    SSD_FUSED_P(16) SSD_FUSED_P(32) SSD_FUSED_P(64) SSD_FUSED_P(128)
+    SSD_FUSED_CASE(16, 256) SSD_FUSED_CASE(32, 256) SSD_FUSED_CASE(64, 256)
+#undef SSD_FUSED_P
+#undef SSD_FUSED_CASE
+    return hipErrorInvalidValue;
+}
+
+template hipError_t launch_ssd_fused<float>(const float*, const float*, const float*, const float*, const float*,
+                                            const float*, const float*, float*, float*, const Dims&, hipStream_t);
+template hipError_t launch_ssd_fused<bf16>(const bf16*, const float*, const float*, const bf16*, const bf16*,
+                                           const float*, const float*, bf16*, float*, const Dims&, hipStream_t);
+
+}  // namespace ssd

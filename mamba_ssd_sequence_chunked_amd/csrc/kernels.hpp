@@ -114,6 +114,13 @@ hipError_t launch_chunk_scan_split_grad(const bf16* x, const bf16* B, const bf16
                                         const float* dA_cs, const bf16* entry_hi, int64_t lo_off, const float* D,
                                         const ScanEpi& epi, const Dims& d, hipStream_t stream);
 
+// the forward as one pass over the sequence per (batch, head), the state on chip (fused.hip):
+// headdim * (dstate rounded up to 32, 64, 128 or 256) <= 16384
+bool fused_supported(const Dims& d);
+template <typename T>
+hipError_t launch_ssd_fused(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
+                            const float* init, T* y, float* final_states, const Dims& d, hipStream_t stream);
+
 template <typename T>
 hipError_t launch_ssd_step(float* state, const T* x, const float* dt, const float* A, const T* B,
                            const T* C, const float* D, T* y, const Dims& d, hipStream_t stream);

@@ -313,6 +313,38 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
     return hip_status(e);
 }
 
+int ssd_forward_fused(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
+                      const float* init_states, void* y, float* final_states, int64_t batch, int64_t seqlen,
+                      int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, void* stream)
+{
+    Dims d{batch, seqlen, nheads, headdim, dstate, ngroups, 256};
+    if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
+    int rc = check_seq(d);
+    if (rc != SSD_OK) return rc;
+    if (!ssd::fused_supported(d)) return SSD_ERR_SHAPE;
+    if (batch == 0) return SSD_OK;
+    if (!final_states) return SSD_ERR_NULL;
+    if (seqlen > 0 && (!x || !dt || !A || !B || !C || !D || !y)) return SSD_ERR_NULL;
+    if (!aligned16(x) || !aligned16(B) || !aligned16(C) || !aligned16(y) || !aligned16(init_states) ||
+        !aligned16(final_states))
+        return SSD_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    const size_t nx = (size_t)(batch * seqlen * nheads * headdim) * es;
+    const size_t nb = (size_t)(batch * seqlen * ngroups * dstate) * es;
+    const size_t nfin = (size_t)(batch * nheads * headdim * dstate) * 4;
+    const size_t ndt = (size_t)(batch * seqlen * nheads) * 4;
+    if (any_overlap({{y, nx}, {final_states, nfin}},
+                    {{x, nx}, {dt, ndt}, {A, (size_t)nheads * 4}, {B, nb}, {C, nb}, {D, (size_t)nheads * 4},
+                     {init_states, nfin}}))
+        return SSD_ERR_ALIAS;
+    hipStream_t s = (hipStream_t)stream;
+    if (dtype == SSD_BF16)
+        return hip_status(ssd::launch_ssd_fused<bf16>((const bf16*)x, dt, A, (const bf16*)B, (const bf16*)C, D,
+                                                      init_states, (bf16*)y, final_states, d, s));
+    return hip_status(ssd::launch_ssd_fused<float>((const float*)x, dt, A, (const float*)B, (const float*)C, D,
+                                                   init_states, (float*)y, final_states, d, s));
+}
+
 size_t ssd_forward_varlen_workspace_bytes(int64_t total_tokens, int64_t nheads, int64_t headdim, int64_t dstate,
                                           int64_t chunk_size, int dtype)
 {

@@ -51,6 +51,8 @@ def load_library():
     lib.ssd_forward_workspace_bytes.argtypes = [i64] * 6 + [i32]
     lib.ssd_forward.restype = i32
     lib.ssd_forward.argtypes = [vp] * 9 + [i64] * 7 + [i32, vp, sz, vp]
+    lib.ssd_forward_fused.restype = i32
+    lib.ssd_forward_fused.argtypes = [vp] * 9 + [i64] * 6 + [i32, vp]
     lib.ssd_dA_cumsum.restype = i32
     lib.ssd_dA_cumsum.argtypes = [fp] * 4 + [i64] * 4 + [vp]
     lib.ssd_chunk_state.restype = i32
@@ -161,6 +163,30 @@ def forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                          _ptr(final), b, L, H, P, N, G, chunk_size, code, _ptr(workspace),
                          workspace.numel(), _stream(dev))
     _check("ssd_forward", rc)
+    return y, final
+
+
+def forward_fused(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                  D: torch.Tensor, init_states: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """One pass over the sequence per (batch, head), the state on chip: returns (y, final_states);
+    see ssd_forward_fused in include/ssd.h."""
+    lib = load_library()
+    b, L, H, P, N, G = _forward_dims(x, B)
+    dev = x.device
+    code = _dtype_code(x)
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    y = torch.empty_like(x)
+    final = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    rc = lib.ssd_forward_fused(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states), _ptr(y),
+                               _ptr(final), b, L, H, P, N, G, code, _stream(dev))
+    _check("ssd_forward_fused", rc)
     return y, final
 
 

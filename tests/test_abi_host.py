@@ -35,7 +35,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert {"ssd_forward", "ssd_step", "ssd_forward_workspace_bytes", "ssd_status_string", "ssd_dA_cumsum",
             "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_selective_scan", "ssd_forward_varlen",
-            "ssd_forward_varlen_workspace_bytes", "ssd_backward", "ssd_backward_workspace_bytes"} <= set(names)
+            "ssd_forward_varlen_workspace_bytes", "ssd_backward", "ssd_backward_workspace_bytes", "ssd_forward_fused"} <= set(names)
     for n in names:
         assert hasattr(lib, n), f"{n} is declared in include/ssd.h but not exported"
 
@@ -150,6 +150,21 @@ def test_forward_varlen_rejects():
     up = lambda v: (v + 255) // 256 * 256    # noqa: E731
     assert ws == 2 * up(4 * nc * 64 * 4) + up(nc * 4 * 16 * 16 * 4) * 2 + up(300 * 4) + up(nc * 16)
     assert lib.ssd_forward_varlen_workspace_bytes(300, 4, 48, 16, 64, 0) == 0
+
+
+def test_fused_rejects():
+    """ssd_forward_fused validates on the host before any launch (fake device pointers are never touched)."""
+    lib = ssd.load_library()
+    args = [fake(i) for i in range(1, 10)]
+    ok = dict(b=2, L=100, H=4, P=64, N=128, G=1)
+    def call(dtype=1, **kw):
+        d = {**ok, **kw}
+        return lib.ssd_forward_fused(*args, d["b"], d["L"], d["H"], d["P"], d["N"], d["G"], dtype, None)
+    assert call(P=128, N=256) == -2            # 128 x 256 state: beyond the on-chip limit
+    assert call(P=48) == -2                     # not a head size
+    assert call(G=3) == -2                      # heads not divisible by groups
+    assert call(dtype=7) == -3                  # dtype
+    assert call(b=0) == 0                       # nothing to do
 
 
 def test_backward_rejects():
