@@ -48,6 +48,7 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--no-scan", action="store_true", help="skip the Mamba-1 selective-scan comparison leg")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length leg")
+    ap.add_argument("--no-fused", action="store_true", help="skip the one-pass (fused) forward leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
     ap.add_argument("--backward-calls", type=int, default=20)
     ap.add_argument("--scan-calls", type=int, default=10)
@@ -295,6 +296,36 @@ def main():
                       traffic=measured_traffic("decode", "ssd_step"))
         print(f"[bench] ssd_step: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
 
+    # ---- the same forward as one pass over the sequence per (batch, head) (ssd_forward_fused)
+    fused = None
+    if not args.no_fused:
+        fy = torch.empty_like(y)
+        ffin = torch.empty_like(final)
+
+        def fused_call():
+            rc = lib.ssd_forward_fused(p(x), p(dt), p(A), p(B), p(C), p(D), p(init), p(fy), p(ffin), b, L, H, P, N, G,
+                                       code, sp)
+            if rc:
+                raise ssd.SSDError("ssd_forward_fused", rc)
+
+        for _ in range(5):
+            fused_call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        nf = max(1, min(args.steps, 20))
+        e0.record(stream)
+        for _ in range(nf):
+            fused_call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = 1e3 * e0.elapsed_time(e1) / nf
+        fused = dict(workload=f"{args.workload}, one workgroup per (batch, head) walking the sequence in 32-token "
+                              "blocks, the state on chip",
+                     calls=nf, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
+                     time_over_chunked=round(us / (1e3 * ms_per_step), 2))
+        print(f"[bench] fused forward: {us:.1f} us/call", file=sys.stderr, flush=True)
+        del fy, ffin
+
     # ---- packed variable-length batch: the same layer shape and token count, mixed sequence lengths
     varlen = None
     if not args.no_varlen and args.workload == "l2p7b":
@@ -445,6 +476,7 @@ def main():
         "ssd_step": decode,
         "backward": bwd,
         "varlen": varlen,
+        "fused_forward": fused,
         "selective_scan": scan,
         "cpu_baseline": cpu,
     }
