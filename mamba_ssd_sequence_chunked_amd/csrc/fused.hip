@@ -89,47 +89,52 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     const T* xh = x + (b * seqlen * nheads + h) * (int64_t)P;
     const T* bg = Bm + (b * seqlen * ngroups + g) * (int64_t)N;
     const T* cg = Cm + (b * seqlen * ngroups + g) * (int64_t)N;
+    // The block's x, B, C rows (zero past the sequence and past N) and dt go through registers: the
+    // next block's are loaded while the current one is multiplied.
+    constexpr int NXV = (kTB * P / EV + kThreads - 1) / kThreads;      // 16-byte pieces per thread
+    constexpr int NBV = (kTB * NP / EV + kThreads - 1) / kThreads;
+    uint4 rx[NXV], rb[NBV], rc[NBV];
+    float rdt = 0.f;
+    auto fetch = [&](int t0) {
+#pragma unroll
+        for (int k = 0; k < NXV; ++k) {
+            const int i = tid + k * kThreads, r = i / (P / EV), c = (i % (P / EV)) * EV;
+            rx[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < kTB * P / EV && t0 + r < seqlen)
+                rx[k] = *reinterpret_cast<const uint4*>(xh + (int64_t)(t0 + r) * nheads * P + c);
+        }
+#pragma unroll
+        for (int k = 0; k < NBV; ++k) {
+            const int i = tid + k * kThreads, r = i / (NP / EV), c = (i % (NP / EV)) * EV;
+            rb[k] = rc[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (i < kTB * NP / EV && t0 + r < seqlen && c < N) {
+                const int64_t o = (int64_t)(t0 + r) * ngroups * N + c;
+                rb[k] = *reinterpret_cast<const uint4*>(bg + o);
+                rc[k] = *reinterpret_cast<const uint4*>(cg + o);
+            }
+        }
+        if (tid < kTB) rdt = t0 + tid < seqlen ? dt[(b * seqlen + t0 + tid) * nheads + h] : 0.f;
+    };
+    auto stash = [&]() {
+#pragma unroll
+        for (int k = 0; k < NXV; ++k) {
+            const int i = tid + k * kThreads, r = i / (P / EV), c = (i % (P / EV)) * EV;
+            if (i < kTB * P / EV) *reinterpret_cast<uint4*>(xs + r * XP + c) = rx[k];
+        }
+#pragma unroll
+        for (int k = 0; k < NBV; ++k) {
+            const int i = tid + k * kThreads, r = i / (NP / EV), c = (i % (NP / EV)) * EV;
+            if (i < kTB * NP / EV) {
+                *reinterpret_cast<uint4*>(bs + r * NPP + c) = rb[k];
+                *reinterpret_cast<uint4*>(cs_ + r * NPP + c) = rc[k];
+            }
+        }
+        if (tid < kTB) dtv[tid] = rdt;
+    };
+    if (seqlen > 0) fetch(0);
     for (int t0 = 0; t0 < seqlen; t0 += kTB) {
-        // the block's x, B, C rows (zero past the sequence and past N) and dt
-        for (int i = tid; i < kTB * P / EV; i += kThreads) {
-            const int r = i / (P / EV), c = (i % (P / EV)) * EV;
-            if constexpr (EV == 8) {
-                Vec8<T> v;
-                if (t0 + r < seqlen) load8(v, xh + (int64_t)(t0 + r) * nheads * P + c);
-                else v.zero();
-                store8(xs + r * XP + c, v);
-            } else {
-                float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (t0 + r < seqlen) f = *reinterpret_cast<const float4*>(xh + (int64_t)(t0 + r) * nheads * P + c);
-                *reinterpret_cast<float4*>(xs + r * XP + c) = f;
-            }
-        }
-        for (int i = tid; i < kTB * NP / EV; i += kThreads) {
-            const int r = i / (NP / EV), c = (i % (NP / EV)) * EV;
-            const bool ok = t0 + r < seqlen && c < N;
-            const int64_t o = (int64_t)(t0 + r) * ngroups * N + c;
-            if constexpr (EV == 8) {
-                Vec8<T> vb, vc;
-                if (ok) {
-                    load8(vb, bg + o);
-                    load8(vc, cg + o);
-                } else {
-                    vb.zero();
-                    vc.zero();
-                }
-                store8(bs + r * NPP + c, vb);
-                store8(cs_ + r * NPP + c, vc);
-            } else {
-                float4 fb = make_float4(0.f, 0.f, 0.f, 0.f), fc = fb;
-                if (ok) {
-                    fb = *reinterpret_cast<const float4*>(bg + o);
-                    fc = *reinterpret_cast<const float4*>(cg + o);
-                }
-                *reinterpret_cast<float4*>(bs + r * NPP + c) = fb;
-                *reinterpret_cast<float4*>(cs_ + r * NPP + c) = fc;
-            }
-        }
-        if (tid < kTB) dtv[tid] = t0 + tid < seqlen ? dt[(b * seqlen + t0 + tid) * nheads + h] : 0.f;
+        stash();
+        if (t0 + kTB < seqlen) fetch(t0 + kTB);
         __syncthreads();
         // in-block prefix sums of dt A, the readout decays exp(cs) and the state weights
         if (wu == 0) {
