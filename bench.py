@@ -33,7 +33,8 @@ KERNEL_SOURCES = {"dA_cumsum": "dA_cumsum.hip", "chunk_state": "chunk_state.hip"
                   "chunk_state_cumsum": "chunk_state.hip", "chunk_state_varlen": "chunk_state.hip",
                   "state_passing": "state_passing.hip", "state_passing_varlen": "state_passing.hip",
                   "chunk_scan": "chunk_scan.hip", "chunk_scan_varlen": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
-                  "selective_scan": "selective_scan.hip", "varlen_meta": "varlen_meta.hip"}
+                  "selective_scan": "selective_scan.hip", "varlen_meta": "varlen_meta.hip",
+                  "ssd_fused": "fused.hip"}
 
 
 def parse_args():
@@ -319,10 +320,14 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         us = 1e3 * e0.elapsed_time(e1) / nf
-        fused = dict(workload=f"{args.workload}, one workgroup per (batch, head) walking the sequence in 32-token "
-                              "blocks, the state on chip",
+        # x read and y written once, B and C once per group, dt, the initial and final states
+        fbytes = 2 * b * L * H * P * es + 2 * b * L * G * N * es + 4 * b * L * H + 2 * 4 * b * H * P * N
+        fused = dict(workload=f"{args.workload}, one workgroup per (batch, head, 32-column slice of the head) "
+                              "walking the sequence in 32-token blocks, the state on chip",
                      calls=nf, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
-                     time_over_chunked=round(us / (1e3 * ms_per_step), 2))
+                     time_over_chunked=round(us / (1e3 * ms_per_step), 2), algorithmic_bytes=fbytes,
+                     achieved_gbs=round(fbytes / (us * 1e3), 1),
+                     traffic=measured_traffic(args.workload, "ssd_fused"))
         print(f"[bench] fused forward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del fy, ffin
 

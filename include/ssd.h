@@ -146,11 +146,11 @@ int ssd_backward(const void* x, const float* dt, const float* A, const void* B, 
 
 /* The same forward as one pass over the sequence per (batch, head), the state kept on chip (the
  * chunk-ordered walk of the mohakchugh blog's block-decomposition outline, section "The Tensor Core
- * Connection"): batch x nheads workgroups each step through the tokens in blocks of 32, so no chunk
- * size and no workspace.  Arguments, layouts, results and errors as for ssd_forward (y and
+ * Connection"): a workgroup per (batch, head, slice of the head dimension) steps through the tokens
+ * in blocks of 32, so no chunk size and no workspace.  Arguments, layouts, results and errors as for ssd_forward (y and
  * final_states to the same tolerance; the sums run in another order), plus SSD_ERR_SHAPE when
  * headdim x (dstate rounded up to 32, 64, 128 or 256) exceeds 16384 (headdim 128 with dstate > 128).
- * A workgroup per (batch, head) is little parallelism on a large GPU: ssd_forward is the fast path. */
+ * The sequential walk leaves little parallelism on a large GPU: ssd_forward is the fast path. */
 int ssd_forward_fused(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
                       const float* init_states, void* y, float* final_states, int64_t batch, int64_t seqlen,
                       int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, void* stream);
@@ -181,7 +181,7 @@ int ssd_forward_varlen(const void* x, const float* dt, const float* A, const voi
                        int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk_size, int dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
-/* Stage 1 (segment decays)./* Stage 1 (segment decays).  For every chunk c and position l inside it:
+/* Stage 1 (segment decays).  For every chunk c and position l inside it:
  *   dA_cs[b,h,c,l]      = sum_{j = cQ .. cQ+l} dt[b,j,h] * A[h]
  *   dt_chunked[b,h,c,l] = dt[b, cQ+l, h]
  * so that exp(dA_cs[l] - dA_cs[s]) is the decay product prod_{j=s+1..l} a_j

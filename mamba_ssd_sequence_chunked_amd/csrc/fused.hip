@@ -3,9 +3,9 @@
 // The block-decomposition outline of the mohakchugh blog (section "The Tensor Core Connection")
 // walks the chunks in order: each chunk's output is its quadratic, attention-like part plus the
 // state that enters it read out through C, and the state then moves on to the next chunk
-// (ql.gl, "The Core of SSD").  Here one workgroup per (batch, head) does exactly that, over blocks
-// of 32 tokens, with the state kept on chip for the whole sequence -- no chunk states, entry
-// states or cumulative sums go through memory and no workspace is needed:
+// (ql.gl, "The Core of SSD").  Here one workgroup per (batch, head, head-dimension slice) does
+// exactly that, over blocks of 32 tokens, with the state kept on chip for the whole sequence -- no
+// chunk states, entry states or cumulative sums go through memory and no workspace is needed:
 //
 //   cs[l]  = sum_{j <= l} dt_j A           (within the block)
 //   y_l    = exp(cs[l]) S C_l  +  sum_{s <= l} (C_l . B_s) exp(cs[l] - cs[s]) dt_s x_s  +  D x_l
@@ -22,8 +22,8 @@
 //   * the state update S^T += (w B)^T X straight into the accumulators that hold S^T
 // A workgroup is 4 wavefronts: wavefront w computes y for the block's tokens 16 (w & 1) .. +15
 // and the head-dimension tiles (w >> 1) + 2 i, and holds the state columns n in tiles w + 4 i.
-// This trades the chunked kernels' parallelism over chunks for a sequential walk: batch x heads
-// workgroups, each stepping through seqlen / 32 blocks.
+// This trades the chunked kernels' parallelism over chunks for a sequential walk: batch x heads x
+// slices workgroups, each stepping through seqlen / 32 blocks.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -32,13 +32,14 @@ namespace ssd {
 namespace {
 
 constexpr int kTB = 32;          // tokens per block
+constexpr int kMinSlice = 32;    // narrowest head-dimension slice per workgroup
 constexpr int kThreads = 256;
 
 template <typename T, int P, int NP>
 __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     const T* __restrict__ x, const float* __restrict__ dt, const float* __restrict__ A, const T* __restrict__ Bm,
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ init, T* __restrict__ y,
-    float* __restrict__ final_states, int seqlen, int nheads, int ngroups, int N)
+    float* __restrict__ final_states, int seqlen, int nheads, int ngroups, int N, int hd)
 {
     constexpr int XP = P + 8, NPP = NP + 8;          // padded LDS rows (elements)
     constexpr int PT = P / 16, NT = NP / 16, KN = NP / 32;
@@ -51,7 +52,11 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     __shared__ __attribute__((aligned(16))) T sp[P * NPP];           // the state rounded to T, rows p
     __shared__ float cum[kTB], ecs[kTB], wv[kTB], dtv[kTB];
 
-    const int bh = blockIdx.x, h = bh % nheads;
+    // P is the width of the head-dimension slice this workgroup owns (hd / P slices per head): y and
+    // the state rows of one slice depend on that slice of x only, so slices are independent and
+    // each recomputes the block's scores.  Consecutive slices and heads run on one XCD (shared L2).
+    const int nsl = hd / P, lb = xcd_logical_block(blockIdx.x, gridDim.x);
+    const int bh = lb / nsl, p0 = (lb % nsl) * P, h = bh % nheads;
     const int64_t b = bh / nheads;
     const int g = h / (nheads / ngroups);
     const int tid = threadIdx.x, lane = tid & 63, r16 = lane & 15, grp = lane >> 4;
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
             const int nt = wu + 4 * i, n = 16 * nt + 4 * grp;
             f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
             if (init && nt < NT && n < N)
-                v = *reinterpret_cast<const f32x4*>(init + ((int64_t)bh * P + 16 * pt + r16) * N + n);
+                v = *reinterpret_cast<const f32x4*>(init + ((int64_t)bh * hd + p0 + 16 * pt + r16) * N + n);
             sacc[i][pt] = v;
         }
     auto put_state = [&]() {
@@ -86,7 +91,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     };
     put_state();
 
-    const T* xh = x + (b * seqlen * nheads + h) * (int64_t)P;
+    const T* xh = x + (b * seqlen * nheads + h) * (int64_t)hd + p0;
     const T* bg = Bm + (b * seqlen * ngroups + g) * (int64_t)N;
     const T* cg = Cm + (b * seqlen * ngroups + g) * (int64_t)N;
     // The block's x, B, C rows (zero past the sequence and past N) and dt go through registers: the
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
             const int i = tid + k * kThreads, r = i / (P / EV), c = (i % (P / EV)) * EV;
             rx[k] = make_uint4(0u, 0u, 0u, 0u);
             if (i < kTB * P / EV && t0 + r < seqlen)
-                rx[k] = *reinterpret_cast<const uint4*>(xh + (int64_t)(t0 + r) * nheads * P + c);
+                rx[k] = *reinterpret_cast<const uint4*>(xh + (int64_t)(t0 + r) * nheads * hd + c);
         }
 #pragma unroll
         for (int k = 0; k < NBV; ++k) {
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
                 const int p = 16 * pt + 4 * grp;
                 if (lok) {
                     const T* xr = xs + l * XP + p;
-                    store4(y + ((b * seqlen + t0 + l) * nheads + h) * (int64_t)P + p,
+                    store4(y + ((b * seqlen + t0 + l) * nheads + h) * (int64_t)hd + p0 + p,
                            acc[0] + dsk * to_f32(xr[0]), acc[1] + dsk * to_f32(xr[1]),
                            acc[2] + dsk * to_f32(xr[2]), acc[3] + dsk * to_f32(xr[3]));
                 }
@@ -236,7 +241,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
         if (nt < NT && n < N) {
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt)
-                *reinterpret_cast<f32x4*>(final_states + ((int64_t)bh * P + 16 * pt + r16) * N + n) = sacc[i][pt];
+                *reinterpret_cast<f32x4*>(final_states + ((int64_t)bh * hd + p0 + 16 * pt + r16) * N + n) = sacc[i][pt];
         }
     }
 }
@@ -245,10 +250,11 @@ template <typename T, int P, int NP>
 hipError_t launch(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
                   const float* init, T* y, float* final_states, const Dims& d, hipStream_t s)
 {
-    const int64_t nblocks = d.batch * d.nheads;
+    const int64_t nblocks = d.batch * d.nheads * (d.headdim / P);
     if (nblocks == 0) return hipSuccess;
     hipLaunchKernelGGL((ssd_fused_kernel<T, P, NP>), dim3((unsigned)nblocks), dim3(kThreads), 0, s, x, dt, A, B, C,
-                       D, init, y, final_states, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate);
+                       D, init, y, final_states, (int)d.seqlen, (int)d.nheads, (int)d.ngroups, (int)d.dstate,
+                       (int)d.headdim);
     return hipGetLastError();
 }
 
@@ -258,13 +264,23 @@ int fused_state_width(int64_t dstate) { return dstate <= 32 ? 32 : dstate <= 64 
 
 bool fused_supported(const Dims& d) { return d.headdim * fused_state_width(d.dstate) <= 16384; }
 
+// Head-dimension slice per workgroup: a workgroup per (batch, head) is too little parallelism on
+// 256 CUs, so wide heads are split until there are enough workgroups (each slice recomputes the
+// block's C.B^T, a small share of its work).
+static int fused_slice_width(const Dims& d)
+{
+    int w = (int)d.headdim;
+    while (w > kMinSlice && d.batch * d.nheads * (d.headdim / w) < 1024) w /= 2;
+    return w;
+}
+
 template <typename T>
 hipError_t launch_ssd_fused(const T* x, const float* dt, const float* A, const T* B, const T* C, const float* D,
                             const float* init, T* y, float* final_states, const Dims& d, hipStream_t s)
 {
-    const int np = fused_state_width(d.dstate);
+    const int np = fused_state_width(d.dstate), pw = fused_slice_width(d);
 #define SSD_FUSED_CASE(PP, NN) \
-    if (d.headdim == PP && np == NN) return launch<T, PP, NN>(x, dt, A, B, C, D, init, y, final_states, d, s);
+    if (pw == PP && np == NN) return launch<T, PP, NN>(x, dt, A, B, C, D, init, y, final_states, d, s);
 #define SSD_FUSED_P(PP) SSD_FUSED_CASE(PP, 32) SSD_FUSED_CASE(PP, 64) SSD_FUSED_CASE(PP, 128)
     SSD_FUSED_P(16) SSD_FUSED_P(32) SSD_FUSED_P(64) SSD_FUSED_P(128)
     SSD_FUSED_CASE(16, 256) SSD_FUSED_CASE(32, 256) SSD_FUSED_CASE(64, 256)
