@@ -41,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     const T* __restrict__ Cm, const float* __restrict__ Dv, const float* __restrict__ init, T* __restrict__ y,
     float* __restrict__ final_states, int seqlen, int nheads, int ngroups, int N, int hd)
 {
-    constexpr int XP = P + 8, NPP = NP + 8;          // padded LDS rows (elements)
+    constexpr int XP = tr_pitch<T>(P), NPP = tr_pitch<T>(NP);   // padded LDS rows (elements)
     constexpr int PT = P / 16, NT = NP / 16, KN = NP / 32;
     constexpr int YT = (PT + 1) / 2;                 // head-dimension tiles of y per wavefront
     constexpr int NTW = (NT + 3) / 4;                // state column tiles per wavefront
@@ -194,11 +194,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) acc[q] *= el;
                 Vec8<T> xf;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = (e < 4 ? 0 : 16) + 4 * grp + (e & 3);
-                    xf.set(e, to_f32(xs[s * XP + 16 * pt + r16]));
-                }
+                load_row_slots(xf, xs, XP, 0, 16 * pt);
                 mma(acc, xf, gf);
                 const int p = 16 * pt + 4 * grp;
                 if (lok) {
@@ -210,22 +206,23 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
             }
         }
 
-        // ---- the state: S^T (n x p) <- exp(cs[last]) S^T + (w B)^T X over the block's tokens (slots s = 8 grp + e)
+        // ---- the state: S^T (n x p) <- exp(cs[last]) S^T + (w B)^T X over the block's tokens (slots as for
+        // the X fragments above: tokens 4 grp + m and 16 + 4 grp + m)
+        float wsl[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) wsl[e] = wv[(e < 4 ? 0 : 16) + 4 * grp + (e & 3)];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             Vec8<T> xb;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) xb.set(e, to_f32(xs[(8 * grp + e) * XP + 16 * pt + r16]));
+            load_row_slots(xb, xs, XP, 0, 16 * pt);
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
                 const int nt = wu + 4 * i;
                 if (nt < NT) {
                     Vec8<T> wb;
+                    load_row_slots(wb, bs, NPP, 0, 16 * nt);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int s = 8 * grp + e;
-                        wb.set(e, to_f32(bs[s * NPP + 16 * nt + r16]) * wv[s]);
-                    }
+                    for (int e = 0; e < 8; ++e) wb.set(e, wb.get(e) * wsl[e]);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) sacc[i][pt][q] *= elast;
                     mma(sacc[i][pt], wb, xb);
