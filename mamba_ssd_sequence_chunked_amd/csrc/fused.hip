@@ -50,7 +50,8 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     __shared__ __attribute__((aligned(16))) T bs[kTB * NPP];
     __shared__ __attribute__((aligned(16))) T cs_[kTB * NPP];
     __shared__ __attribute__((aligned(16))) T sp[P * NPP];           // the state rounded to T, rows p
-    __shared__ float cum[kTB], ecs[kTB], wv[kTB], dtv[kTB];
+    // per-block tables, two sets: wavefront 0 fills the next block's while the others use the current
+    __shared__ float cum[2][kTB], ecs[2][kTB], wv[2][kTB], dtv[2][kTB];
 
     // P is the width of the head-dimension slice this workgroup owns (hd / P slices per head): y and
     // the state rows of one slice depend on that slice of x only, so slices are independent and
@@ -134,26 +135,35 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
                 *reinterpret_cast<uint4*>(cs_ + r * NPP + c) = rc[k];
             }
         }
-        if (tid < kTB) dtv[tid] = rdt;
     };
-    if (seqlen > 0) fetch(0);
-    for (int t0 = 0; t0 < seqlen; t0 += kTB) {
-        stash();
-        if (t0 + kTB < seqlen) fetch(t0 + kTB);
-        __syncthreads();
-        // in-block prefix sums of dt A, the readout decays exp(cs) and the state weights
+    // in-block prefix sums of dt A, the readout decays exp(cs) and the state weights of the block whose
+    // dt wavefront 0 holds in registers (lane j: token j), into table set u
+    auto tables = [&](int u) {
         if (wu == 0) {
-            const float v = lane < kTB ? dtv[lane] * a : 0.f;
+            const float v = lane < kTB ? rdt * a : 0.f;
             const float c = wave_inclusive_sum(v);
             const float last = __shfl(c, kTB - 1, kWave);
             if (lane < kTB) {
-                cum[lane] = c;
-                ecs[lane] = __expf(c);
-                wv[lane] = dtv[lane] * __expf(last - c);
+                cum[u][lane] = c;
+                ecs[u][lane] = __expf(c);
+                wv[u][lane] = rdt * __expf(last - c);
+                dtv[u][lane] = rdt;
             }
         }
-        __syncthreads();
-        const float elast = __expf(cum[kTB - 1]);
+    };
+    if (seqlen > 0) {
+        fetch(0);
+        tables(0);
+    }
+    for (int t0 = 0, u = 0; t0 < seqlen; t0 += kTB, u ^= 1) {
+        stash();
+        if (t0 + kTB < seqlen) fetch(t0 + kTB);
+        __syncthreads();                                 // this block's tiles, tables and state copy are in LDS
+        const float* cum_ = cum[u];
+        const float* ecs_ = ecs[u];
+        const float* wv_ = wv[u];
+        const float* dtv_ = dtv[u];
+        const float elast = __expf(cum_[kTB - 1]);
 
         // ---- y of the wavefront's tokens l = 16 lt + r16 (the lane's column) and head-dimension tiles
         const int lt = wu & 1, l = 16 * lt + r16;
@@ -169,15 +179,15 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
                 mma(d0, b0, cf);
                 mma(d1, b1, cf);
             }
-            const float cl = cum[l];
+            const float cl = cum_[l];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int s0 = 4 * grp + q, s1 = 16 + s0;
-                gf.set(q, select(s0 <= l, d0[q] * (__expf(fminf(cl - cum[s0], 0.f)) * dtv[s0]), 0.f));
-                gf.set(4 + q, select(s1 <= l, d1[q] * (__expf(fminf(cl - cum[s1], 0.f)) * dtv[s1]), 0.f));
+                gf.set(q, select(s0 <= l, d0[q] * (__expf(fminf(cl - cum_[s0], 0.f)) * dtv_[s0]), 0.f));
+                gf.set(4 + q, select(s1 <= l, d1[q] * (__expf(fminf(cl - cum_[s1], 0.f)) * dtv_[s1]), 0.f));
             }
         }
-        const float el = ecs[l];
+        const float el = ecs_[l];
         const bool lok = t0 + l < seqlen;
 #pragma unroll
         for (int i = 0; i < YT; ++i) {
@@ -210,7 +220,7 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
         // the X fragments above: tokens 4 grp + m and 16 + 4 grp + m)
         float wsl[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) wsl[e] = wv[(e < 4 ? 0 : 16) + 4 * grp + (e & 3)];
+        for (int e = 0; e < 8; ++e) wsl[e] = wv_[(e < 4 ? 0 : 16) + 4 * grp + (e & 3)];
 #pragma unroll
         for (int pt = 0; pt < PT; ++pt) {
             Vec8<T> xb;
@@ -229,8 +239,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
                 }
             }
         }
+        if (t0 + kTB < seqlen) tables(u ^ 1);           // the other set was last read before this block's barrier
         __syncthreads();                                 // every read of this block's tiles and state is done
-        put_state();                                     // (read after the next block's first barrier)
+        put_state();                                     // (read after the next block's barrier)
     }
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
