@@ -92,34 +92,41 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
     };
     put_state();
 
-    const T* xh = x + (b * seqlen * nheads + h) * (int64_t)hd + p0;
-    const T* bg = Bm + (b * seqlen * ngroups + g) * (int64_t)N;
-    const T* cg = Cm + (b * seqlen * ngroups + g) * (int64_t)N;
-    // The block's x, B, C rows (zero past the sequence and past N) and dt go through registers: the
-    // next block's are loaded while the current one is multiplied.
+    // The block's x, B, C rows and dt go through registers: the next block's are loaded while the
+    // current one is multiplied.  Every access is one unconditional buffer instruction over a resource
+    // that ends at the block's last token (rows past the sequence, state columns past N and idle lanes
+    // read zeros), so the only wait before the rows are used is for these loads.
     constexpr int NXV = (kTB * P / EV + kThreads - 1) / kThreads;      // 16-byte pieces per thread
     constexpr int NBV = (kTB * NP / EV + kThreads - 1) / kThreads;
+    constexpr int ES = (int)sizeof(T);
     uint4 rx[NXV], rb[NBV], rc[NBV];
     float rdt = 0.f;
     auto fetch = [&](int t0) {
+        const int rows = min(kTB, seqlen - t0);
+        const int64_t tok = b * seqlen + t0;
+        const __amdgpu_buffer_rsrc_t rxs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(x + tok * nheads * hd), 0, rows * nheads * hd * ES, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rbs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(Bm + tok * ngroups * N), 0, rows * ngroups * N * ES, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rcs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>(Cm + tok * ngroups * N), 0, rows * ngroups * N * ES, kBufferDword3);
+        const __amdgpu_buffer_rsrc_t rds = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(dt + tok * nheads), 0, rows * nheads * 4, kBufferDword3);
 #pragma unroll
         for (int k = 0; k < NXV; ++k) {
             const int i = tid + k * kThreads, r = i / (P / EV), c = (i % (P / EV)) * EV;
-            rx[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < kTB * P / EV && t0 + r < seqlen)
-                rx[k] = *reinterpret_cast<const uint4*>(xh + (int64_t)(t0 + r) * nheads * hd + c);
+            const int vo = i < kTB * P / EV ? ((r * nheads + h) * hd + p0 + c) * ES : kDropped;
+            rx[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rxs, vo, 0, 0));
         }
 #pragma unroll
         for (int k = 0; k < NBV; ++k) {
             const int i = tid + k * kThreads, r = i / (NP / EV), c = (i % (NP / EV)) * EV;
-            rb[k] = rc[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (i < kTB * NP / EV && t0 + r < seqlen && c < N) {
-                const int64_t o = (int64_t)(t0 + r) * ngroups * N + c;
-                rb[k] = *reinterpret_cast<const uint4*>(bg + o);
-                rc[k] = *reinterpret_cast<const uint4*>(cg + o);
-            }
+            const int vo = i < kTB * NP / EV && c < N ? ((r * ngroups + g) * N + c) * ES : kDropped;
+            rb[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rbs, vo, 0, 0));
+            rc[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rcs, vo, 0, 0));
         }
-        if (tid < kTB) rdt = t0 + tid < seqlen ? dt[(b * seqlen + t0 + tid) * nheads + h] : 0.f;
+        rdt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            rds, tid < kTB ? (tid * nheads + h) * 4 : kDropped, 0, 0));
     };
     auto stash = [&]() {
 #pragma unroll
@@ -188,7 +195,9 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
             }
         }
         const float el = ecs_[l];
-        const bool lok = t0 + l < seqlen;
+        // y rows of this block; rows past the sequence fall outside the resource and are dropped
+        const __amdgpu_buffer_rsrc_t rys = __builtin_amdgcn_make_buffer_rsrc(
+            y + (b * seqlen + t0) * nheads * hd, 0, min(kTB, seqlen - t0) * nheads * hd * ES, kBufferDword3);
 #pragma unroll
         for (int i = 0; i < YT; ++i) {
             const int pt = (wu >> 1) + 2 * i;
@@ -207,12 +216,10 @@ __global__ __launch_bounds__(kThreads) void ssd_fused_kernel(
                 load_row_slots(xf, xs, XP, 0, 16 * pt);
                 mma(acc, xf, gf);
                 const int p = 16 * pt + 4 * grp;
-                if (lok) {
-                    const T* xr = xs + l * XP + p;
-                    store4(y + ((b * seqlen + t0 + l) * nheads + h) * (int64_t)hd + p0 + p,
-                           acc[0] + dsk * to_f32(xr[0]), acc[1] + dsk * to_f32(xr[1]),
-                           acc[2] + dsk * to_f32(xr[2]), acc[3] + dsk * to_f32(xr[3]));
-                }
+                const T* xr = xs + l * XP + p;
+                const f32x4 o = f32x4{acc[0] + dsk * to_f32(xr[0]), acc[1] + dsk * to_f32(xr[1]),
+                                      acc[2] + dsk * to_f32(xr[2]), acc[3] + dsk * to_f32(xr[3])};
+                buffer_store4(rys, ((l * nheads + h) * hd + p0 + p) * ES, 0, o, T());
             }
         }
 
