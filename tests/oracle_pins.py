@@ -573,5 +573,44 @@ def pin_backward_structure(lib=None):
         assert _rel(gr[k], g1[k] + g2[k]) < TOL, f"linearity {k}"
 
 
-BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_structure]
+def pin_backward_dA_scale(lib=None):
+    """W3: dA_scale, rebuilt from the dense quadratic form instead of the adjoint recurrence.
+
+    The scale is sum over (b, t) of T_t (sum_p |dy_t[p] yhat_t[p]| + sum_p |u_t[p] du_t[p]|),
+    with T_t = sum_{j <= t} dt_j, yhat = y - D x (the mixer part of y, from ``dense_mixer``),
+    u_t = dt_t x_t and du_t = g_t B_t.  The adjoint state g_t = dL/dh_t is written out as the
+    transpose of the matrix mixer: g_t[p, :] = sum_{t' >= t} (prod_{j=t+1..t'} a_j) dy_t'[p] C_t'
+    + (prod_{j=t+1..L-1} a_j) dfinal[p, :], so du_t[p] = sum_t' dec[t', t] (C_t' . B_t) dy_t'[p]
+    + dec[L-1, t] (dfinal[p, :] . B_t), the decay products again formed as explicit products."""
+    rng = np.random.default_rng(43)
+    for G, use_dfin in ((1, True), (2, False)):
+        x, dt, A, Bm, Cm, D, h0 = rand_problem(43 + G, b=2, L=11, H=4, P=3, N=4, G=G, init=True)
+        dy = rng.standard_normal(x.shape)
+        dfin = rng.standard_normal(h0.shape) if use_dfin else None
+        gr = oracle.backward(x, dt, A, Bm, Cm, D, h0, dy, dfin, lib=lib)
+        y, _ = dense_mixer(x, dt, A, Bm, Cm, D, h0)
+        b, L, H, P = x.shape
+        hpg = H // G
+        ref = np.zeros(H)
+        for bi in range(b):
+            for h in range(H):
+                g = h // hpg
+                a = np.exp(dt[bi, :, h] * A[h])
+                dec = np.zeros((L, L))
+                for t in range(L):
+                    for i in range(t + 1):
+                        dec[t, i] = np.prod(a[i + 1:t + 1])
+                CB = Cm[bi, :, g, :] @ Bm[bi, :, g, :].T           # CB[t', t] = C_t' . B_t
+                du = np.tril(CB * dec).T @ dy[bi, :, h, :]          # du[t, p]
+                if dfin is not None:
+                    du += dec[L - 1, :, None] * (Bm[bi, :, g, :] @ dfin[bi, h].T)
+                yhat = y[bi, :, h, :] - D[h] * x[bi, :, h, :]
+                u = dt[bi, :, h, None] * x[bi, :, h, :]
+                T = np.cumsum(dt[bi, :, h])
+                mag = np.sum(np.abs(dy[bi, :, h, :] * yhat), axis=1) + np.sum(np.abs(u * du), axis=1)
+                ref[h] += np.sum(T * mag)
+        assert _rel(gr["dA_scale"], ref) < 1e-12, f"dA_scale: {_rel(gr['dA_scale'], ref)}"
+
+
+BACKWARD_PINS = [pin_backward_finite_differences, pin_backward_structure, pin_backward_dA_scale]
 ALL_PINS = ALL_PINS + BACKWARD_PINS

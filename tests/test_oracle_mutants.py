@@ -59,6 +59,11 @@ BACKWARD_MUTANTS = {
     "bwd_dA_missing_dt": [("dA_acc += dtv * a * da;", "dA_acc += a * da;")],
     "bwd_dinit_not_decayed": [("for (int64_t i = 0; i < PN; ++i) gs[i] *= a;",
                                "if (t > 0) for (int64_t i = 0; i < PN; ++i) gs[i] *= a;")],
+    # the scale dA's error is measured against
+    "bwd_scale_prefix_exclusive": [("for (int64_t j = 0; j <= t; ++j) T += dt", "for (int64_t j = 0; j < t; ++j) T += dt")],
+    "bwd_scale_previous_state": [("yh += hs[(t + 1) * PN + p * N + n] * Ct[n];", "yh += hs[t * PN + p * N + n] * Ct[n];")],
+    "bwd_scale_missing_du_term": [("mag += fabs(dyt[p] * yh) + fabs(dtv * xt[p] * du[p]);", "mag += fabs(dyt[p] * yh);")],
+    "bwd_scale_missing_dt": [("fabs(dtv * xt[p] * du[p])", "fabs(xt[p] * du[p])")],
 }
 
 PINS = [pin_hand_example, pin_skip_only, pin_zero_input, pin_scalar_closed_forms, pin_groups,
