@@ -149,3 +149,30 @@ def test_linear_attention_case_on_gpu():
         V = dt[0, :, h, None] * X[0, :, h, :]
         ref[0, :, h, :] = np.tril(Cm[0, :, 0, :] @ Bm[0, :, 0, :].T) @ V + inp.D[h] * X[0, :, h, :]
     assert slice_rel_err(to_f64(y), ref, 2) <= 1e-4
+
+
+def test_nan_in_x_reach():
+    """A NaN in x at token t0, head h, column p of the head reaches y[:, h, p] from the first token
+    of t0's 32-token block within its chunk on, not only from t0 on as in the recurrence: the block's
+    masked scores are zero and zero times NaN is NaN on the matrix cores.  Nothing else changes: y
+    before that block, the other columns and the other heads stay bit-identical, y[t0:, h, p] is NaN,
+    and of the final state only row p of head h."""
+    import torch
+    import mamba_ssd_sequence_chunked_amd as ssd
+    inp = make_random(1, 700, 4, 64, 128, 1, 256, "bf16", "shifted", True, seed=307)
+    d = device_inputs(inp)
+    y1, f1 = ssd.forward(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], 256, d["init"])
+    t0, h, p = 256 + 77, 2, 5                 # token 77 of the second chunk: its block is tokens 64..95
+    x2 = d["x"].clone()
+    x2[0, t0, h, p] = float("nan")
+    y2, f2 = ssd.forward(x2, d["dt"], d["A"], d["B"], d["C"], d["D"], 256, d["init"])
+    torch.cuda.synchronize()
+    first = 256 + 64
+    keep = torch.ones_like(y1, dtype=torch.bool)
+    keep[0, first:, h, p] = False
+    assert torch.equal(y1[keep], y2[keep])
+    assert bool(torch.isnan(y2[0, t0:, h, p]).all())
+    fkeep = torch.ones_like(f1, dtype=torch.bool)
+    fkeep[0, h, p] = False
+    assert torch.equal(f1[fkeep], f2[fkeep])
+    assert bool(torch.isnan(f2[0, h, p]).all())

@@ -71,18 +71,13 @@ def test_selective_scan_split_resume():
     assert slice_rel_err(to_f64(f2), to_f64(fin), 1) <= 1e-5
 
 
-def test_selective_scan_full_size_sampled():
+def test_selective_scan_full_size():
     """The 2.7B-width Mamba-1 workload (4 x 4096 tokens, 5120 channels, N = 16, bf16) in the
-    benchmark's launch configuration; channels are independent, so sampled channel ranges are
-    checked against the oracle run on those channels alone."""
+    benchmark's launch configuration, every (batch, channel) row against the oracle."""
     inp = make_scan_inputs("scan2p7b")
     y, fin = _run(inp)
-    for b in (0, 3):
-        for c0 in (0, 2528, 5056):
-            cs = np.s_[c0:c0 + 64]
-            y_ref, fin_ref = oracle.selective_scan(
-                bf16_to_f64(np.ascontiguousarray(inp.x[b:b + 1, :, cs])), inp.delta[b:b + 1, :, cs],
-                inp.A[cs], bf16_to_f64(inp.B[b:b + 1]), bf16_to_f64(inp.C[b:b + 1]), inp.D[cs], None)
-            print(f"scan2p7b b={b} channels {c0}..{c0 + 63}", flush=True)
-            assert slice_rel_err(y[b:b + 1, :, cs], y_ref, 2) <= TOL["bf16"]
-            assert slice_rel_err(fin[b:b + 1, cs], fin_ref, 1) <= TOL["bf16"]
+    print("scan2p7b: GPU done, running the oracle", flush=True)
+    y_ref, fin_ref = oracle.selective_scan(inp.f64("x"), inp.delta, inp.A, inp.f64("B"), inp.f64("C"), inp.D, None)
+    # per (batch, channel): every channel is its own recurrence, so its outputs form the slice
+    assert slice_rel_err(y, y_ref, 2) <= TOL["bf16"]
+    assert slice_rel_err(fin, fin_ref, 1) <= TOL["bf16"]

@@ -81,13 +81,12 @@ def test_varlen_no_tokens():
     assert y.shape == (0, 2, 16) and fin.shape == (2, 2, 16, 16) and torch.all(fin == 0)
 
 
-def test_varlen_full_size_sampled():
+def test_varlen_full_size():
     """The 2.7B-layer shape over 16384 packed tokens of mixed lengths (the benchmark's launch
-    configuration), checked on sampled heads against the oracle run on those heads alone."""
+    configuration), every head of every sequence checked against the oracle run on each sequence."""
     inp = make_varlen_inputs("varlen2p7b")
     y, fin = _run(inp)
-    heads = [0, 41, 79]
-    y_ref, fin_ref = oracle.forward_varlen(inp.f64("x")[:, heads], inp.dt[:, heads], inp.A[heads], inp.f64("B"),
-                                           inp.f64("C"), inp.D[heads], inp.cu_seqlens)
-    print(f"varlen2p7b: {len(inp.cu_seqlens) - 1} sequences, heads {heads}", flush=True)
-    _check(y[:, heads], fin[:, heads], y_ref, fin_ref, inp.cu_seqlens, TOL["bf16"])
+    print(f"varlen2p7b: {len(inp.cu_seqlens) - 1} sequences, GPU done, running the oracle", flush=True)
+    y_ref, fin_ref = oracle.forward_varlen(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D,
+                                           inp.cu_seqlens)
+    _check(y, fin, y_ref, fin_ref, inp.cu_seqlens, TOL["bf16"])
