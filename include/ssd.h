@@ -52,11 +52,19 @@
  *     exception crosses this interface.
  *   - Shape limits: 0 <= batch <= 65535; seqlen >= 0; 1 <= nheads <= 65535
  *     with nheads * headdim <= 2^20; headdim in {16, 32, 64, 128}; dstate a
- *     multiple of 16 in [16, 256]; ngroups >= 1 dividing nheads; chunk_size
+ *     multiple of 16 in [16, 256]; ngroups >= 1 dividing nheads, with
+ *     ngroups * dstate <= 2^20; chunk_size
  *     a multiple of 16 in [16, 256].  seqlen need not be a multiple of
  *     chunk_size: the last chunk is then shorter.
  *   - Outputs must not overlap inputs (the step state is the one in/out
  *     argument); overlap is reported as SSD_ERR_ALIAS.
+ *   - Non-finite inputs: in the recurrence a NaN or Inf in x at token t of
+ *     head h reaches y only from token t on (in that head and head-dimension
+ *     column).  The chunked forwards reach it from the first token of t's
+ *     32-token block within its chunk (the block's masked scores are zero
+ *     and zero times NaN is NaN on the matrix cores), up to 31 tokens
+ *     earlier, still only in that column of that head.  Non-finite dt, B or
+ *     C values reach y from their own token on.
  */
 #ifndef SSD_MI355X_H
 #define SSD_MI355X_H
@@ -145,8 +153,8 @@ int ssd_backward(const void* x, const float* dt, const float* A, const void* B, 
                  size_t workspace_bytes, void* stream);
 
 /* The same forward as one pass over the sequence per (batch, head), the state kept on chip (the
- * chunk-ordered walk of the mohakchugh blog's block-decomposition outline, section "The Tensor Core
- * Connection"): a workgroup per (batch, head, slice of the head dimension) steps through the tokens
+ * chunk-ordered walk of the mohakchugh blog's block-decomposition outline, section "Block
+ * Decomposition: The Hardware-Aware Algorithm"): a workgroup per (batch, head, slice of the head dimension) steps through the tokens
  * in blocks of 32, so no chunk size and no workspace.  Arguments, layouts, results and errors as for ssd_forward (y and
  * final_states to the same tolerance; the sums run in another order), plus SSD_ERR_SHAPE when
  * headdim x (dstate rounded up to 32, 64, 128 or 256) exceeds 16384 (headdim 128 with dstate > 128).

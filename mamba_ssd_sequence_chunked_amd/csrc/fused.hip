@@ -1,6 +1,7 @@
 // fused.hip - the chunked forward as one pass over the sequence per (batch, head).
 //
-// The block-decomposition outline of the mohakchugh blog (section "The Tensor Core Connection")
+// The block-decomposition outline of the mohakchugh blog (section "Block Decomposition: The
+// Hardware-Aware Algorithm")
 // walks the chunks in order: each chunk's output is its quadratic, attention-like part plus the
 // state that enters it read out through C, and the state then moves on to the next chunk
 // (ql.gl, "The Core of SSD").  Here one workgroup per (batch, head, head-dimension slice) does

@@ -89,6 +89,7 @@ def _forward(lib, **kw):
     (dict(nheads=65536), ERR_SHAPE),
     (dict(batch=65536), ERR_SHAPE),
     (dict(nheads=8200, headdim=128), ERR_SHAPE),     # nheads * headdim above 2^20
+    (dict(nheads=8200, ngroups=8200, dstate=256), ERR_SHAPE),   # ngroups * dstate above 2^20
     (dict(dtype=2), ERR_DTYPE),
     (dict(x=None), ERR_NULL),
     (dict(final=None), ERR_NULL),
