@@ -11,6 +11,12 @@ recurrent-mode kernel on the decode workload (batch 256, fp32 state
 host beside it.
 
     python bench.py [--steps K] [--warmup W] [--workload l2p7b|l130m|long64k]
+
+Order of the run: the secondary legs (decode, one-pass forward, packed
+variable-length batch, backward, Mamba-1 scan, the 130M- and 64K-layer
+workloads) run first, then the W untimed warmup steps and the K timed steps
+of the headline, then per-call (warm and MALL-flushed) and per-kernel timings
+of the same forward, then the CPU oracle.
 """
 from __future__ import annotations
 
@@ -51,6 +57,9 @@ def parse_args():
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed variable-length leg")
     ap.add_argument("--no-fused", action="store_true", help="skip the one-pass (fused) forward leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass leg")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip timing the forward on the 130M- and 64K-layer workloads")
+    ap.add_argument("--no-cold", action="store_true", help="skip the MALL-flushed per-call timings")
     ap.add_argument("--backward-calls", type=int, default=20)
     ap.add_argument("--scan-calls", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -125,6 +134,43 @@ def measured_traffic(workload, name):
     return float(m_b.group(1))
 
 
+def counter_summary(workload, name):
+    """Matrix-core counters per launch from the committed rocprofv3 summary
+    (profiles/mfma_counters_<kernel>_<workload>.txt), or None when there is none for this kernel
+    and workload or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"mfma_counters_{name}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    if not m_src or m_src.group(1) != source_digest(name):
+        return None
+    out = {}
+    for key in ("mfma_instructions_per_launch", "mfma_flops_issued_per_launch", "mfma_busy_frac",
+                "valu_instructions_per_launch", "lds_bank_conflict_cycles_per_launch"):
+        m = re.search(rf"^{key}:\s*([0-9.eE+-]+)", text, re.M)
+        if m:
+            out[key] = float(m.group(1))
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def stats_us(ms_list):
+    v = sorted(1e3 * m for m in ms_list)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return dict(mean=round(sum(v) / n, 2), median=round(med, 2), min=round(v[0], 2), calls=n)
+
+
 # ------------------------------------------------------------------------------------------------
 
 def copy_calibration():
@@ -160,7 +206,6 @@ def main():
 
     lib = ssd.load_library()
     dev = torch.device("cuda:0")
-    cfg = CONFIGS[args.workload]
     inp = make_inputs(args.workload)
     b, L, H, P, N, G = inp.dims
     Q = inp.chunk_size
@@ -205,55 +250,19 @@ def main():
                                                  N, G, Q, code, sp),
     }
 
-    # ---- warmup and the timed region (whole ssd_forward calls)
-    for _ in range(args.warmup):
-        forward()
-    torch.cuda.synchronize()
-    print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        forward()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    tokens = b * L
-    value = tokens / (ms_per_step / 1e3)
-    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e3 / args.steps:.1f} us)",
-          file=sys.stderr, flush=True)
+    def time_region(fn, n):
+        """ms per call of n back-to-back calls between two events on the library's stream"""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
-    # ---- per-kernel durations: the same four launches with events between them
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        evs[i][0].record(stream)
-        for k, name in enumerate(KERNELS):
-            rc = stage_calls[name]()
-            if rc:
-                raise ssd.SSDError(name, rc)
-            evs[i][k + 1].record(stream)
-    torch.cuda.synchronize()
-    kern_us = {name: 1e3 * sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
-               for k, name in enumerate(KERNELS)}
-    work = kernel_work(b, L, H, P, N, G, Q, es, init is not None)
-    kernels = {}
-    for name in KERNELS:
-        us = kern_us[name]
-        w = work[name]
-        kernels[name] = dict(us=round(us, 2), alg_bytes=w["bytes"], alg_flops=w["flops"],
-                             gbs=round(w["bytes"] / us / 1e3, 1), hbm_frac=round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
-                             tflops=round(w["flops"] / us / 1e6, 2),
-                             mfma_frac=round(w["flops"] / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
-    dominant = max(KERNELS, key=lambda n: kern_us[n])
-    dk = kernels[dominant]
-    traffic = measured_traffic(args.workload, dominant)
-    roofline = dict(kernel=dominant, bound="hbm", achieved=dk["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
-                    alg_bytes_per_launch=dk["alg_bytes"], us_per_launch=dk["us"])
-    print(f"[bench] per-kernel us: {json.dumps(kern_us)}", file=sys.stderr, flush=True)
+    # ================================================================================================
+    # secondary legs first (their results are reported beside the headline)
 
     # ---- recurrent mode on the decode workload
     decode = None
@@ -271,24 +280,19 @@ def main():
         sB = [(torch.randn((db, dG, dN), generator=g, device=dev) / dN ** 0.5).to(torch.bfloat16) for _ in range(nset)]
         sC = [(torch.randn((db, dG, dN), generator=g, device=dev) / dN ** 0.5).to(torch.bfloat16) for _ in range(nset)]
         yd = torch.empty((db, dH, dP), dtype=torch.bfloat16, device=dev)
+        ctr = [0]
 
-        def one(i):
-            k = i % nset
+        def one():
+            k = ctr[0] % nset
+            ctr[0] += 1
             rc = lib.ssd_step(p(state), p(sx[k]), p(sdt[k]), p(dA), p(sB[k]), p(sC[k]), p(dD), p(yd), db, dH, dP, dN,
                               dG, ssd.SSD_BF16, sp)
             if rc:
                 raise ssd.SSDError("ssd_step", rc)
 
-        for i in range(16):
-            one(i)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(args.decode_steps):
-            one(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.decode_steps
+        for _ in range(16):
+            one()
+        us = 1e3 * time_region(one, args.decode_steps)
         sw = step_work(db, dH, dP, dN, dG, 2)
         gbs = sw["bytes"] / us / 1e3
         decode = dict(workload="decode: batch 256, 80 heads x 64, state 128, bf16 tokens, fp32 state",
@@ -296,6 +300,7 @@ def main():
                       alg_bytes_per_step=sw["bytes"], gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
                       traffic=measured_traffic("decode", "ssd_step"))
         print(f"[bench] ssd_step: {us:.1f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del state, sx, sdt, sB, sC, yd
 
     # ---- the same forward as one pass over the sequence per (batch, head) (ssd_forward_fused)
     fused = None
@@ -311,22 +316,14 @@ def main():
 
         for _ in range(5):
             fused_call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         nf = max(1, min(args.steps, 20))
-        e0.record(stream)
-        for _ in range(nf):
-            fused_call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / nf
+        us = 1e3 * time_region(fused_call, nf)
         # x read and y written once, B and C once per group, dt, the initial and final states
         fbytes = 2 * b * L * H * P * es + 2 * b * L * G * N * es + 4 * b * L * H + 2 * 4 * b * H * P * N
         fused = dict(workload=f"{args.workload}, one workgroup per (batch, head, 32-column slice of the head) "
                               "walking the sequence in 32-token blocks, the state on chip",
                      calls=nf, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
-                     time_over_chunked=round(us / (1e3 * ms_per_step), 2), algorithmic_bytes=fbytes,
-                     achieved_gbs=round(fbytes / (us * 1e3), 1),
+                     algorithmic_bytes=fbytes, achieved_gbs=round(fbytes / (us * 1e3), 1),
                      traffic=measured_traffic(args.workload, "ssd_fused"))
         print(f"[bench] fused forward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del fy, ffin
@@ -351,16 +348,9 @@ def main():
             if rc:
                 raise ssd.SSDError("ssd_forward_varlen", rc)
 
-        for _ in range(20):
+        for _ in range(5):
             varlen_call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            varlen_call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.steps
+        us = 1e3 * time_region(varlen_call, max(1, min(args.steps, 20)))
         lens = np.diff(vi.cu_seqlens)
         varlen = dict(workload=f"varlen2p7b: {vT} packed tokens in {nseq} sequences (lengths {int(lens.min())}-"
                                f"{int(lens.max())}), 80 heads x 64, dstate 128, chunk 256, bf16",
@@ -389,18 +379,11 @@ def main():
 
         for _ in range(3):
             bwd_call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.backward_calls):
-            bwd_call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.backward_calls
+        us = 1e3 * time_region(bwd_call, args.backward_calls)
         bwd = dict(workload=f"{args.workload} backward: dx, ddt, dA, dB, dC, dD, dinit for a random dL/dy",
                    calls=args.backward_calls, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
-                   time_over_forward=round(us / (ms_per_step * 1e3), 2),
-                   note="the decay-gradient path takes fp32-accurate products: bf16 hi + lo pairs on the bf16 matrix cores (see the library header)")
+                   note="the decay-gradient path takes fp32-accurate products: bf16 hi + lo pairs on the bf16 matrix "
+                        "cores (see the library header)")
         print(f"[bench] backward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del dyb, bws, gx, gB, gC
 
@@ -427,24 +410,172 @@ def main():
                 raise ssd.SSDError("ssd_selective_scan", rc)
 
         scan_call()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.scan_calls):
-            scan_call()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = 1e3 * e0.elapsed_time(e1) / args.scan_calls
+        us = 1e3 * time_region(scan_call, args.scan_calls)
         upd = sb * sL * sD * sN / (us / 1e6)
         scan = dict(workload=f"scan2p7b: Mamba-1 selective scan, batch {sb}, seqlen {sL}, {sD} channels, dstate {sN}, "
                              "bf16 x/B/C (inputs drawn on the device, timing only)",
                     calls=args.scan_calls, us_per_call=round(us, 1), tokens_per_s=round(sb * sL / (us / 1e6), 1),
                     bound="alu", updates_per_s=round(upd, 1), peak_updates_per_s=SCAN_UPDATE_PEAK,
-                    frac=round(upd / SCAN_UPDATE_PEAK, 4),
-                    # same batch and tokens as the l2p7b forward (whose state is 8x larger)
-                    time_over_ssd_forward=round(us / (ms_per_step * 1e3), 3) if args.workload == "l2p7b" else None)
+                    frac=round(upd / SCAN_UPDATE_PEAK, 4))
         print(f"[bench] selective scan: {us:.1f} us/call", file=sys.stderr, flush=True)
         del sx, sdl, sBm, sCm, sy
+
+    # ---- the forward on the other layer workloads (inputs drawn on the device: timing only; the
+    # seeded host draws of the same shapes are what the parity tests check)
+    others = None
+    if not args.no_other_workloads:
+        others = {}
+        for wname in ("l130m", "l2p7b", "long64k"):
+            if wname == args.workload:
+                continue
+            c = CONFIGS[wname]
+            g = torch.Generator(device=dev)
+            g.manual_seed(c.seed)
+            ob, oL, oH, oP, oN, oG, oQ = c.batch, c.seqlen, c.nheads, c.headdim, c.dstate, c.ngroups, c.chunk_size
+            ox = torch.randn((ob, oL, oH, oP), generator=g, device=dev).to(torch.bfloat16)
+            z = torch.randn((ob, oL, oH), generator=g, device=dev)
+            if c.dt_kind == "shifted":
+                z = z - 2.0
+            else:
+                z = z + torch.log(torch.expm1(1e-3 + (1e-1 - 1e-3) * torch.rand((ob, oL, oH), generator=g, device=dev)))
+            odt = torch.nn.functional.softplus(z)
+            oA = -torch.exp(torch.rand(oH, generator=g, device=dev) * float(np.log(16.0)))
+            oB = (torch.randn((ob, oL, oG, oN), generator=g, device=dev) / oN ** 0.5).to(torch.bfloat16)
+            oC = (torch.randn((ob, oL, oG, oN), generator=g, device=dev) / oN ** 0.5).to(torch.bfloat16)
+            oD = torch.randn(oH, generator=g, device=dev)
+            oinit = 0.1 * torch.randn((ob, oH, oP, oN), generator=g, device=dev) if c.init else None
+            oy = torch.empty_like(ox)
+            ofin = torch.empty((ob, oH, oP, oN), dtype=torch.float32, device=dev)
+            ows_bytes = ssd.workspace_bytes(ob, oL, oH, oP, oN, oQ, ssd.SSD_BF16)
+            ows = torch.empty(ows_bytes, dtype=torch.uint8, device=dev)
+
+            def other_call():
+                rc = lib.ssd_forward(p(ox), p(odt), p(oA), p(oB), p(oC), p(oD), p(oinit), p(oy), p(ofin), ob, oL, oH,
+                                     oP, oN, oG, oQ, ssd.SSD_BF16, p(ows), ows_bytes, sp)
+                if rc:
+                    raise ssd.SSDError("ssd_forward", rc)
+
+            for _ in range(5):
+                other_call()
+            n_o = max(1, min(args.steps, 20))
+            us = 1e3 * time_region(other_call, n_o)
+            others[wname] = dict(workload=f"{wname}: batch {ob}, seqlen {oL}, {oH} heads x {oP}, dstate {oN}, "
+                                          f"{oG} group(s), chunk {oQ}, bf16 x/B/C", calls=n_o, us_per_call=round(us, 1),
+                                 tokens_per_s=round(ob * oL / (us / 1e6), 1))
+            print(f"[bench] {wname} forward: {us:.1f} us/call", file=sys.stderr, flush=True)
+            del ox, odt, oB, oC, oy, ofin, ows, oinit
+
+    # ================================================================================================
+    # the headline: W warmup steps, then exactly K timed steps (whole ssd_forward calls)
+    for _ in range(args.warmup):
+        forward()
+    torch.cuda.synchronize()
+    print(f"[bench] {args.workload}: warmup {args.warmup} done", file=sys.stderr, flush=True)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        forward()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    tokens = b * L
+    value = tokens / (ms_per_step / 1e3)
+    print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)",
+          file=sys.stderr, flush=True)
+
+    # ---- the same forward call by call: warm, and with L2 and the MALL flushed before every call
+    def per_call(fn, n, flush=None):
+        out = []
+        for _ in range(n):
+            if flush is not None:
+                flush()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            out.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(c) for a, c in out]
+
+    ncall = max(20, args.steps)
+    fwd_warm = stats_us(per_call(forward, ncall))
+    fwd_cold = None
+    flush_buf = None
+    if not args.no_cold:
+        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fill = [0]
+
+        def flush():
+            fill[0] = (fill[0] + 1) & 0xFF
+            flush_buf.fill_(fill[0])
+
+        fwd_cold = stats_us(per_call(forward, ncall, flush))
+    print(f"[bench] forward per call: warm {fwd_warm}, cold {fwd_cold}", file=sys.stderr, flush=True)
+
+    # ---- per-kernel durations: the same four launches with events between them, the queue drained before
+    # each set (so the first interval does not inherit the previous set's tail)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(ncall)]
+    for i in range(ncall):
+        torch.cuda.synchronize()
+        evs[i][0].record(stream)
+        for k, name in enumerate(KERNELS):
+            rc = stage_calls[name]()
+            if rc:
+                raise ssd.SSDError(name, rc)
+            evs[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    kern_ms = {name: [evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(ncall)] for k, name in enumerate(KERNELS)}
+    kern_cold = {}
+    if flush_buf is not None:
+        # each stage alone after a flush (its inputs from HBM, as the first touch in a pipeline would be)
+        for k, name in enumerate(KERNELS):
+            kern_cold[name] = stats_us(per_call(stage_calls[name], ncall, flush))
+    work = kernel_work(b, L, H, P, N, G, Q, es, init is not None)
+    kernels = {}
+    for name in KERNELS:
+        st = stats_us(kern_ms[name])
+        us = st["mean"]
+        w = work[name]
+        kernels[name] = dict(us=round(us, 2), us_median=st["median"], us_min=st["min"], alg_bytes=w["bytes"],
+                             alg_flops=w["flops"], gbs=round(w["bytes"] / us / 1e3, 1),
+                             hbm_frac=round(w["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
+                             tflops=round(w["flops"] / us / 1e6, 2),
+                             mfma_frac=round(w["flops"] / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
+        if name in kern_cold:
+            kernels[name]["cold"] = kern_cold[name]
+            kernels[name]["cold_hbm_frac"] = round(w["bytes"] / kern_cold[name]["median"] / 1e3 / HBM_PEAK_GBS, 4)
+        cnt = counter_summary(args.workload, name)
+        if cnt is not None and "mfma_flops_issued_per_launch" in cnt:
+            issued = cnt["mfma_flops_issued_per_launch"]
+            kernels[name]["mfma_issued"] = dict(
+                flops_per_launch=issued, tflops=round(issued / us / 1e6, 2),
+                frac=round(issued / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+                busy_frac_counter=cnt.get("mfma_busy_frac"),
+                source="rocprofv3 SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 per launch (committed counter summary) over the "
+                       "live event-timed duration; busy_frac_counter = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE "
+                       "per XCD x 1024 SIMDs) in the counter run")
+    dominant = max(KERNELS, key=lambda n: kernels[n]["us"])
+    dk = kernels[dominant]
+    traffic = measured_traffic(args.workload, dominant)
+    roofline = dict(kernel=dominant, bound="hbm", achieved=dk["gbs"], peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(dk["gbs"] / HBM_PEAK_GBS, 4), traffic=traffic,
+                    alg_bytes_per_launch=dk["alg_bytes"], us_per_launch=dk["us"], us_median=dk["us_median"],
+                    us_min=dk["us_min"])
+    if "mfma_issued" in dk:
+        roofline["mfma"] = dict(alg_frac=dk["mfma_frac"], issued_frac=dk["mfma_issued"]["frac"],
+                                busy_frac_counter=dk["mfma_issued"]["busy_frac_counter"])
+    print(f"[bench] per-kernel us: {json.dumps({n: kernels[n]['us'] for n in KERNELS})}", file=sys.stderr, flush=True)
+
+    if fused is not None:
+        fused["time_over_chunked"] = round(fused["us_per_call"] / (1e3 * ms_per_step), 2)
+    if bwd is not None:
+        bwd["time_over_forward"] = round(bwd["us_per_call"] / (ms_per_step * 1e3), 2)
+    if scan is not None and args.workload == "l2p7b":
+        # same batch and tokens as the l2p7b forward (whose state is 8x larger)
+        scan["time_over_ssd_forward"] = round(scan["us_per_call"] / (ms_per_step * 1e3), 3)
 
     # ---- the fp64 CPU oracle on the host, beside it
     cpu = None
@@ -461,7 +592,7 @@ def main():
         el = time.perf_counter() - t0
         # tokens/s of the whole workload = (token-heads per second) / heads
         cpu = dict(value=round(b * L * heads / el / H, 1), unit="tokens/s", cores=oracle.max_threads(),
-                   kind="oracle",
+                   kind="oracle", cpu_model=cpu_model(), threads=oracle.max_threads(), host_cpus=os.cpu_count(),
                    sample=f"{args.workload}: all {b}x{L} tokens, {heads} of {H} heads, fp64 token-by-token "
                           f"recurrence, {el:.2f} s wall")
         print(f"[bench] oracle: {el:.2f} s for {heads} heads", file=sys.stderr, flush=True)
@@ -475,14 +606,18 @@ def main():
                                f"{G} group(s), chunk {Q}, {inp.dtype} x/B/C",
                    "global_batch": b, "seq_len": L, "parallelism": "single GPU"},
         "roofline": roofline,
+        "forward_per_call_us": {"warm": fwd_warm, "cold_mall_flushed": fwd_cold},
         "kernels": kernels,
-        "kernels_note": "the stage entry points timed one by one; inside ssd_forward stage 1 runs in the prologue "
-                        "of the stage-2 kernel, so the forward launches three kernels",
+        "kernels_note": "the stage entry points timed one by one (mean, median, min over the calls); inside "
+                        "ssd_forward stage 1 runs in the prologue of the stage-2 kernel, so the forward launches "
+                        "three kernels; cold = each stage alone after a 512 MB write that flushes L2 and the MALL",
+        "other_workloads": others,
         "ssd_step": decode,
         "backward": bwd,
         "varlen": varlen,
         "fused_forward": fused,
         "selective_scan": scan,
+        "order": "secondary legs, then warmup and the timed steps, then per-call and per-kernel timings",
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
