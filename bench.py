@@ -486,7 +486,7 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall * 1e6 / args.steps:.1f} us/step)",
           file=sys.stderr, flush=True)
 
-    # ---- the same forward call by call: warm, and with L2 and the MALL flushed before every call
+    # ---- the same forward call by call: warm, and with L2 and the MALL evicted before every call
     def per_call(fn, n, flush=None):
         out = []
         for _ in range(n):
@@ -505,21 +505,27 @@ def main():
     fwd_cold = None
     flush_buf = None
     if not args.no_cold:
-        flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        fill = [0]
+        # a 512 MB read (a reduction into one value) between calls: it evicts the call's inputs from L2
+        # and the 256 MB MALL without leaving dirty lines there for the timed call to write back
+        flush_buf = torch.ones(128 << 20, dtype=torch.int32, device=dev)
+        flush_out = torch.empty((), dtype=torch.int64, device=dev)
 
         def flush():
-            fill[0] = (fill[0] + 1) & 0xFF
-            flush_buf.fill_(fill[0])
+            torch.sum(flush_buf, dim=0, dtype=torch.int64, out=flush_out)
 
         fwd_cold = stats_us(per_call(forward, ncall, flush))
     print(f"[bench] forward per call: warm {fwd_warm}, cold {fwd_cold}", file=sys.stderr, flush=True)
 
-    # ---- per-kernel durations: the same four launches with events between them, the queue drained before
-    # each set (so the first interval does not inherit the previous set's tail)
+    # ---- per-kernel durations: the same four launches with events between them, after one untimed set;
+    # the queue is drained before each set and a one-element fill runs just before its first event, so
+    # the first interval neither inherits the previous set's tail nor starts on an idle queue
+    for name in KERNELS:
+        stage_calls[name]()
+    lead = torch.empty(1, dtype=torch.float32, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(KERNELS) + 1)] for _ in range(ncall)]
     for i in range(ncall):
         torch.cuda.synchronize()
+        lead.fill_(float(i))
         evs[i][0].record(stream)
         for k, name in enumerate(KERNELS):
             rc = stage_calls[name]()
@@ -610,7 +616,7 @@ def main():
         "kernels": kernels,
         "kernels_note": "the stage entry points timed one by one (mean, median, min over the calls); inside "
                         "ssd_forward stage 1 runs in the prologue of the stage-2 kernel, so the forward launches "
-                        "three kernels; cold = each stage alone after a 512 MB write that flushes L2 and the MALL",
+                        "three kernels; cold = each stage alone after a 512 MB read that evicts L2 and the MALL",
         "other_workloads": others,
         "ssd_step": decode,
         "backward": bwd,

@@ -87,6 +87,7 @@ struct ScanCfg {
     static constexpr int EPB = 16 / (int)sizeof(T);              // B / C elements per 16-byte chunk
     static constexpr int B_CH = NP * (int)sizeof(T) / 16;         // chunks per B row
     static constexpr int S_CH = SW * (int)sizeof(T) / 16;          // chunks per S_in slab row
+    static constexpr int S_RS = swz_row_shift(S_CH);               // slab rows read 16 at a time
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);      // x of one head, one stage
     static constexpr int b_bytes = kSB * NP * (int)sizeof(T);
     static constexpr int stage_bytes = HB * xh_bytes + b_bytes;
@@ -215,34 +216,80 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         dma16(row + min(4 * lane, Q - 4), ((q & 1) ? lds_addr(dtt) : lds_addr(cst)) + hh * (kMaxQ * 4));
     }
 
-    // ---- then the heads' S_in tiles (first two slabs) and the first stages of the ring
+    // ---- then the heads' S_in tiles (first two slabs) and the first stages of the ring.  With bf16
+    // operands and head dimensions up to 64 the copies' per-lane source offsets are worked out once and
+    // each slab and stage only moves the base (the wider shapes have no registers to spare for them).
+    constexpr bool kPlanned = std::is_same_v<T, bf16> && P <= 64;
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
     // slab buffers: even slabs in the slab area, odd slabs in the last ring slot (free until the stage
     // loop) or, when they do not fit there, after the even ones
     auto sbuf = [&](int sl) -> unsigned char* { return (sl & 1) ? region + S::odd_off : stile; };
-    auto issue_s = [&](int sl) {
-        // tiles 0 .. HB-1 the heads' (hi) slabs, HB .. 2 HB-1 their lo slabs (split mode)
-        tiles_load_async<S::S_CH, P, HB * (S::kSplit ? 2 : 1), kWaves>(lds_addr(region) + ((sl & 1) ? S::odd_off : S::ring_bytes), S::sh_bytes, [&](int t, int r, int ch) -> const void* {
-            const int hh = t % HB;
-            return ent + (t >= HB ? lo_off : 0) + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N +
-                   min(sl * SW + ch * EPC, N - EPC);
+    // slab tiles 0 .. HB-1 the heads' (hi) slabs, HB .. 2 HB-1 their lo slabs (split mode)
+    using SCopies = TileCopies<S::S_CH, P, HB * (S::kSplit ? 2 : 1), kWaves, S::S_RS>;
+    SCopies scp;
+    if constexpr (kPlanned)
+        scp.plan(wu, [&](int t, int r, int ch) -> unsigned {
+            return (unsigned)(((min(t % HB, nh - 1) * P + r) * N + ch * EPC) * (int)sizeof(T));
         });
+    auto issue_s = [&](int sl) {
+        const unsigned dst = lds_addr(region) + ((sl & 1) ? S::odd_off : S::ring_bytes);
+        if (kPlanned && sl * SW + SW <= N) {
+            scp.issue(wu, [&](int t) -> const void* { return ent + (t >= HB ? lo_off : 0) + sl * SW; }, dst, S::sh_bytes);
+        } else {
+            // (and the last slab of a state width that is not a multiple of its width: columns clamped)
+            tiles_load_async<S::S_CH, P, HB * (S::kSplit ? 2 : 1), kWaves, S::S_RS>(dst, S::sh_bytes,
+                [&](int t, int r, int ch) -> const void* {
+                    const int hh = t % HB;
+                    return ent + (t >= HB ? lo_off : 0) + (int64_t)min(hh, nh - 1) * P * N + (int64_t)r * N +
+                           min(sl * SW + ch * EPC, N - EPC);
+                });
+        }
     };
     issue_s(0);
     if (S::NSL > 1) issue_s(1);
+    // stage tiles: x of the HB heads (tile = head), then the group's B
+    using XCopies = TileCopies<S::X_CH, kSB, HB, kWaves>;
+    using BCopies = TileCopies<S::B_CH, kSB, 1, kWaves>;
+    XCopies xcp;
+    BCopies bcp;
+    const unsigned xrow_bytes = (unsigned)(xl.row * (int64_t)sizeof(T));
+    const unsigned brow_bytes = (unsigned)(ngroups * N * (int)sizeof(T));
+    if constexpr (kPlanned) {
+        if constexpr (EPI != 2)
+            xcp.plan(wu, [&](int hh, int r, int ch) -> unsigned {
+                return r * xrow_bytes +
+                       (unsigned)((((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs + ch * EPC) * (int)sizeof(T));
+            });
+        bcp.plan(wu, [&](int, int r, int ch) -> unsigned {
+            return r * brow_bytes + (unsigned)(min(ch * S::EPB, N - S::EPB) * (int)sizeof(T));
+        });
+    }
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
         const unsigned stg = lds_addr(region) + (sb % kStages) * S::stage_bytes;
-        tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
-            const int64_t tau = t0 + min(s0 + r, len - 1);
-            int64_t tok = b * seqlen + tau;
-            if constexpr (EPI == 2) tok = b * xl.rev_L + min((int64_t)seqlen - 1 - tau, xl.rev_L - 1);   // reversed x
-            return x + tok * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs + ch * EPC;
-        });
-        const T* bg = Bm + (int64_t)g * N;
-        tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
-            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * S::EPB, N - S::EPB);
-        });
+        const int rmax = len - 1 - s0;                    // rows past it (past the sequence) read its row
+        if constexpr (EPI == 2 || !kPlanned) {
+            tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int hh, int r, int ch) -> const void* {
+                const int64_t tau = t0 + min(s0 + r, len - 1);
+                int64_t tok = b * seqlen + tau;
+                // reversed x: row tau of the reversed sequence is the caller's token seqlen - 1 - tau
+                if constexpr (EPI == 2) tok = b * xl.rev_L + min((int64_t)seqlen - 1 - tau, xl.rev_L - 1);
+                return x + tok * xl.row + (int64_t)((h0 + min(hh, nh - 1)) / xl.hdiv) * xl.hs + ch * EPC;
+            });
+        } else {
+            const T* xb = x + (b * seqlen + t0 + s0) * xl.row;
+            xcp.issue(wu, [&](int) -> const void* { return xb; }, stg, S::xh_bytes, rmax, xrow_bytes);
+        }
+        if constexpr (kPlanned) {
+            const T* bb = Bm + ((b * seqlen + t0 + s0) * ngroups + g) * (int64_t)N;
+            bcp.issue(wu, [&](int) -> const void* { return bb; }, stg + HB * S::xh_bytes, 0, rmax, brow_bytes);
+        } else {
+            const T* bg = Bm + (int64_t)g * N;
+            tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
+                return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N +
+                       min(ch * S::EPB, N - S::EPB);
+            });
+        }
     };
 #pragma unroll
     for (int sb = 0; sb < kStages - 1; ++sb)
@@ -304,11 +351,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
                 for (int pt = 0; pt < P / 16; ++pt) {
                     Vec8<T> af;
-                    swz_load8<S::S_CH>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
+                    swz_load8<S::S_CH, S::S_RS>(af, stl, 16 * pt + r16, 32 * kk + 8 * grp);
                     mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
                     mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
                     if constexpr (S::kSplit) {
-                        swz_load8<S::S_CH>(af, stl + HB * S::sh_bytes, 16 * pt + r16, 32 * kk + 8 * grp);
+                        swz_load8<S::S_CH, S::S_RS>(af, stl + HB * S::sh_bytes, 16 * pt + r16, 32 * kk + 8 * grp);
                         mma(acc[0][hh][pt], af, cf[0][sl * (SW / 32) + kk]);
                         mma(acc[1][hh][pt], af, cf[1][sl * (SW / 32) + kk]);
                     }
@@ -370,14 +417,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     const float4 va = *reinterpret_cast<const float4*>(vr);
                     const float4 vb = *reinterpret_cast<const float4*>(vr + 16);
                     Vec8<T> gf, gl;                               // gl: the lo parts (split mode)
-                    auto gset = [&](int i, float v) {
-                        if constexpr (S::kSplit) split_set(gf, gl, i, v);
-                        else gf.set(i, v);
-                    };
-                    gset(0, gt[0][0] * (u * va.x)); gset(1, gt[0][1] * (u * va.y));
-                    gset(2, gt[0][2] * (u * va.z)); gset(3, gt[0][3] * (u * va.w));
-                    gset(4, gt[1][0] * (u * vb.x)); gset(5, gt[1][1] * (u * vb.y));
-                    gset(6, gt[1][2] * (u * vb.z)); gset(7, gt[1][3] * (u * vb.w));
+                    const float gv[8] = {gt[0][0] * (u * va.x), gt[0][1] * (u * va.y), gt[0][2] * (u * va.z),
+                                         gt[0][3] * (u * va.w), gt[1][0] * (u * vb.x), gt[1][1] * (u * vb.y),
+                                         gt[1][2] * (u * vb.z), gt[1][3] * (u * vb.w)};
+                    if constexpr (S::kSplit) pack8_split(gf, gl, gv);
+                    else pack8(gf, gv);
                     const unsigned char* xt = stg + hh * S::xh_bytes;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {
@@ -396,6 +440,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                         const float cl = csr[lrow];
                     const int rst = kVarlen ? lst[min(lrow, kMaxQ - 1)] : 0;   // first token of the row's sequence
                     Vec8<T> gf, gl;                               // G[lrow][s], s = s0 + 16 st2 + 4 grp + i
+                    float gv[8];
 #pragma unroll
                     for (int st2 = 0; st2 < 2; ++st2) {
                         const int sb4 = s0 + 16 * st2 + 4 * grp;
@@ -405,11 +450,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const float v = gt[st2][i] * (__expf(cl - cv[i]) * dv[i]);
-                            const float g = select(sb4 + i <= lrow && (!kVarlen || sb4 + i >= rst), v, 0.f);
-                            if constexpr (S::kSplit) split_set(gf, gl, 4 * st2 + i, g);
-                            else gf.set(4 * st2 + i, g);
+                            gv[4 * st2 + i] = select(sb4 + i <= lrow && (!kVarlen || sb4 + i >= rst), v, 0.f);
                         }
                     }
+                    if constexpr (S::kSplit) pack8_split(gf, gl, gv);
+                    else pack8(gf, gv);
                     const unsigned char* xt = stg + hh * S::xh_bytes;
 #pragma unroll
                     for (int pt = 0; pt < P / 16; ++pt) {

@@ -53,6 +53,8 @@ struct StateCfg {
     static constexpr int EPC = 16 / (int)sizeof(T);
     static constexpr int X_CH = P * (int)sizeof(T) / 16;
     static constexpr int B_CH = NP * (int)sizeof(T) / 16;
+    // B rows of 256 bytes read with the transpose read take the doubled swizzle key (common.hpp)
+    static constexpr int B_KM = (sizeof(T) == 2 && B_CH == 16) ? 2 : 1;
     static constexpr int xh_bytes = kSB * P * (int)sizeof(T);
     static constexpr int stage_bytes = HB * xh_bytes + kSB * NP * (int)sizeof(T);
     static constexpr int lds = kStages * stage_bytes + 4 * HB * kMaxQ;
@@ -63,6 +65,11 @@ struct StateCfg {
     static constexpr bool uniform = x_inst % kWaves == 0 && b_inst % kWaves == 0;
     static constexpr int per_wave = uniform ? (x_inst + b_inst) / kWaves : 0;
     static constexpr bool fits = lds <= 160 * 1024 && NT >= 1;
+    // two workgroups per CU need 4 wavefronts per SIMD, so at most 128 VGPRs: asked of the compiler
+    // for the shapes whose LDS allows two workgroups and whose accumulators and fragments fit that
+    // budget without spilling (bf16 or fp32 with head dimension up to 64 and state width up to 128,
+    // single products); the others take what they need
+    static constexpr int kMinWaves = lds <= 80 * 1024 && P <= 64 && NK <= 4 ? 4 : 2;
 };
 
 // Heads per workgroup: as many as keep a wavefront's accumulators within 64
@@ -98,7 +105,7 @@ struct VarlenArgs {
 // split into bf16 hi + lo (hi = bf16(v), lo = bf16(v - hi), together v to 2^-18) and each product is
 // taken twice on the bf16 matrix cores into the fp32 accumulators.
 template <typename T, int P, int NK, int HB, bool kOwnCumsum, bool kVarlen, bool kSplit = false>
-__global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
+__global__ __launch_bounds__(kThreads, (kSplit ? 2 : StateCfg<T, P, NK, HB>::kMinWaves)) void chunk_state_kernel(
     const T* __restrict__ x, const T* __restrict__ Bm, float* __restrict__ dt_chunked,
     float* __restrict__ dA_cs, const float* __restrict__ dt, const float* __restrict__ A,
     float* __restrict__ chunk_states, VarlenArgs va, int seqlen, int nheads, int ngroups, int N, int Q,
@@ -156,17 +163,42 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
     const int n0 = (wave % S::NSPLIT % S::NSN) * NT * 16;          // its first state column
     const int p0 = (wave % S::NSPLIT / S::NSN) * PT * 16;          // and its first row (>= P: no rows)
 
+    // stage copies (rows past the sequence read its last token).  Outside the pair-product mode, whose
+    // registers are all taken, the per-lane source offsets are worked out once and each stage only
+    // moves the base.
+    constexpr bool kPlanned = !kSplit;
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    TileCopies<S::X_CH, kSB, HB, kWaves> xcp;
+    TileCopies<S::B_CH, kSB, 1, kWaves, 0, S::B_KM> bcp;
+    const unsigned xrow_bytes = (unsigned)(nheads * P * (int)sizeof(T));
+    const unsigned brow_bytes = (unsigned)(ngroups * N * (int)sizeof(T));
+    if constexpr (kPlanned) {
+        xcp.plan(wu, [&](int ht, int r, int ch) -> unsigned {
+            return r * xrow_bytes + (unsigned)((min(ht, nh - 1) * P + ch * EPC) * (int)sizeof(T));
+        });
+        bcp.plan(wu, [&](int, int r, int ch) -> unsigned {
+            return r * brow_bytes + (unsigned)(min(ch * EPC, N - EPC) * (int)sizeof(T));
+        });
+    }
     auto issue_stage = [&](int sb) {
         const int s0 = sb * kSB;
         const unsigned stg = lds_addr(ring) + (sb % kStages) * S::stage_bytes;
-        const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
-        tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int ht, int r, int ch) -> const void* {
-            return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(ht, nh - 1) * P + ch * EPC;
-        });
-        const T* bg = Bm + (int64_t)g * N;
-        tile_load_async<S::B_CH, kSB, kWaves>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
-            return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
-        });
+        if constexpr (kPlanned) {
+            const int rmax = len - 1 - s0;
+            const T* xs = x + ((b * seqlen + t0 + s0) * nheads + h0) * (int64_t)P;
+            xcp.issue(wu, [&](int) -> const void* { return xs; }, stg, S::xh_bytes, rmax, xrow_bytes);
+            const T* bs = Bm + ((b * seqlen + t0 + s0) * ngroups + g) * (int64_t)N;
+            bcp.issue(wu, [&](int) -> const void* { return bs; }, stg + HB * S::xh_bytes, 0, rmax, brow_bytes);
+        } else {
+            const T* xs = x + (b * seqlen + t0) * (int64_t)nheads * P + (int64_t)h0 * P;
+            tiles_load_async<S::X_CH, kSB, HB, kWaves>(stg, S::xh_bytes, [&](int ht, int r, int ch) -> const void* {
+                return xs + (int64_t)min(s0 + r, len - 1) * nheads * P + (int64_t)min(ht, nh - 1) * P + ch * EPC;
+            });
+            const T* bg = Bm + (int64_t)g * N;
+            tile_load_async<S::B_CH, kSB, kWaves, 0, S::B_KM>(stg + HB * S::xh_bytes, [&](int r, int ch) -> const void* {
+                return bg + (b * seqlen + t0 + min(s0 + r, len - 1)) * (int64_t)ngroups * N + min(ch * EPC, N - EPC);
+            });
+        }
     };
 #pragma unroll
     for (int sb = 0; sb < kStages - 1; ++sb)
@@ -245,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_state_kernel(
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             Vec8<T> bf, bl;                                   // bl: the lo parts (split mode)
-            swz_row_slots<S::B_CH>(bf, bt, 0, n0 + 16 * nt);
+            swz_row_slots<S::B_CH, S::B_KM>(bf, bt, 0, n0 + 16 * nt);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float v = bf.get(e) * wv[e];

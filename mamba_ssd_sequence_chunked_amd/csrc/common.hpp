@@ -124,6 +124,32 @@ __device__ __forceinline__ void split_set(Vec8<bf16>& hi, Vec8<bf16>& lo, int i,
     lo.v[i] = static_cast<bf16>(v - static_cast<float>(h));
 }
 
+// 8 fp32 values as one operand fragment; bf16 converts them in pairs (v_cvt_pk_bf16_f32, round to
+// nearest even), so selects made on the fp32 values stay in front of the conversion.
+__device__ __forceinline__ void pack8(Vec8<bf16>& f, const float (&v)[8]) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
+    const bf16x2 b = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
+    const bf16x2 c = __builtin_convertvector((f32x2{v[4], v[5]}), bf16x2);
+    const bf16x2 d = __builtin_convertvector((f32x2{v[6], v[7]}), bf16x2);
+    const bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
+    f.v = __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ void pack8(Vec8<float>& f, const float (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = v[i];
+}
+// The pair form of split_set for 8 values: hi = bf16(v), lo = bf16(v - hi).
+__device__ __forceinline__ void pack8_split(Vec8<bf16>& hi, Vec8<bf16>& lo, const float (&v)[8]) {
+    pack8(hi, v);
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = v[i] - static_cast<float>(hi.v[i]);
+    pack8(lo, r);
+}
+
 // LDS pointer for a generic pointer known to point into LDS: the low 32 bits
 // of such a flat address are the LDS address (taken as an integer, so no
 // null-pointer check of a generic -> local cast is generated).
@@ -196,12 +222,22 @@ __device__ __forceinline__ Vec8<float> masked(const Vec8<float>& v, bool ok) {
 // one wavefront instruction writes 64 consecutive chunks (lane i -> chunk
 // slot i of that 1 KB), so each lane loads the global chunk that belongs in
 // its slot.  R * CH must be a multiple of 64.
-template <int CH>
+//
+// RS > 0 takes the XOR key from row / 2^RS instead: for tiles read as 16 rows x one 16-byte chunk
+// per 16-lane group whose rows are shorter than the 256 bytes of one pass over the banks
+// (CH = 16 / 2^RS), so that the rows sharing a pass get different slots.  KM = 2 doubles the key:
+// for 256-byte rows read with the transpose read (8 rows x two adjacent chunks per pass), so that
+// rows r and r ^ 1 do not land on the same pair of slots.
+template <int CH, int RS = 0, int KM = 1>
 struct SwzTile {
     static constexpr int kMask = (CH < 16 ? CH : 16) - 1;
     static constexpr int kRowBytes = CH * 16;
-    __device__ __forceinline__ static int offset(int r, int c) { return r * kRowBytes + ((c ^ (r & kMask)) << 4); }
+    __device__ __forceinline__ static int key(int r) { return ((r >> RS) * KM) & kMask; }
+    __device__ __forceinline__ static int offset(int r, int c) { return r * kRowBytes + ((c ^ key(r)) << 4); }
 };
+
+// Row shift of SwzTile for CH-chunk rows read 16 rows at a time (see above).
+constexpr int swz_row_shift(int ch) { return ch >= 16 ? 0 : ch == 8 ? 1 : ch == 4 ? 2 : ch == 2 ? 3 : 4; }
 
 // LDS address (an integer) of a __shared__ object, taken from its local
 // address-space form so that no generic pointer is materialised.
@@ -226,15 +262,15 @@ __device__ __forceinline__ void dma16(const void* gsrc, unsigned lds_base) {
 // Issue the loads of one tile: src(r, c) returns the global address of logical
 // chunk c of row r (it must always be a valid address).  Returns nothing; the
 // data is in LDS once this wave's vmcnt reaches zero and a barrier has passed.
-template <int CH, int R, int NW = 4, class F>
+template <int CH, int R, int NW = 4, int RS = 0, int KM = 1, class F>
 __device__ __forceinline__ void tile_load_async(unsigned tile, F src) {
-    using TL = SwzTile<CH>;
+    using TL = SwzTile<CH, RS, KM>;
     constexpr int kInst = R * CH / 64;                 // wavefront instructions for the tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int q = wave; q < kInst; q += NW) {
         const int pos = q * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
-        const int c = slot ^ (r & TL::kMask);
+        const int c = slot ^ TL::key(r);
         dma16(src(r, c), tile + q * 1024u);
     }
 }
@@ -243,19 +279,79 @@ __device__ __forceinline__ void tile_load_async(unsigned tile, F src) {
 // copies are dealt round-robin over the NW wavefronts as one sequence, so
 // every wavefront issues (NT * R * CH / 64) / NW of them when that divides.
 // src(t, r, c) returns the global address of logical chunk c of row r of tile t.
-template <int CH, int R, int NT, int NW, class F>
+template <int CH, int R, int NT, int NW, int RS = 0, int KM = 1, class F>
 __device__ __forceinline__ void tiles_load_async(unsigned base, int stride, F src) {
-    using TL = SwzTile<CH>;
+    using TL = SwzTile<CH, RS, KM>;
     constexpr int kPer = R * CH / 64;                  // wavefront instructions per tile
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int q = wave; q < NT * kPer; q += NW) {
         const int t = q / kPer, qq = q % kPer;
         const int pos = qq * 64 + lane;
         const int r = pos / CH, slot = pos % CH;
-        const int c = slot ^ (r & TL::kMask);
+        const int c = slot ^ TL::key(r);
         dma16(src(t, r, c), base + t * stride + qq * 1024u);
     }
 }
+
+// The same 16-byte global->LDS load with a wave-uniform base address and a per-lane 32-bit byte
+// offset (the instruction's scalar-base form): lane i's data, at sbase + voff, goes to LDS address
+// lds_base + 16 i.
+__device__ __forceinline__ void dma16_off(const void* sbase, unsigned voff, unsigned lds_base) {
+    const unsigned a = __builtin_amdgcn_readfirstlane(lds_base);
+    unsigned saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(voff), "s"(sbase), "s"(a)
+                 : "memory");
+}
+
+// One wavefront's share of the copies of NT swizzled tiles of R rows x CH chunks (the copies of
+// all tiles dealt round robin over NW wavefronts as one sequence, as tiles_load_async deals them),
+// with the per-lane source offsets worked out once: plan() stores them, issue() sends the copies
+// from a base that may change between calls (the next block of rows) at the cost of a scalar add.
+// Copy k of the wavefront is q = wave + NW k: tile q / kPer, 1 KB piece q % kPer of the tile.
+template <int CH, int R, int NT, int NW, int RS = 0, int KM = 1>
+struct TileCopies {
+    using TL = SwzTile<CH, RS, KM>;
+    static constexpr int kPer = R * CH / 64;          // wavefront instructions per tile
+    static constexpr int kTotal = NT * kPer;
+    static constexpr int kK = (kTotal + NW - 1) / NW; // copies per wavefront (at most)
+    unsigned off[kK];
+
+    // off_of(t, r, c): byte offset, from the base of tile t, of logical chunk c of row r
+    template <class F>
+    __device__ __forceinline__ void plan(int wave, F off_of) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int k = 0; k < kK; ++k) {
+            const int q = wave + NW * k;
+            const int t = min(q, kTotal - 1) / kPer, qq = q % kPer;
+            const int pos = qq * 64 + lane;
+            const int r = pos / CH, c = (pos % CH) ^ TL::key(r);
+            off[k] = off_of(t, r, c);
+        }
+    }
+    // base_of(t): base address of tile t; lds: LDS address of tile 0, the tiles stride bytes apart.
+    // When rows are row_bytes apart in the source and offsets below row_bytes pick the column, rows
+    // past rmax (0 <= rmax < R - 1) read row rmax instead.  (The row is recovered from the offset by a
+    // division, on that path only, so no register holds it through the caller's loop.)
+    template <class F>
+    __device__ __forceinline__ void issue(int wave, F base_of, unsigned lds, int stride, int rmax = R,
+                                          unsigned row_bytes = 0) const {
+#pragma unroll
+        for (int k = 0; k < kK; ++k) {
+            const int q = wave + NW * k;
+            if (kTotal % NW != 0 && q >= kTotal) break;
+            const int t = q / kPer, qq = q % kPer;
+            unsigned o = off[k];
+            if (rmax < R - 1) {
+                const unsigned r = o / row_bytes;
+                if (r > (unsigned)rmax) o -= (r - (unsigned)rmax) * row_bytes;
+            }
+            dma16_off(base_of(t), o, lds + t * stride + qq * 1024u);
+        }
+    }
+};
 
 // Wait for all of this wavefront's outstanding vector-memory operations.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -270,14 +366,14 @@ __device__ __forceinline__ void wait_vmem_below() {
 
 // Fragment of 8 consecutive elements along a row of a swizzled tile (columns
 // c0 .. c0+7, c0 a multiple of 8 for bf16 / 4 for fp32).
-template <int CH>
+template <int CH, int RS = 0>
 __device__ __forceinline__ void swz_load8(Vec8<bf16>& f, const unsigned char* tile, int r, int c0) {
-    f.v = *reinterpret_cast<const bf16x8*>(tile + SwzTile<CH>::offset(r, c0 >> 3));
+    f.v = *reinterpret_cast<const bf16x8*>(tile + SwzTile<CH, RS>::offset(r, c0 >> 3));
 }
-template <int CH>
+template <int CH, int RS = 0>
 __device__ __forceinline__ void swz_load8(Vec8<float>& f, const unsigned char* tile, int r, int c0) {
-    const float4 a = *reinterpret_cast<const float4*>(tile + SwzTile<CH>::offset(r, c0 >> 2));
-    const float4 b = *reinterpret_cast<const float4*>(tile + SwzTile<CH>::offset(r, (c0 >> 2) + 1));
+    const float4 a = *reinterpret_cast<const float4*>(tile + SwzTile<CH, RS>::offset(r, c0 >> 2));
+    const float4 b = *reinterpret_cast<const float4*>(tile + SwzTile<CH, RS>::offset(r, (c0 >> 2) + 1));
     f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
     f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
@@ -298,29 +394,29 @@ __device__ __forceinline__ float4 swz_load4f(const float* tile_, int r, int c0) 
 // Fragment whose 8 contraction slots run down the rows of a swizzled tile
 // (the slot layout of load_row_slots): lane 16 g + r gets column c0 + r of
 // rows k0 + 4g + m and k0 + 16 + 4g + m, m = 0..3.
-template <int CH>
+template <int CH, int KM = 1>
 __device__ __forceinline__ void swz_row_slots(Vec8<bf16>& f, const unsigned char* tile, int k0, int c0) {
     typedef short v4i16 __attribute__((ext_vector_type(4)));
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int row = k0 + 4 * g + (r >> 2);
     const int col = c0 + 4 * (r & 3);                          // 4 elements = 8 bytes, inside one chunk
-    const unsigned char* p0 = tile + SwzTile<CH>::offset(row, col >> 3) + 2 * (col & 7);
-    const unsigned char* p1 = tile + SwzTile<CH>::offset(row + 16, col >> 3) + 2 * (col & 7);
+    const unsigned char* p0 = tile + SwzTile<CH, 0, KM>::offset(row, col >> 3) + 2 * (col & 7);
+    const unsigned char* p1 = tile + SwzTile<CH, 0, KM>::offset(row + 16, col >> 3) + 2 * (col & 7);
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p0));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(as_lds<v4i16>(p1));
     const v8i16 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
     f.v = __builtin_bit_cast(bf16x8, ab);
 }
-template <int CH>
+template <int CH, int KM = 1>
 __device__ __forceinline__ void swz_row_slots(Vec8<float>& f, const unsigned char* tile, int k0, int c0) {
     const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
     const int col = c0 + r;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
         const int r0 = k0 + 4 * g + m, r1 = r0 + 16;
-        f.v[m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r0, col >> 2) + 4 * (col & 3));
-        f.v[4 + m] = *reinterpret_cast<const float*>(tile + SwzTile<CH>::offset(r1, col >> 2) + 4 * (col & 3));
+        f.v[m] = *reinterpret_cast<const float*>(tile + SwzTile<CH, 0, KM>::offset(r0, col >> 2) + 4 * (col & 3));
+        f.v[4 + m] = *reinterpret_cast<const float*>(tile + SwzTile<CH, 0, KM>::offset(r1, col >> 2) + 4 * (col & 3));
     }
 }
 
