@@ -35,7 +35,8 @@
  *   - All tensor pointers are DEVICE pointers (current HIP device) to dense,
  *     row-major arrays in the layouts given per call.  The caller owns every
  *     buffer, including the workspace; the library allocates nothing, keeps
- *     no mutable global state and is safe to call from several threads.
+ *     no mutable global state and is safe to call from several threads
+ *     (except ssd_forward_noalloc, whose static scratch is shared: see there).
  *   - "T" is the storage type of x, B, C, y and of the chunk-entry states:
  *     dtype SSD_F32 (float) or SSD_BF16 (bfloat16, 2 bytes).  dt, A, D,
  *     initial/final/step states and the fp32 workspace arrays are float.
@@ -85,7 +86,8 @@ typedef enum {
     SSD_ERR_DTYPE = -3,     /* dtype is not SSD_F32 or SSD_BF16 */
     SSD_ERR_WORKSPACE = -4, /* workspace smaller than ssd_forward_workspace_bytes */
     SSD_ERR_HIP = -5,       /* the HIP runtime reported an error at launch */
-    SSD_ERR_ALIAS = -6      /* an output overlaps an input */
+    SSD_ERR_ALIAS = -6,     /* an output overlaps an input */
+    SSD_ERR_SCRATCH = -7    /* ssd_forward_noalloc: one batch row needs more than the static scratch */
 } ssd_status;
 
 /* Human-readable text of a status code (static storage; never NULL). */
@@ -128,6 +130,24 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* ssd_forward for callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same arguments, results and errors, with no
+ * workspace argument.  The workspace is a static scratch array in the library's device code
+ * (ssd_forward_noalloc_scratch_bytes() = 64 MiB), one copy per GPU, held from the library's load
+ * until the process ends; the call allocates nothing.  Batch rows are independent, so the forward
+ * runs on slices of batch rows whose workspace (ssd_forward_workspace_bytes of the slice) fits the
+ * scratch, one slice after another on `stream`; the results equal ssd_forward's bit for bit.
+ * Returns SSD_ERR_SCRATCH, before any device work, when one batch row's workspace exceeds the
+ * scratch (for example 65536 tokens x 80 heads of 64 x 256 states).  Every call on a GPU shares
+ * that GPU's scratch: calls that overlap in time on one GPU (on different streams, or from
+ * different threads without ordering) race and give wrong results.  Nothing in the scratch needs
+ * to start at zero: every byte a call reads was written by the same call. */
+size_t ssd_forward_noalloc_scratch_bytes(void);
+int ssd_forward_noalloc(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                        const float* D, const float* init_states, void* y, float* final_states, int64_t batch,
+                        int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                        int64_t chunk_size, int dtype, void* stream);
 
 /* Gradients of ssd_forward (the training pass) for dL/dy = dy and dL/d(final_states) = dfinal
  * (NULL = 0), by the adjoint of the recurrence: the adjoint state runs backwards in time as an SSD

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssd.h"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -96,6 +98,43 @@ Workspace layout(const Dims& d, int dtype)
     return w;
 }
 
+// ssd_forward's body (argument checks and the launch sequence on a caller workspace).
+int forward_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                 const float* D, const float* init_states, void* y, float* final_states,
+                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+
+}  // namespace
+
+// The static scratch of ssd_forward_noalloc: device memory of the code object, one copy per GPU the
+// library is loaded on, held until the process ends.  In host code its name is a host-side stand-in,
+// not a device address: the address on a device comes from hipGetSymbolAddress with that device
+// current, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SSD_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SSD_OK;
+}
+
 struct VarlenWorkspace {
     size_t cs, dtc, states, entry, tstart, cmeta, total;
 };
@@ -134,11 +173,14 @@ const char* ssd_status_string(int status)
     case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace smaller than ssd_forward_workspace_bytes()";
     case SSD_ERR_HIP: return "SSD_ERR_HIP: the HIP runtime reported an error at launch";
     case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output buffer overlaps an input or another output";
+    case SSD_ERR_SCRATCH:
+        return "SSD_ERR_SCRATCH: one batch row's forward workspace exceeds the library's static scratch "
+               "(ssd_forward_noalloc_scratch_bytes(); use ssd_forward with a caller workspace)";
     default: return "unknown ssd status";
     }
 }
 
-int ssd_abi_version(void) { return 103; }
+int ssd_abi_version(void) { return 104; }
 
 int64_t ssd_num_chunks(int64_t seqlen, int64_t chunk_size)
 {
@@ -259,6 +301,63 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
                 size_t workspace_bytes, void* stream)
 {
+    return forward_impl(x, dt, A, B, C, D, init_states, y, final_states, batch, seqlen, nheads, headdim, dstate,
+                        ngroups, chunk_size, dtype, workspace, workspace_bytes, stream);
+}
+
+size_t ssd_forward_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+int ssd_forward_noalloc(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                        const float* D, const float* init_states, void* y, float* final_states, int64_t batch,
+                        int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                        int64_t chunk_size, int dtype, void* stream)
+{
+    Dims d{batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size};
+    if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
+    int rc = check_seq(d);
+    if (rc != SSD_OK) return rc;
+    if (batch == 0) return SSD_OK;
+    // batch rows are independent: run the forward on slices of rows whose workspace fits the scratch
+    Dims one = d;
+    one.batch = 1;
+    const size_t per_row = layout(one, dtype).total;
+    if (per_row > kScratchBytes) return SSD_ERR_SCRATCH;
+    int64_t nb = std::min<int64_t>(batch, (int64_t)(kScratchBytes / per_row));
+    for (;;) {
+        Dims sl = d;
+        sl.batch = nb;
+        if (layout(sl, dtype).total <= kScratchBytes || nb == 1) break;
+        --nb;
+    }
+    void* ws = nullptr;
+    rc = scratch_on_current_device(&ws);
+    if (rc != SSD_OK) return rc;
+    const size_t es = elem_size(dtype);
+    const int64_t row_x = seqlen * nheads * headdim, row_dt = seqlen * nheads, row_b = seqlen * ngroups * dstate;
+    const int64_t row_s = nheads * headdim * dstate;
+    for (int64_t b0 = 0; b0 < batch; b0 += nb) {
+        const int64_t n = std::min(nb, batch - b0);
+        auto off = [&](const void* p, int64_t elems) -> const void* {
+            return p ? static_cast<const unsigned char*>(p) + b0 * elems : nullptr;
+        };
+        rc = forward_impl(off(x, row_x * es), (const float*)off(dt, row_dt * 4), A, off(B, row_b * es),
+                          off(C, row_b * es), D, (const float*)off(init_states, row_s * 4),
+                          const_cast<void*>(off(y, row_x * es)), (float*)off(final_states, row_s * 4), n, seqlen,
+                          nheads, headdim, dstate, ngroups, chunk_size, dtype, ws, kScratchBytes, stream);
+        if (rc != SSD_OK) return rc;
+    }
+    return SSD_OK;
+}
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                 const float* D, const float* init_states, void* y, float* final_states,
+                 int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate,
+                 int64_t ngroups, int64_t chunk_size, int dtype, void* workspace,
+                 size_t workspace_bytes, void* stream)
+{
     Dims d{batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size};
     if (!valid_dtype(dtype)) return SSD_ERR_DTYPE;
     int rc = check_seq(d);
@@ -313,6 +412,10 @@ int ssd_forward(const void* x, const float* dt, const float* A, const void* B, c
     }
     return hip_status(e);
 }
+
+}  // namespace
+
+extern "C" {
 
 int ssd_forward_fused(const void* x, const float* dt, const float* A, const void* B, const void* C, const float* D,
                       const float* init_states, void* y, float* final_states, int64_t batch, int64_t seqlen,

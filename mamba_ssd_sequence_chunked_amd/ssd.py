@@ -51,6 +51,10 @@ def load_library():
     lib.ssd_forward_workspace_bytes.argtypes = [i64] * 6 + [i32]
     lib.ssd_forward.restype = i32
     lib.ssd_forward.argtypes = [vp] * 9 + [i64] * 7 + [i32, vp, sz, vp]
+    lib.ssd_forward_noalloc.restype = i32
+    lib.ssd_forward_noalloc.argtypes = [vp] * 9 + [i64] * 7 + [i32, vp]
+    lib.ssd_forward_noalloc_scratch_bytes.restype = sz
+    lib.ssd_forward_noalloc_scratch_bytes.argtypes = []
     lib.ssd_forward_fused.restype = i32
     lib.ssd_forward_fused.argtypes = [vp] * 9 + [i64] * 6 + [i32, vp]
     lib.ssd_dA_cumsum.restype = i32
@@ -164,6 +168,36 @@ def forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                          workspace.numel(), _stream(dev))
     _check("ssd_forward", rc)
     return y, final
+
+
+def forward_noalloc(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+                    D: torch.Tensor, chunk_size: int, init_states: Optional[torch.Tensor] = None,
+                    y: Optional[torch.Tensor] = None,
+                    final_states: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """ssd_forward on the library's static scratch (no workspace; see ssd_forward_noalloc in
+    include/ssd.h).  y and final_states may be passed in, so that the call allocates nothing."""
+    lib = load_library()
+    b, L, H, P, N, G = _forward_dims(x, B)
+    dev = x.device
+    code = _dtype_code(x)
+    _need(x, "x", (b, L, H, P), x.dtype, dev)
+    _need(dt, "dt", (b, L, H), torch.float32, dev)
+    _need(A, "A", (H,), torch.float32, dev)
+    _need(B, "B", (b, L, G, N), x.dtype, dev)
+    _need(C, "C", (b, L, G, N), x.dtype, dev)
+    _need(D, "D", (H,), torch.float32, dev)
+    if init_states is not None:
+        _need(init_states, "init_states", (b, H, P, N), torch.float32, dev)
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", (b, L, H, P), x.dtype, dev)
+    if final_states is None:
+        final_states = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    _need(final_states, "final_states", (b, H, P, N), torch.float32, dev)
+    rc = lib.ssd_forward_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init_states), _ptr(y),
+                                 _ptr(final_states), b, L, H, P, N, G, chunk_size, code, _stream(dev))
+    _check("ssd_forward_noalloc", rc)
+    return y, final_states
 
 
 def forward_fused(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -41,10 +41,10 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS):
+    for code in (OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_WS, ERR_HIP, ERR_ALIAS, -7):
         assert ssd.status_string(code).startswith("SSD_")
     assert "unknown" in ssd.status_string(123)
-    assert ssd.load_library().ssd_abi_version() == 103
+    assert ssd.load_library().ssd_abi_version() == 104
 
 
 def test_num_chunks_and_workspace():
@@ -151,6 +151,23 @@ def test_forward_varlen_rejects():
     up = lambda v: (v + 255) // 256 * 256    # noqa: E731
     assert ws == 2 * up(4 * nc * 64 * 4) + up(nc * 4 * 16 * 16 * 4) * 2 + up(300 * 4) + up(nc * 16)
     assert lib.ssd_forward_varlen_workspace_bytes(300, 4, 48, 16, 64, 0) == 0
+
+
+def test_noalloc_rejects():
+    """ssd_forward_noalloc validates on the host, and refuses before any device work a problem whose single
+    batch row needs more workspace than the static scratch (fake device pointers are never touched)."""
+    lib = ssd.load_library()
+    assert lib.ssd_forward_noalloc_scratch_bytes() == 64 << 20
+    args = [fake(i) for i in range(1, 10)]
+
+    def call(b=2, L=100, H=4, P=64, N=128, G=1, Q=64, dtype=1):
+        return lib.ssd_forward_noalloc(*args, b, L, H, P, N, G, Q, dtype, None)
+
+    assert call(L=65536, H=80, N=256, G=8, Q=256) == -7          # one row: 2.2 GB of workspace
+    assert ssd.status_string(-7).startswith("SSD_ERR_SCRATCH")
+    assert call(P=48) == ERR_SHAPE
+    assert call(dtype=9) == ERR_DTYPE
+    assert call(b=0) == OK                                       # nothing to do, nothing enqueued
 
 
 def test_fused_rejects():
