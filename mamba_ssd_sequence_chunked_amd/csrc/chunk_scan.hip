@@ -221,9 +221,15 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     // each slab and stage only moves the base (the wider shapes have no registers to spare for them).
     constexpr bool kPlanned = std::is_same_v<T, bf16> && P <= 64;
     const T* ent = entry + (((int64_t)b * nc + c) * nheads + h0) * (int64_t)P * N;
-    // slab buffers: even slabs in the slab area, odd slabs in the last ring slot (free until the stage
-    // loop) or, when they do not fit there, after the even ones
-    auto sbuf = [&](int sl) -> unsigned char* { return (sl & 1) ? region + S::odd_off : stile; };
+    // slab buffers: when every slab of the heads' S_in fits the region (the ring is free until the stage
+    // loop), all of them side by side from the region's start, loaded at once; else even slabs in the
+    // slab area and odd slabs in the last ring slot or, when they do not fit there, after the even ones
+    constexpr int kSlabSet = HB * (S::kSplit ? 2 : 1) * S::sh_bytes;     // one slab of every head (and plane)
+    constexpr bool kAllSlabs = S::NSL > 1 && S::NSL * kSlabSet <= S::region;
+    auto slab_off = [&](int sl) -> int {
+        return kAllSlabs ? sl * kSlabSet : ((sl & 1) ? S::odd_off : S::ring_bytes);
+    };
+    auto sbuf = [&](int sl) -> unsigned char* { return region + slab_off(sl); };
     // slab tiles 0 .. HB-1 the heads' (hi) slabs, HB .. 2 HB-1 their lo slabs (split mode)
     using SCopies = TileCopies<S::S_CH, P, HB * (S::kSplit ? 2 : 1), kWaves, S::S_RS>;
     SCopies scp;
@@ -232,7 +238,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             return (unsigned)(((min(t % HB, nh - 1) * P + r) * N + ch * EPC) * (int)sizeof(T));
         });
     auto issue_s = [&](int sl) {
-        const unsigned dst = lds_addr(region) + ((sl & 1) ? S::odd_off : S::ring_bytes);
+        const unsigned dst = lds_addr(region) + slab_off(sl);
         if (kPlanned && sl * SW + SW <= N) {
             scp.issue(wu, [&](int t) -> const void* { return ent + (t >= HB ? lo_off : 0) + sl * SW; }, dst, S::sh_bytes);
         } else {
@@ -245,8 +251,13 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                 });
         }
     };
-    issue_s(0);
-    if (S::NSL > 1) issue_s(1);
+    if constexpr (kAllSlabs) {
+#pragma unroll
+        for (int sl = 0; sl < S::NSL; ++sl) issue_s(sl);
+    } else {
+        issue_s(0);
+        if (S::NSL > 1) issue_s(1);
+    }
     // stage tiles: x of the HB heads (tile = head), then the group's B
     using XCopies = TileCopies<S::X_CH, kSB, HB, kWaves>;
     using BCopies = TileCopies<S::B_CH, kSB, 1, kWaves>;
@@ -291,9 +302,11 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
             });
         }
     };
+    if constexpr (!kAllSlabs) {
 #pragma unroll
-    for (int sb = 0; sb < kStages - 1; ++sb)
-        if (sb < nsb) issue_stage(sb);
+        for (int sb = 0; sb < kStages - 1; ++sb)
+            if (sb < nsb) issue_stage(sb);
+    }
 
     float dsk[HB];                                                  // skip weights D of the heads
 #pragma unroll
@@ -302,9 +315,10 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         for (int l = tid; l < kMaxQ; l += kThreads) lst[l] = tstart[t0 + min(l, len - 1)] - (int)t0;
     }
     // the tables have landed once only the copies issued after them may still fly
-    constexpr int kAfter = (1 + (S::NSL > 1)) * (S::s_inst / kWaves) + (kStages - 1) * S::per_wave;
+    constexpr int kAfter = kAllSlabs ? S::NSL * (S::s_inst / kWaves)
+                                     : (1 + (S::NSL > 1)) * (S::s_inst / kWaves) + (kStages - 1) * S::per_wave;
     if constexpr (!kVarlen && S::uniform && S::s_inst % kWaves == 0 && kAfter < 64) {
-        if (nsb >= kStages - 1) wait_vmem_below<kAfter>();
+        if (kAllSlabs || nsb >= kStages - 1) wait_vmem_below<kAfter>();
         else wait_vmem();
     } else {
         wait_vmem();
@@ -332,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
     // ---- inter-chunk term: exp(cs[l]) * S_in[p, :] . C_l (slab by slab when S_in does not fit whole)
 #pragma unroll
     for (int sl = 0; sl < S::NSL; ++sl) {
-        if (sl > 0) {
+        if (!kAllSlabs && sl > 0) {
             __syncthreads();                       // slab sl-1 consumed: its buffer takes slab sl+1
             if (sl + 1 < S::NSL) {
                 issue_s(sl + 1);
@@ -378,17 +392,30 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         }
     }
 
-    if (S::NSL > 1) __syncthreads();               // the last ring slot held odd slabs
+    if (S::NSL > 1) __syncthreads();               // the ring held slabs
+    // stages issued before the loop: with all slabs loaded at once the first kStages go now
+    int issued = kAllSlabs ? 0 : min(nsb, kStages - 1);
+    if constexpr (kAllSlabs) {
+#pragma unroll
+        for (int sb = 0; sb < kStages; ++sb)
+            if (sb < nsb) issue_stage(sb);
+        issued = min(nsb, kStages);
+    }
     // ---- intra-chunk term, one 32-token stage at a time
     for (int sb = 0; sb < nsb; ++sb) {
         const int s0 = sb * kSB;
-        if (sb > 0) {
-            // stage sb landed; the kStages - 2 stages issued after it may still fly
-            if (S::uniform && kStages > 2 && sb + kStages - 2 < nsb) wait_vmem_below<(kStages - 2) * S::per_wave>();
+        if (kAllSlabs || sb > 0) {
+            // stage sb landed; the stages issued after it (up to kStages - 1) may still fly
+            const int after = min(issued, nsb) - 1 - sb;
+            if (S::uniform && after == kStages - 1) wait_vmem_below<(kStages - 1) * S::per_wave>();
+            else if (S::uniform && kStages > 2 && after == kStages - 2) wait_vmem_below<(kStages - 2) * S::per_wave>();
             else wait_vmem();
             __syncthreads();
         }
-        if (sb + kStages - 1 < nsb) issue_stage(sb + kStages - 1);
+        if (sb + kStages - 1 < nsb && sb + kStages - 1 >= issued) {
+            issue_stage(sb + kStages - 1);
+            issued = sb + kStages;
+        }
         const unsigned char* stg = ring + (sb % kStages) * S::stage_bytes;
         const unsigned char* bt = stg + HB * S::xh_bytes;
 #pragma unroll
@@ -443,6 +470,12 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
                     float gv[8];
 #pragma unroll
                     for (int st2 = 0; st2 < 2; ++st2) {
+                        if (st2 == 1 && lb == s0) {
+                            // a block at the stage's start: the stage's second 16 tokens all follow its rows
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) gv[4 + i] = 0.f;
+                            continue;
+                        }
                         const int sb4 = s0 + 16 * st2 + 4 * grp;
                         const float4 c4 = *reinterpret_cast<const float4*>(csr + sb4);
                         const float4 d4 = *reinterpret_cast<const float4*>(dtr + sb4);
