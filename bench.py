@@ -92,6 +92,61 @@ def kernel_work(b, L, H, P, N, G, Q, es, init):
     return work
 
 
+def backward_work(b, L, H, P, N, G, Q, es):
+    """Algorithmic bytes and flops of ssd_backward (bf16 inputs), whole pass and per dominant kernel.
+
+    Whole pass: the minimum bytes are one read of x, dt, B, C, dy and one write of dx, ddt, dB, dC; the
+    flops are the forward recomputed (y - D x), the adjoint readout du = g B (an SSD of the same shape),
+    the scores dy . x^T inside chunks and their products with B and C, and the state terms of dB and dC
+    (2 P N per token and head each).  Per kernel: the two pair-product readout passes, which read the
+    hi and lo planes of the entry (resp. adjoint) states and each take every product twice."""
+    nc = -(-L // Q)
+    causal = Q * (Q + 1) // 2
+    st = b * nc * H * P * N
+    tab = b * H * nc * Q * 4
+    fw = kernel_work(b, L, H, P, N, G, Q, es, False)
+    fwd_flops = sum(v["flops"] for v in fw.values())
+    total = dict(bytes=3 * b * L * H * P * es + 2 * b * L * H * 4 + 4 * b * L * G * N * es,
+                 flops=2 * fwd_flops + 2 * b * nc * H * causal * P + 2 * 2 * b * nc * G * causal * N
+                 + 2 * 2 * b * L * H * P * N)
+    # the readout's matrix-core work taken twice (hi and lo operands): causal C.B^T once per group, G x,
+    # and the state readout C . S
+    split_flops = 2 * (2 * b * nc * G * causal * N + 2 * b * nc * H * causal * P + 2 * b * L * H * N * P)
+    kernels = {
+        # x, B, C, the decay tables, the entry states' hi and lo planes, dy; dy . yhat per (token, head) out
+        "chunk_scan_split_dot": dict(bytes=2 * b * L * H * P * es + 2 * b * L * G * N * es + 2 * tab + 2 * st * es
+                                     + b * H * L * 4, flops=split_flops),
+        # dy (the input role, read again per token where it is then cached), reversed C and B, tables, the
+        # adjoint states' planes; x and dt per token; dx, x . du and x . dy out
+        "chunk_scan_split_grad": dict(bytes=3 * b * L * H * P * es + 2 * b * L * G * N * es + 2 * tab + 2 * st * es
+                                      + b * L * H * 4 + 2 * b * H * L * 4, flops=split_flops),
+    }
+    return total, kernels
+
+
+def trace_average_us(path_name, kernel_label):
+    """Average duration of a kernel in a committed rocprofv3 trace summary (profiles/<path_name>), or
+    None when the summary is missing, does not list the kernel, or its source digest no longer
+    matches the backward's sources."""
+    path = os.path.join(ROOT, "profiles", path_name)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_src = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    if not m_src or m_src.group(1) != backward_digest():
+        return None
+    m = re.search(rf"^\| {re.escape(kernel_label)} \(`[^`]*`\) \| \d+ \| ([0-9.]+) \|", text, re.M)
+    return float(m.group(1)) if m else None
+
+
+def backward_digest():
+    h = hashlib.sha256()
+    for f in ("bwd.hip", "bwd_dbc.hip", "chunk_scan.hip", "chunk_state.hip", "state_passing.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "mamba_ssd_sequence_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(_code_only(fh.read()))
+    return h.hexdigest()[:16]
+
+
 # Vector-ALU ceiling of the selective scan: each (token, channel, state) update needs four fp32
 # VALU operations (delta*A, u*B, the state FMA, the readout FMA) and one exponential.  A SIMD
 # retires 16 lanes of a plain VALU op per cycle and a transcendental at a quarter of that, so an
@@ -380,10 +435,24 @@ def main():
         for _ in range(3):
             bwd_call()
         us = 1e3 * time_region(bwd_call, args.backward_calls)
+        bw_total, bw_kernels = backward_work(b, L, H, P, N, G, Q, es)
         bwd = dict(workload=f"{args.workload} backward: dx, ddt, dA, dB, dC, dD, dinit for a random dL/dy",
                    calls=args.backward_calls, us_per_call=round(us, 1), tokens_per_s=round(b * L / (us / 1e6), 1),
+                   alg_bytes_min=bw_total["bytes"], alg_flops=bw_total["flops"],
+                   hbm_frac_min_bytes=round(bw_total["bytes"] / us / 1e3 / HBM_PEAK_GBS, 4),
+                   mfma_frac_alg=round(bw_total["flops"] / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
                    note="the decay-gradient path takes fp32-accurate products: bf16 hi + lo pairs on the bf16 matrix "
                         "cores (see the library header)")
+        if inp.dtype == "bf16":
+            # the dominant kernels inside the pass, timed by the committed rocprofv3 trace of the same build
+            dk = {}
+            for kname, w in bw_kernels.items():
+                kus = trace_average_us(f"kernel_trace_backward_{args.workload}.md", kname)
+                dk[kname] = dict(alg_bytes=w["bytes"], issued_flops=w["flops"], us_trace=kus,
+                                 hbm_frac=None if kus is None else round(w["bytes"] / kus / 1e3 / HBM_PEAK_GBS, 4),
+                                 mfma_frac_issued=None if kus is None else
+                                 round(w["flops"] / kus / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4))
+            bwd["kernels"] = dk
         print(f"[bench] backward: {us:.1f} us/call", file=sys.stderr, flush=True)
         del dyb, bws, gx, gB, gC
 
