@@ -613,7 +613,9 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
         // y through LDS (the ring is free now): one row block at a time, each wavefront stages its 16
         // rows of all the workgroup's heads as bf16, then stores whole token rows -- the heads of a
         // token are adjacent in y, so a row is HB * P * 2 contiguous bytes -- in 16-byte pieces
-        constexpr int kRowW = HB * P / 2 + 8;                   // 4-byte words per staged row (padded)
+        // 4-byte words per staged row, padded to 4 mod 32 so that the rows of a 16-byte write start 4 banks
+        // apart and a write of 8 lanes (8 rows) covers every bank once
+        constexpr int kRowW = HB * P / 2 + 4;
         constexpr int CPR = HB * P * 2 / 16;                    // 16-byte pieces per row
         constexpr int kIter = (16 * CPR + 63) / 64;
         static_assert(kWaves * 16 * kRowW * 4 <= S::region, "y staging");
@@ -625,15 +627,25 @@ __global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
-            for (int hh = 0; hh < HB; ++hh)
+            for (int hh = 0; hh < HB; ++hh) {
+                if constexpr (P >= 32) {
+                    // a lane holds 4 columns of each 16-column tile; swapping the upper 16-lane row of a pair
+                    // with the lower row of the next tile's values leaves 8 adjacent columns per lane, so one
+                    // 16-byte write replaces two 8-byte ones: lanes of the even rows (grp 0, 2) then hold
+                    // columns 32 pp + 8 (grp / 2) .. + 7, lanes of the odd rows the same 16 columns further
 #pragma unroll
-                for (int pt = 0; pt < P / 16; ++pt) {
-                    const f32x4 v = acc[j][hh][pt];
-                    bf16x4 q;
-                    q[0] = static_cast<bf16>(v[0]); q[1] = static_cast<bf16>(v[1]);
-                    q[2] = static_cast<bf16>(v[2]); q[3] = static_cast<bf16>(v[3]);
-                    *reinterpret_cast<bf16x4*>(ys + r16 * kRowW + hh * (P / 2) + 8 * pt + 2 * grp) = q;
+                    for (int pp = 0; pp < P / 32; ++pp) {
+                        const uint2 a = pack4_bf16(acc[j][hh][2 * pp]), c = pack4_bf16(acc[j][hh][2 * pp + 1]);
+                        const auto sx = __builtin_amdgcn_permlane16_swap(a.x, c.x, false, false);
+                        const auto sy = __builtin_amdgcn_permlane16_swap(a.y, c.y, false, false);
+                        const int col = 32 * pp + 16 * (grp & 1) + 8 * (grp >> 1);
+                        *reinterpret_cast<uint4*>(ys + r16 * kRowW + hh * (P / 2) + col / 2) =
+                            make_uint4(sx[0], sy[0], sx[1], sy[1]);
+                    }
+                } else {
+                    *reinterpret_cast<uint2*>(ys + r16 * kRowW + hh * (P / 2) + 2 * grp) = pack4_bf16(acc[j][hh][0]);
                 }
+            }
             __syncthreads();
 #pragma unroll
             for (int it = 0; it < kIter; ++it) {

@@ -137,6 +137,14 @@ __device__ __forceinline__ void pack8(Vec8<bf16>& f, const float (&v)[8]) {
     const bf16x4 cd = __builtin_shufflevector(c, d, 0, 1, 2, 3);
     f.v = __builtin_shufflevector(ab, cd, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// A 16x16 accumulator fragment's 4 values as bf16 (round to nearest even), in two 4-byte words.
+__device__ __forceinline__ uint2 pack4_bf16(const f32x4& v) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 a = __builtin_convertvector((f32x2{v[0], v[1]}), bf16x2);
+    const bf16x2 b = __builtin_convertvector((f32x2{v[2], v[3]}), bf16x2);
+    return make_uint2(__builtin_bit_cast(unsigned, a), __builtin_bit_cast(unsigned, b));
+}
 __device__ __forceinline__ void pack8(Vec8<float>& f, const float (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) f.v[i] = v[i];
