@@ -40,7 +40,14 @@ KERNEL_SOURCES = {"dA_cumsum": "dA_cumsum.hip", "chunk_state": "chunk_state.hip"
                   "state_passing": "state_passing.hip", "state_passing_varlen": "state_passing.hip",
                   "chunk_scan": "chunk_scan.hip", "chunk_scan_varlen": "chunk_scan.hip", "ssd_step": "ssd_step.hip",
                   "selective_scan": "selective_scan.hip", "varlen_meta": "varlen_meta.hip",
-                  "ssd_fused": "fused.hip"}
+                  "ssd_fused": "fused.hip",
+                  # the backward's kernels: the pair-product (hi/lo) variants of the forward's and its own
+                  "chunk_scan_split_dot": "chunk_scan.hip", "chunk_scan_split_grad": "chunk_scan.hip",
+                  "chunk_scan_f32out": "chunk_scan.hip", "chunk_state_split": "chunk_state.hip",
+                  "chunk_state_cumsum_split": "chunk_state.hip", "state_passing_split": "state_passing.hip",
+                  **{k: "bwd.hip" for k in ("bwd_group_sum", "bwd_heads", "bwd_passing", "bwd_prep", "bwd_rows",
+                                            "bwd_scan", "bwd_tables", "bwd_transpose", "bwd_zero")},
+                  **{k: "bwd_dbc.hip" for k in ("bwd_dbc", "bwd_inter", "bwd_score")}}
 
 
 def parse_args():
