@@ -24,7 +24,10 @@
 //                        group's arrays) -- and summed over the heads of each group afterwards
 //   per token            with q_t = dy_t . yhat_t - u_t . du_t the gradient of the log-decay dt_t A
 //                        is the suffix sum of q from t plus <dfinal, h_final> (the telescoping of
-//                        <g_t, h_t> over t), so ddt = A dl + x . du, dA = sum dt dl, dD = sum x . dy
+//                        <g_t, h_t> over t); it is taken within t's chunk only, plus the same
+//                        gradient at the token after the chunk, <Gout, h> at the chunk boundary
+//                        (formed by the adjoint passing), so ddt = A dl + x . du, dA = sum dt dl,
+//                        dD = sum x . dy
 //
 // The reversal pads the sequence in front to whole chunks (zero tokens, unit decay), so the
 // reversed chunks line up with the forward's.
@@ -207,25 +210,54 @@ __global__ __launch_bounds__(kT) void bwd_transpose_kernel(const E* __restrict__
     }
 }
 
+// Sum over the 64 lanes of a wavefront, in fp64; every lane gets the sum.
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
 // backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
 // order (P x N: fp32, or for TD = bf16 as bf16 hi / lo planes, the lo plane lo_off elements after
-// the hi one); dinit at the end
+// the hi one); dinit at the end.  With it, for every chunk but the last, the log-decay gradient at
+// the first token after the chunk, <Gout[c], h at the chunk's last token> (that state is the entry
+// state of chunk c + 1; same planes as Gout), as fp64 partial sums, one per wavefront:
+// Rp[((b H + h) nc + c) nparts + part], nparts = 4 gridDim.x
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
-                                                         const float* __restrict__ dfinal, void* __restrict__ Gout_rev,
-                                                         float* __restrict__ dinit, int64_t lo_off, int H, int P,
-                                                         int N, int Q, int nc)
+                                                         const float* __restrict__ dfinal, const TD* __restrict__ entry,
+                                                         void* __restrict__ Gout_rev, float* __restrict__ dinit,
+                                                         double* __restrict__ Rp, int64_t lo_off, int H, int P, int N,
+                                                         int Q, int nc)
 {
     const int PN = P * N;
     const int h = blockIdx.y;
     const int64_t b = blockIdx.z;
     const int e = blockIdx.x * (4 * kT) + 4 * threadIdx.x;
-    if (e >= PN) return;
+    const bool on = e < PN;                         // whole wavefronts are on or off (PN % 256 == 0)
     const int64_t bh = b * H + h;
-    float4 s = dfinal ? *reinterpret_cast<const float4*>(dfinal + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const int nparts = (int)gridDim.x * (kT / 64);
+    const int part = (int)blockIdx.x * (kT / 64) + (int)threadIdx.x / 64;
+    float4 s = on && dfinal ? *reinterpret_cast<const float4*>(dfinal + bh * PN + e) : make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = nc - 1; c >= 0; --c) {
         const int cr = nc - 1 - c;
         const int64_t go = ((b * nc + cr) * H + h) * (int64_t)PN + e;
+        if (c < nc - 1) {
+            double r = 0.0;
+            if (on) {
+                const int64_t eo = ((b * nc + c + 1) * H + h) * (int64_t)PN + e;
+                float4 hv = load4f(entry + eo);
+                if constexpr (std::is_same_v<TD, bf16>) {
+                    const float4 lo = load4f(entry + lo_off + eo);
+                    hv.x += lo.x; hv.y += lo.y; hv.z += lo.z; hv.w += lo.w;
+                }
+                r = (double)s.x * hv.x + (double)s.y * hv.y + (double)s.z * hv.z + (double)s.w * hv.w;
+            }
+            r = wave_sum_f64(r);
+            if ((threadIdx.x & 63) == 0) Rp[(bh * nc + c) * nparts + part] = r;
+        }
+        if (!on) continue;
         if constexpr (std::is_same_v<TD, bf16>) {
             auto rem = [](float v) { return v - static_cast<float>(static_cast<bf16>(v)); };
             bf16* gh = static_cast<bf16*>(Gout_rev) + go;
@@ -241,7 +273,7 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
         s.z = fmaf(dec, s.z, gh.z);
         s.w = fmaf(dec, s.w, gh.w);
     }
-    *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
+    if (on) *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
 }
 
 // per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
@@ -291,21 +323,29 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, 
 }
 
 // per (b, h): with q_t = dy_t . yhat_t - dt_t x_t . du_t (the three scalars stored (batch, head, token),
-// dt read from the chunked copy (batch, head, padded token)),
-// the log-decay gradient dl_t = sum_{t' >= t} q_t' + <dfinal, h_final>, ddt = A dl + x.du,
-// and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.  Thread i takes the 16 tokens
-// ending at L - 16 i (a suffix block), so the suffix sum is a prefix sum over threads.  The sums
-// run in fp64: dA adds up terms that cancel to a few parts in a thousand of their magnitude.
+// dt read from the chunked copy (batch, head, padded token)), the log-decay gradient of a token t in
+// chunk k is dl_t = sum_{t <= t' <= e_k} q_t' + R_k, e_k the chunk's last token and R_k the gradient at
+// the token after it (from the states, Rp; for the last chunk <dfinal, h_final>), then
+// ddt = A dl + x.du, and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.
+// Equal in exact arithmetic to the suffix sum of q over the whole sequence plus <dfinal, h_final>, but
+// each q carries the rounding of the fp32 products it is formed from, and a suffix sum over the whole
+// sequence adds those errors up over every later chunk; restarting at each chunk boundary keeps
+// them to one chunk's worth.  The sums run in fp64: thread i takes the 16 tokens ending at
+// top - 16 i (top = L rounded up to 16, so each thread's tokens lie in one chunk), the suffix sum S
+// over the whole sequence is a prefix sum over threads, and dl_t = S_t - S_{e_k + 1} + R_k.
 __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dtc, const float* __restrict__ A,
                                                       const float* __restrict__ yd, const float* __restrict__ xdu,
                                                       const float* __restrict__ xdy,
                                                       const float* __restrict__ dfinal,
-                                                      const float* __restrict__ hfinal, float* __restrict__ ddt,
-                                                      double* __restrict__ dAp, double* __restrict__ dDp, int64_t L,
-                                                      int64_t Lp, int H, int P, int N)
+                                                      const float* __restrict__ hfinal, const double* __restrict__ Rp,
+                                                      int nparts, float* __restrict__ ddt, double* __restrict__ dAp,
+                                                      double* __restrict__ dDp, int64_t L, int64_t Lp, int H, int P,
+                                                      int N, int Q, int nc)
 {
     constexpr int kPer = 16;
     __shared__ double sc[kT];
+    __shared__ double ex[kT];           // S + <dfinal, h_final> after each thread's tokens
+    __shared__ double corr[kT + 1];     // per chunk met by the span: R_k - (S_{e_k + 1} + <dfinal, h_final>)
     const int h = blockIdx.x % H;
     const int64_t b = blockIdx.x / H;
     const int64_t bh = b * H + h;
@@ -333,10 +373,12 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
         for (int64_t i = tid; i < PN; i += kT) fh += (double)dfinal[bh * PN + i] * hfinal[bh * PN + i];
     }
     double carry = block_sum(fh);
+    double bcarry = 0.0;                // S_{e_k + 1} + fh of a chunk that reaches above the span
     const double a = A[h];
     double dA_acc = 0.0, dD_acc = 0.0;
     const int64_t span = (int64_t)kT * kPer;
-    for (int64_t hi = L; hi > 0; hi -= span) {
+    const int64_t top = (L + kPer - 1) / kPer * kPer;
+    for (int64_t hi = top; hi > 0; hi -= span) {
         // this thread's tokens: [hi - kPer (tid + 1), hi - kPer tid), latest first
         const int64_t t1 = hi - (int64_t)kPer * tid;
         float qs[kPer], xs[kPer];
@@ -357,16 +399,38 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
         }
         const double incl = block_scan(own);
         const double total = sc[kT - 1];
-        double run = carry + incl - own;                    // everything after this thread's tokens
+        const double excl = carry + incl - own;             // everything after this thread's tokens
+        ex[tid] = excl;
+        __syncthreads();
+        // the chunks this span meets, k0 .. k1 (at most kT + 1 of them: chunks hold >= 16 tokens)
+        const int64_t lo = hi - span > 0 ? hi - span : 0;
+        const int64_t k0 = lo / Q, k1 = (hi - 1) / Q;
+        for (int64_t k = k0 + tid; k <= k1; k += kT) {
+            double cr = 0.0;
+            if (k < nc - 1) {
+                const int64_t end = (k + 1) * Q;             // first token after chunk k
+                const double sk = end <= hi ? ex[(hi - end) / kPer] : bcarry;
+                double r = 0.0;
+                const double* rp = Rp + (bh * nc + k) * nparts;
+                for (int j = 0; j < nparts; ++j) r += rp[j];
+                cr = r - sk;
+            }
+            corr[k - k0] = cr;
+        }
+        __syncthreads();
+        double run = excl;
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
             run += qs[k];
             if (t >= 0 && t < L) {
-                ddt[(b * L + t) * H + h] = (float)(a * run + xs[k]);
-                dA_acc += (double)dtc[bh * Lp + t] * run;
+                const double dl = run + corr[t / Q - k0];
+                ddt[(b * L + t) * H + h] = (float)(a * dl + xs[k]);
+                dA_acc += (double)dtc[bh * Lp + t] * dl;
             }
         }
+        // a chunk reaching across the span's lower edge has its end in this span
+        if (lo > 0 && lo % Q != 0) bcarry = ex[(hi - (lo / Q + 1) * Q) / kPer];
         carry += total;
     }
     const double sa = block_sum(dA_acc);
@@ -475,6 +539,7 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.xdy = take(B * d.seqlen * H * 4);
     w.dAp = take(B * H * 8);
     w.dDp = take(B * H * 8);
+    w.Rp = take(B * H * nc * ((P * N + 1023) / 1024 * 4) * 8);   // per (b, h, chunk): one fp64 sum per wavefront
     w.total = std::max<size_t>(o, 256);
     return w;
 }
@@ -526,9 +591,11 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     SSD_TRY(hipGetLastError());
     if constexpr (kBf16) SSD_TRY(launch_chunk_state_split(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
     else SSD_TRY(launch_chunk_state<float>(dy, Cm, F(w.W), F(w.Z), F(w.states), d, s));
-    hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3((unsigned)((P * N + 4 * kT - 1) / (4 * kT)), (unsigned)H,
-                       (unsigned)B), dim3(kT), 0, s, F(w.states), F(w.cs), dfinal, (void*)(ws + w.Gout_rev),
-                       dinit, st, H, P, N, Q, nc);
+    const unsigned npass = (unsigned)((P * N + 4 * kT - 1) / (4 * kT));
+    const int nparts = (int)npass * (kT / 64);
+    hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3(npass, (unsigned)H, (unsigned)B), dim3(kT), 0, s, F(w.states),
+                       F(w.cs), dfinal, TT(w.entry), (void*)(ws + w.Gout_rev), dinit,
+                       reinterpret_cast<double*>(ws + w.Rp), st, H, P, N, Q, nc);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
     // (bf16 inputs: the du pass reads dy itself in reversed order; the reversed dy and u copies serve the
@@ -586,8 +653,9 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
             SSD_TRY(hipGetLastError());
         }
         hipLaunchKernelGGL(bwd_scan_kernel, dim3((unsigned)(B * H)), dim3(kT), 0, s, F(w.dtc), A, F(w.yd), F(w.xdu),
-                           F(w.xdy), dfinal, F(w.hfinal), ddt, reinterpret_cast<double*>(ws + w.dAp),
-                           reinterpret_cast<double*>(ws + w.dDp), L, Lp, H, P, N);
+                           F(w.xdy), dfinal, F(w.hfinal), reinterpret_cast<const double*>(ws + w.Rp), nparts, ddt,
+                           reinterpret_cast<double*>(ws + w.dAp), reinterpret_cast<double*>(ws + w.dDp), L, Lp, H, P,
+                           N, Q, nc);
         SSD_TRY(hipGetLastError());
     }
     if (!dbc) {

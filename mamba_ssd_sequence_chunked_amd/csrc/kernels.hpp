@@ -133,7 +133,7 @@ hipError_t launch_selective_scan(const T* x, const float* delta, const float* A,
 // the backward pass (bwd.hip): workspace parts (byte offsets) and the launcher
 struct BwdLayout {
     size_t cs, dtc, W, Z, dtp, csp, states, entry, SinT, Gout_rev, GoutT_rev, hfinal, yhat, dy_rev, B_rev,
-        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, Mp, dCi, dBi, zeros, yd, xdu, xdy, dAp, dDp, total;
+        C_rev, dy_revD, u_revD, du_rev, dBh_rev, dCh, Mp, dCi, dBi, zeros, yd, xdu, xdy, dAp, dDp, Rp, total;
 };
 // dB and dC summed over the heads inside the kernels (bwd_dbc.hip): bf16 inputs, headdim % 32 == 0,
 // chunk % 64 == 0; Mp holds bwd_dbc_slices() partial sums of the (B, nc, G, Q, Q) score matrices,

@@ -26,6 +26,10 @@ CASES = [
     (1, 130, 4, 32, 16, 2, 64, "bf16", True, False),
     # and one the per-head passes take (chunk not a multiple of 64, head size 16)
     (1, 100, 4, 16, 32, 1, 32, "bf16", False, True),
+    # longer than one 4096-token pass of the suffix-sum kernel, with a chunk (192 tokens) that
+    # straddles the pass boundary: the per-chunk restart carried across passes
+    (1, 4500, 2, 16, 32, 1, 192, "f32", True, True),
+    (1, 4500, 2, 32, 32, 1, 192, "bf16", False, True),
 ]
 
 
@@ -63,6 +67,24 @@ def test_backward_matches_oracle(c):
     assert slice_rel_err(g["dinit"], r["dinit"], 1) <= tol, "dinit"
     # dA (one value per head) at the stated bar, normwise over the heads; its error relative to the
     # size of the per-token products it is summed from is printed beside it
+    print(f"dA: normwise {_rel_all(g['dA'], r['dA']):.3e}, "
+          f"of its terms' size {np.max(np.abs(g['dA'] - r['dA']) / r['dA_scale']):.3e}")
+    assert _rel_all(g["dA"], r["dA"]) <= tol, "dA"
+    assert _rel_all(g["dD"], r["dD"]) <= tol, "dD"
+
+
+def test_backward_tiny_workload():
+    """The small workload (1 x 512 tokens, 4 heads, P = N = 16, chunk 64, fp32): its dA is ~25 000 times
+    smaller than the per-token products it is formed from, the hardest case here for dA's bar."""
+    inp = make_inputs("tiny")
+    dy = np.random.default_rng(11).standard_normal(inp.x.shape).astype(np.float32)
+    g = _grads(inp, dy, None)
+    r = oracle.backward(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D, None, dy.astype(np.float64))
+    tol = TOL["f32"]
+    assert slice_rel_err(g["dx"], r["dx"], 2) <= tol, "dx"
+    assert slice_rel_err(g["ddt"][..., None], r["ddt"][..., None], 2) <= tol, "ddt"
+    assert slice_rel_err(g["dB"], r["dB"], 2) <= tol, "dB"
+    assert slice_rel_err(g["dC"], r["dC"], 2) <= tol, "dC"
     print(f"dA: normwise {_rel_all(g['dA'], r['dA']):.3e}, "
           f"of its terms' size {np.max(np.abs(g['dA'] - r['dA']) / r['dA_scale']):.3e}")
     assert _rel_all(g["dA"], r["dA"]) <= tol, "dA"
