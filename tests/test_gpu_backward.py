@@ -60,6 +60,8 @@ def test_backward_matches_oracle(c):
     g = _grads(inp, dy, dfinal)
     r = oracle.backward(inp.f64("x"), inp.dt, inp.A, inp.f64("B"), inp.f64("C"), inp.D, inp.f64("init"), dyf, dfinal)
     tol = TOL[dt]
+    print("errors: " + ", ".join(f"{k} {slice_rel_err(g[k] if k != 'ddt' else g[k][..., None], r[k] if k != 'ddt' else r[k][..., None], 1 if k == 'dinit' else 2):.2e}"
+                                 for k in ("dx", "ddt", "dB", "dC", "dinit")))
     assert slice_rel_err(g["dx"], r["dx"], 2) <= tol, "dx"
     assert slice_rel_err(g["ddt"][..., None], r["ddt"][..., None], 2) <= tol, "ddt"
     assert slice_rel_err(g["dB"], r["dB"], 2) <= tol, "dB"
