@@ -24,10 +24,11 @@
 //                        group's arrays) -- and summed over the heads of each group afterwards
 //   per token            with q_t = dy_t . yhat_t - u_t . du_t the gradient of the log-decay dt_t A
 //                        is the suffix sum of q from t plus <dfinal, h_final> (the telescoping of
-//                        <g_t, h_t> over t); it is taken within t's chunk only, plus the same
-//                        gradient at the token after the chunk, <Gout, h> at the chunk boundary
-//                        (formed by the adjoint passing), so ddt = A dl + x . du, dA = sum dt dl,
-//                        dD = sum x . dy
+//                        <g_t, h_t> over t); it is taken within t's chunk only, from both ends: the
+//                        gradient at the chunk's first token and at the token after it are inner
+//                        products of adjoint and forward states at the boundaries (formed by the
+//                        adjoint passing), and the mean of the two exact forms is used; then
+//                        ddt = A dl + x . du, dA = sum dt dl, dD = sum x . dy
 //
 // The reversal pads the sequence in front to whole chunks (zero tokens, unit decay), so the
 // reversed chunks line up with the forward's.
@@ -220,15 +221,16 @@ __device__ __forceinline__ double wave_sum_f64(double v)
 
 // backwards over chunks: Gout[c] = state entering from later tokens, written in reversed chunk
 // order (P x N: fp32, or for TD = bf16 as bf16 hi / lo planes, the lo plane lo_off elements after
-// the hi one); dinit at the end.  With it, for every chunk but the last, the log-decay gradient at
-// the first token after the chunk, <Gout[c], h at the chunk's last token> (that state is the entry
-// state of chunk c + 1; same planes as Gout), as fp64 partial sums, one per wavefront:
-// Rp[((b H + h) nc + c) nparts + part], nparts = 4 gridDim.x
+// the hi one); dinit at the end.  With them, the log-decay gradient at the first token of chunks
+// 1 .. nc-1, <Gout[c-1], entry state of chunk c> (same planes as Gout), and at token 0,
+// <dinit, init> (0 without an initial state), as fp64 partial sums, one per wavefront:
+// Bp[((b H + h) (nc + 1) + c) nparts + part], nparts = 4 gridDim.x (slot nc is not written)
 template <typename TD>
 __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict__ Ghat, const float* __restrict__ cs,
                                                          const float* __restrict__ dfinal, const TD* __restrict__ entry,
+                                                         const float* __restrict__ init,
                                                          void* __restrict__ Gout_rev, float* __restrict__ dinit,
-                                                         double* __restrict__ Rp, int64_t lo_off, int H, int P, int N,
+                                                         double* __restrict__ Bp, int64_t lo_off, int H, int P, int N,
                                                          int Q, int nc)
 {
     const int PN = P * N;
@@ -255,7 +257,7 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
                 r = (double)s.x * hv.x + (double)s.y * hv.y + (double)s.z * hv.z + (double)s.w * hv.w;
             }
             r = wave_sum_f64(r);
-            if ((threadIdx.x & 63) == 0) Rp[(bh * nc + c) * nparts + part] = r;
+            if ((threadIdx.x & 63) == 0) Bp[(bh * (nc + 1) + c + 1) * nparts + part] = r;
         }
         if (!on) continue;
         if constexpr (std::is_same_v<TD, bf16>) {
@@ -273,7 +275,16 @@ __global__ __launch_bounds__(kT) void bwd_passing_kernel(const float* __restrict
         s.z = fmaf(dec, s.z, gh.z);
         s.w = fmaf(dec, s.w, gh.w);
     }
-    if (on) *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
+    double r0 = 0.0;
+    if (on) {
+        *reinterpret_cast<float4*>(dinit + bh * PN + e) = s;
+        if (init) {
+            const float4 iv = *reinterpret_cast<const float4*>(init + bh * PN + e);
+            r0 = (double)s.x * iv.x + (double)s.y * iv.y + (double)s.z * iv.z + (double)s.w * iv.w;
+        }
+    }
+    r0 = wave_sum_f64(r0);
+    if ((threadIdx.x & 63) == 0) Bp[bh * (nc + 1) * nparts + part] = r0;
 }
 
 // per (b, t, h) row, all rows in parallel: dx = dt du + D dy, and the scalars the decay
@@ -323,21 +334,23 @@ __global__ __launch_bounds__(kT) void bwd_rows_kernel(const TD* __restrict__ x, 
 }
 
 // per (b, h): with q_t = dy_t . yhat_t - dt_t x_t . du_t (the three scalars stored (batch, head, token),
-// dt read from the chunked copy (batch, head, padded token)), the log-decay gradient of a token t in
-// chunk k is dl_t = sum_{t <= t' <= e_k} q_t' + R_k, e_k the chunk's last token and R_k the gradient at
-// the token after it (from the states, Rp; for the last chunk <dfinal, h_final>), then
-// ddt = A dl + x.du, and the per-(b, h) parts of dA = sum dt dl and dD = sum x.dy.
-// Equal in exact arithmetic to the suffix sum of q over the whole sequence plus <dfinal, h_final>, but
-// each q carries the rounding of the fp32 products it is formed from, and a suffix sum over the whole
-// sequence adds those errors up over every later chunk; restarting at each chunk boundary keeps
-// them to one chunk's worth.  The sums run in fp64: thread i takes the 16 tokens ending at
-// top - 16 i (top = L rounded up to 16, so each thread's tokens lie in one chunk), the suffix sum S
-// over the whole sequence is a prefix sum over threads, and dl_t = S_t - S_{e_k + 1} + R_k.
+// dt read from the chunked copy (batch, head, padded token)), the log-decay gradient dl of a token t in
+// chunk k, from either end of its chunk:
+//   dl_t = Bnd[k + 1] + sum_{t <= t' < (k + 1) Q} q_t'     (Bnd[nc] = <dfinal, h_final>)
+//   dl_t = Bnd[k]     - sum_{k Q <= t' < t} q_t'
+// Bnd[j] the gradient at token j Q, from the states (Bp).  Both forms are exact; each q carries the
+// rounding of the fp32 products it is formed from, and their mean halves the largest weight with which
+// one q's error enters dA (and keeps it within the chunk: a suffix sum over the whole sequence
+// gathered every later chunk's errors).  Then ddt = A dl + x.du, and the per-(b, h) parts of
+// dA = sum dt dl and dD = sum x.dy.  The sums run in fp64: thread i takes the 16 tokens ending at
+// hi - 16 i, a pass covers whole chunks (hi and hi - span are chunk boundaries, so each thread's tokens
+// lie in one chunk), and the suffix sum S over the whole sequence is a prefix sum over threads, from
+// which the two forms are dl_t = S_t + (Bnd[k + 1] - S_{(k+1) Q}) = S_t + (Bnd[k] - S_{k Q}).
 __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ dtc, const float* __restrict__ A,
                                                       const float* __restrict__ yd, const float* __restrict__ xdu,
                                                       const float* __restrict__ xdy,
                                                       const float* __restrict__ dfinal,
-                                                      const float* __restrict__ hfinal, const double* __restrict__ Rp,
+                                                      const float* __restrict__ hfinal, const double* __restrict__ Bp,
                                                       int nparts, float* __restrict__ ddt, double* __restrict__ dAp,
                                                       double* __restrict__ dDp, int64_t L, int64_t Lp, int H, int P,
                                                       int N, int Q, int nc)
@@ -345,7 +358,8 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
     constexpr int kPer = 16;
     __shared__ double sc[kT];
     __shared__ double ex[kT];           // S + <dfinal, h_final> after each thread's tokens
-    __shared__ double corr[kT + 1];     // per chunk met by the span: R_k - (S_{e_k + 1} + <dfinal, h_final>)
+    __shared__ double in[kT];           // the same from each thread's first token on
+    __shared__ double corr[kT];         // per chunk of the pass: the mean of the two forms' offsets
     const int h = blockIdx.x % H;
     const int64_t b = blockIdx.x / H;
     const int64_t bh = b * H + h;
@@ -367,18 +381,24 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
         block_scan(v);
         return sc[kT - 1];
     };
+    auto bnd = [&](int64_t j) {                          // Bnd[j], j < nc
+        const double* bp = Bp + (bh * (nc + 1) + j) * nparts;
+        double r = 0.0;
+        for (int i = 0; i < nparts; ++i) r += bp[i];
+        return r;
+    };
     double fh = 0.0;
     if (dfinal) {
         const int64_t PN = (int64_t)P * N;
         for (int64_t i = tid; i < PN; i += kT) fh += (double)dfinal[bh * PN + i] * hfinal[bh * PN + i];
     }
-    double carry = block_sum(fh);
-    double bcarry = 0.0;                // S_{e_k + 1} + fh of a chunk that reaches above the span
+    fh = block_sum(fh);
+    double carry = fh;
     const double a = A[h];
     double dA_acc = 0.0, dD_acc = 0.0;
-    const int64_t span = (int64_t)kT * kPer;
-    const int64_t top = (L + kPer - 1) / kPer * kPer;
-    for (int64_t hi = top; hi > 0; hi -= span) {
+    const int64_t span = (int64_t)(kT * kPer / Q) * Q;   // whole chunks per pass (Q <= 256)
+    const int nact = (int)(span / kPer);                  // threads with tokens
+    for (int64_t hi = (int64_t)nc * Q; hi > 0; hi -= span) {
         // this thread's tokens: [hi - kPer (tid + 1), hi - kPer tid), latest first
         const int64_t t1 = hi - (int64_t)kPer * tid;
         float qs[kPer], xs[kPer];
@@ -387,7 +407,7 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
             float q = 0.f, xu = 0.f;
-            if (t >= 0 && t < L) {
+            if (tid < nact && t >= 0 && t < L) {
                 const int64_t rt = bh * L + t;
                 xu = xdu[rt];
                 q = yd[rt] - dtc[bh * Lp + t] * xu;
@@ -399,38 +419,28 @@ __global__ __launch_bounds__(kT) void bwd_scan_kernel(const float* __restrict__ 
         }
         const double incl = block_scan(own);
         const double total = sc[kT - 1];
-        const double excl = carry + incl - own;             // everything after this thread's tokens
-        ex[tid] = excl;
+        ex[tid] = carry + incl - own;
+        in[tid] = carry + incl;
         __syncthreads();
-        // the chunks this span meets, k0 .. k1 (at most kT + 1 of them: chunks hold >= 16 tokens)
         const int64_t lo = hi - span > 0 ? hi - span : 0;
-        const int64_t k0 = lo / Q, k1 = (hi - 1) / Q;
+        const int64_t k0 = lo / Q, k1 = hi / Q - 1;       // the pass's chunks (at most kT of them)
         for (int64_t k = k0 + tid; k <= k1; k += kT) {
-            double cr = 0.0;
-            if (k < nc - 1) {
-                const int64_t end = (k + 1) * Q;             // first token after chunk k
-                const double sk = end <= hi ? ex[(hi - end) / kPer] : bcarry;
-                double r = 0.0;
-                const double* rp = Rp + (bh * nc + k) * nparts;
-                for (int j = 0; j < nparts; ++j) r += rp[j];
-                cr = r - sk;
-            }
-            corr[k - k0] = cr;
+            const double right = (k + 1 < nc ? bnd(k + 1) : fh) - ex[(hi - (k + 1) * Q) / kPer];
+            const double left = bnd(k) - in[(hi - k * Q) / kPer - 1];
+            corr[k - k0] = 0.5 * (right + left);
         }
         __syncthreads();
-        double run = excl;
+        double run = ex[tid];
 #pragma unroll
         for (int k = 0; k < kPer; ++k) {
             const int64_t t = t1 - 1 - k;
             run += qs[k];
-            if (t >= 0 && t < L) {
+            if (tid < nact && t >= 0 && t < L) {
                 const double dl = run + corr[t / Q - k0];
                 ddt[(b * L + t) * H + h] = (float)(a * dl + xs[k]);
                 dA_acc += (double)dtc[bh * Lp + t] * dl;
             }
         }
-        // a chunk reaching across the span's lower edge has its end in this span
-        if (lo > 0 && lo % Q != 0) bcarry = ex[(hi - (lo / Q + 1) * Q) / kPer];
         carry += total;
     }
     const double sa = block_sum(dA_acc);
@@ -539,7 +549,8 @@ BwdLayout bwd_layout(const Dims& d, int elemD)
     w.xdy = take(B * d.seqlen * H * 4);
     w.dAp = take(B * H * 8);
     w.dDp = take(B * H * 8);
-    w.Rp = take(B * H * nc * ((P * N + 1023) / 1024 * 4) * 8);   // per (b, h, chunk): one fp64 sum per wavefront
+    w.Rp = take(B * H * (nc + 1) * ((P * N + 1023) / 1024 * 4) * 8);   // per (b, h, chunk boundary): one fp64
+                                                                        // sum per wavefront
     w.total = std::max<size_t>(o, 256);
     return w;
 }
@@ -594,7 +605,7 @@ hipError_t run_backward(const TD* x, const float* dt, const float* A, const TD* 
     const unsigned npass = (unsigned)((P * N + 4 * kT - 1) / (4 * kT));
     const int nparts = (int)npass * (kT / 64);
     hipLaunchKernelGGL((bwd_passing_kernel<TD>), dim3(npass, (unsigned)H, (unsigned)B), dim3(kT), 0, s, F(w.states),
-                       F(w.cs), dfinal, TT(w.entry), (void*)(ws + w.Gout_rev), dinit,
+                       F(w.cs), dfinal, TT(w.entry), init, (void*)(ws + w.Gout_rev), dinit,
                        reinterpret_cast<double*>(ws + w.Rp), st, H, P, N, Q, nc);
     SSD_TRY(hipGetLastError());
     // reversed and per-head copies, S_in^T
