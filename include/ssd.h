@@ -153,9 +153,10 @@ int ssd_forward_noalloc(const void* x, const float* dt, const float* A, const vo
  * (NULL = 0), by the adjoint of the recurrence: the adjoint state runs backwards in time as an SSD
  * of its own (dy as input, C in the role of B), computed with the same stage kernels on
  * time-reversed and role-swapped arrays; the log-decay gradient is the suffix sum over tokens of
- * dy.(y - D x) - (dt x).(dL/d(dt x)), summed within each chunk from both of its ends, where the
- * gradient is the inner product of the adjoint and forward states at the chunk boundary (so
- * rounding does not accumulate across chunks).  Arguments as for ssd_forward, plus
+ * dy.(y - D x) - (dt x).(dL/d(dt x)), summed within each chunk from its end (bf16 inputs: the mean
+ * of the sums from both ends), where the gradient is the inner product of the adjoint and forward
+ * states at the chunk boundary (so rounding does not accumulate across chunks).  Arguments as for
+ * ssd_forward, plus
  *   dy T (batch, seqlen, nheads, headdim); dfinal float (batch, nheads, headdim, dstate) or NULL
  *   dx T like x; ddt float like dt; dA, dD float (nheads); dB, dC T like B, C;
  *   dinit float (batch, nheads, headdim, dstate): the gradient of the initial state (written

@@ -30,6 +30,11 @@ CASES = [
     # straddles the pass boundary: the per-chunk restart carried across passes
     (1, 4500, 2, 16, 32, 1, 192, "f32", True, True),
     (1, 4500, 2, 32, 32, 1, 192, "bf16", False, True),
+    # one chunk with both boundary values from the states (initial state and final-state gradient);
+    # chunk 16 over 5000 tokens (256 chunks per pass of the scan); chunk 48 (passes of 4080 tokens)
+    (1, 200, 4, 32, 64, 1, 256, "f32", True, True),
+    (1, 5000, 2, 16, 16, 1, 16, "f32", True, True),
+    (1, 4200, 2, 16, 32, 1, 48, "bf16", True, True),
 ]
 
 
