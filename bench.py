@@ -692,7 +692,9 @@ def main():
         "kernels": kernels,
         "kernels_note": "the stage entry points timed one by one (mean, median, min over the calls); inside "
                         "ssd_forward stage 1 runs in the prologue of the stage-2 kernel, so the forward launches "
-                        "three kernels; cold = each stage alone after a 512 MB read that evicts L2 and the MALL",
+                        "three kernels; cold = each stage alone after a 512 MB read that evicts L2 and the MALL; "
+                        "the events around each stage add a few us, which shows on the shortest one (dA_cumsum; "
+                        "the committed kernel traces give the launches' own durations)",
         "other_workloads": others,
         "ssd_step": decode,
         "backward": bwd,
