@@ -20,6 +20,9 @@ CASES = [
     (1, 48, 2, 64, 128, 1, 256, "bf16", "ranged", True),     # one partial chunk
     (1, 1, 2, 32, 32, 1, 16, "bf16", "shifted", True),       # a single token
     (1, 1, 2, 32, 32, 1, 16, "f32", "shifted", False),
+    # chunks that are not whole 32-token stages: the last stage of every chunk is half empty
+    (2, 500, 8, 64, 128, 1, 48, "bf16", "shifted", True),
+    (1, 700, 4, 64, 128, 1, 176, "bf16", "ranged", False),
 ]
 
 
@@ -56,7 +59,7 @@ def test_tiny_configuration():
     assert slice_rel_err(to_f64(fin), fin_ref, 1) <= 1e-4
 
 
-@pytest.mark.parametrize("Q", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("Q", [16, 32, 48, 64, 80, 112, 128, 208, 240, 256])
 def test_chunk_size_invariance(Q):
     """The chunk size changes how the work is blocked, not the result."""
     inp = make_random(2, 600, 4, 64, 64, 2, Q, "f32", "shifted", True, seed=300)

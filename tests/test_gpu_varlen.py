@@ -20,6 +20,9 @@ CASES = [
     (list(np.random.default_rng(7).integers(1, 13, 40)), 8, 64, 128, 1, 64, "bf16"),
     ([5, 700, 33, 129], 6, 128, 256, 3, 256, "bf16"),
     ([17, 48, 95], 3, 16, 48, 3, 16, "f32"),
+    # chunks that are not whole 32-token stages, sequences starting inside the half-empty last stage
+    ([300, 7, 150, 81, 1], 4, 64, 128, 1, 80, "bf16"),
+    ([90, 250, 33], 2, 32, 64, 1, 208, "f32"),
 ]
 
 
