@@ -35,6 +35,9 @@ CASES = [
     (1, 200, 4, 32, 64, 1, 256, "f32", True, True),
     (1, 5000, 2, 16, 16, 1, 16, "f32", True, True),
     (1, 4200, 2, 16, 32, 1, 48, "bf16", True, True),
+    # one head per group (the one-head launch shape; group sums of a single head)
+    (1, 300, 4, 64, 64, 4, 64, "bf16", True, True),
+    (2, 150, 3, 32, 32, 3, 32, "f32", False, True),
 ]
 
 
