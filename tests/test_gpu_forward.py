@@ -23,6 +23,9 @@ CASES = [
     # chunks that are not whole 32-token stages: the last stage of every chunk is half empty
     (2, 500, 8, 64, 128, 1, 48, "bf16", "shifted", True),
     (1, 700, 4, 64, 128, 1, 176, "bf16", "ranged", False),
+    # the largest head dimension with the largest state
+    (1, 300, 3, 128, 256, 1, 256, "bf16", "shifted", True),
+    (2, 200, 2, 128, 256, 2, 128, "f32", "shifted", True),
 ]
 
 
