@@ -38,6 +38,9 @@ CASES = [
     # one head per group (the one-head launch shape; group sums of a single head)
     (1, 300, 4, 64, 64, 4, 64, "bf16", True, True),
     (2, 150, 3, 32, 32, 3, 32, "f32", False, True),
+    # the largest head dimension with the largest state
+    (1, 150, 2, 128, 256, 1, 64, "bf16", True, True),
+    (1, 100, 2, 128, 256, 1, 32, "f32", True, True),
 ]
 
 
